@@ -1,0 +1,221 @@
+"""Pins for the oracle's quantizer (block exponent, E2M1 code, packing).
+
+Each test ties the oracle to something other than itself: the E2M1 grid and
+its closed forms, an independent nearest-value search, the mathematical
+definition of the UE8M0 exponent, hand-derived bytes, and the one statistic
+the pages print (ROCm/aiter PR 5484, "One deliberate deviation").
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from pack_token_amd.workloads import bf16_bits_to_f32, to_bf16_bits
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+MIDPOINTS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+MIDPOINT_EVEN_CODES = np.array([0, 2, 2, 4, 4, 6, 6])
+
+# every finite bf16 pattern
+_ALL = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+_EXP = (_ALL.astype(np.uint32) >> 7) & 0xFF
+FINITE_BF16 = _ALL[_EXP != 0xFF]
+
+
+def nearest_code_even(m):
+    """Independent E2M1 code search: nearest grid magnitude, a tie goes to
+    the even code, above 6 saturates to 6.  m: float64 magnitudes."""
+    m = np.minimum(np.abs(m), 6.0)
+    d = np.abs(m[..., None] - GRID)
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best
+    # among tied candidates prefer an even code
+    even = cand & (np.arange(8) % 2 == 0)
+    pick = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(cand, axis=-1))
+    return pick.astype(np.uint8)
+
+
+def ue8m0_by_definition(amax):
+    """Least e in [1, 254] with amax <= 6 * 2^(e-127) (float64, exact)."""
+    amax = np.asarray(amax, np.float64)
+    e = np.ceil(np.log2(np.maximum(amax, 1e-300) / 6.0)) + 127
+    e = e.astype(np.int64)
+    # correct any log2 rounding at exact powers of two
+    lo = 6.0 * np.ldexp(1.0, e - 1 - 127)
+    e = np.where(amax <= lo, e - 1, e)
+    hi = 6.0 * np.ldexp(1.0, e - 127)
+    e = np.where(amax > hi, e + 1, e)
+    return np.clip(e, 1, 254)
+
+
+def test_grid_values_map_to_their_codes():
+    # 6 * 2^k must be a finite fp32: k <= 125
+    for k in range(-126, 126):
+        e = 127 + k
+        v = (GRID * 2.0 ** k).astype(np.float32)
+        assert np.array_equal(oracle.e2m1_nibbles(v, e), np.arange(8, dtype=np.uint8)), k
+        assert np.array_equal(oracle.e2m1_nibbles(-v, e), np.arange(8, dtype=np.uint8) | 8), k
+
+
+def test_midpoints_round_half_to_even():
+    for k in range(-120, 120, 7):
+        v = (MIDPOINTS * 2.0 ** k).astype(np.float32)
+        assert np.array_equal(oracle.e2m1_nibbles(v, 127 + k), MIDPOINT_EVEN_CODES), k
+        assert np.array_equal(oracle.e2m1_nibbles(-v, 127 + k), MIDPOINT_EVEN_CODES | 8), k
+
+
+def test_signed_zero_codes():
+    v = np.array([0.0, -0.0, -1e-30, 1e-30, -0.2, 0.2, -0.25, 0.25], np.float32)
+    got = oracle.e2m1_nibbles(v, 127)
+    assert list(got) == [0x0, 0x8, 0x8, 0x0, 0x8, 0x0, 0x8, 0x0]
+
+
+def test_group_exponent_closed_forms():
+    # amax = 6 * 2^k  ->  e = 127 + k  (6 * 2^k finite: k <= 125)
+    for k in range(-126, 126):
+        g = np.zeros((1, 32), np.float32)
+        g[0, 5] = np.float32(6.0 * 2.0 ** k)
+        g[0, 9] = np.float32(-1.0 * 2.0 ** k)
+        assert oracle.group_exponents(g)[0] == 127 + k, k
+    # all-zero group, +0 and -0 mixed -> e = 1
+    z = np.where(np.arange(32) % 2 == 0, 0.0, -0.0).astype(np.float32)[None]
+    assert oracle.group_exponents(z)[0] == 1
+    # group at the largest finite bf16 -> e = 253
+    big = np.zeros((1, 32), np.float32)
+    big[0, 0] = bf16_bits_to_f32(np.array([0x7F7F], np.uint16))[0]
+    assert oracle.group_exponents(big)[0] == 253
+
+
+def test_group_exponent_exhaustive_against_definition():
+    """All 32,639 positive finite bf16 amax values: (bits>>23)+(mant!=0) of
+    fl(amax/6) equals the least e with amax <= 6*2^(e-127), clamped to [1,254];
+    and e never reaches the clamp bounds' far side (e in [1,253])."""
+    pos = FINITE_BF16[(FINITE_BF16 > 0) & (FINITE_BF16 < 0x8000)]
+    assert pos.size == 32639
+    amax = bf16_bits_to_f32(pos)
+    g = np.zeros((pos.size, 32), np.float32)
+    g[:, 0] = amax
+    e = oracle.group_exponents(g)
+    assert np.array_equal(e, ue8m0_by_definition(amax))
+    assert e.min() == 1 and e.max() == 253
+
+
+def test_scale_floor_values():
+    z = np.zeros((1, 32), np.float32)
+    # e = least e with floor <= 2^(e-127)
+    for floor, e in [(1e-10, 94), (1e-12, 88), (1e-4, 114), (2.0 ** -126, 1), (0.0, 1)]:
+        assert oracle.group_exponents(z, float(np.float32(floor)))[0] == e, floor
+    # a floor only raises e where amax/6 is below it
+    g = np.zeros((1, 32), np.float32)
+    g[0, 0] = 6.0
+    assert oracle.group_exponents(g, float(np.float32(1e-4)))[0] == 127
+
+
+def test_subnormal_only_group():
+    rng = np.random.default_rng(5)
+    bits = (rng.integers(1, 0x80, 32) | (rng.integers(0, 2, 32) << 15)).astype(np.uint16)
+    v = bf16_bits_to_f32(bits)
+    assert oracle.group_exponents(v[None])[0] == 1
+    m = v.astype(np.float64) * 2.0 ** 126
+    want = nearest_code_even(m) | (np.signbit(v).astype(np.uint8) << 3)
+    assert np.array_equal(oracle.e2m1_nibbles(v, 1), want)
+
+
+@pytest.mark.slow
+def test_brute_force_every_bf16_every_exponent():
+    """Every finite bf16 value x every e in [1,253] (16.5 M cases) against an
+    independent nearest-magnitude search with ties to the even code."""
+    v = bf16_bits_to_f32(FINITE_BF16)
+    sign = np.signbit(v).astype(np.uint8) << 3
+    v64 = v.astype(np.float64)
+    for e in range(1, 254):
+        want = nearest_code_even(v64 * 2.0 ** (127 - e)) | sign
+        got = oracle.e2m1_nibbles(v, e)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, (e, FINITE_BF16[bad[:5]], got[bad[:5]], want[bad[:5]])
+
+
+def test_inverse_scale_equals_division_below_254():
+    """Multiplying by 2^(127-e) equals dividing by 2^(e-127) for every finite
+    bf16 and e <= 253 (sgl-project/sglang PR 39656 review: equal except at
+    exponent 254)."""
+    v = bf16_bits_to_f32(FINITE_BF16)
+    for e in list(range(1, 20)) + list(range(120, 136)) + list(range(240, 254)):
+        a = v * np.float32(2.0 ** (127 - e))
+        b = v / np.float32(2.0 ** (e - 127))
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), e
+
+
+def test_hand_derived_group_bytes():
+    d = json.load(open(os.path.join(GOLDEN, "hand_e2m1_group.json")))
+    x = np.zeros((1, 128), np.float32)
+    x[0, :32] = np.array(d["values"], np.float32)
+    # the remaining groups are zero
+    b, e = oracle.quantize_rows(x)
+    assert e[0, 0] == d["e"]
+    assert list(b[0, :16]) == d["bytes"]
+    assert list(e[0, 1:]) == [1, 1, 1]
+    assert not b[0, 16:].any()
+
+
+def test_dequant_within_half_grid_step():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((512, 128)).astype(np.float32) * np.exp(rng.uniform(-30, 30, (512, 1))).astype(np.float32)
+    x = bf16_bits_to_f32(to_bf16_bits(x))
+    b, e = oracle.quantize_rows(x)
+    T, H = 512, 16
+    q_out = b.reshape(32, 16, 64)
+    qs = np.zeros((32, 1, 4, 16, 4), np.uint8)
+    for r in range(512):
+        t, h = divmod(r, 16)
+        qs[t, 0, :, h, 0] = e[r]
+    y = oracle.dequant_q(q_out, qs).reshape(512, 128)
+    scale = np.repeat(np.ldexp(1.0, e.astype(np.int64) - 127), 32, axis=1)
+    m = np.abs(x.astype(np.float64)) / scale
+    step = np.where(m < 2, 0.5, np.where(m < 4, 1.0, 2.0))
+    assert np.all(np.abs(y - x.astype(np.float64)) <= 0.5 * step * scale + 0.0)
+    # sign is always preserved (zero codes included)
+    assert np.array_equal(np.signbit(y), np.signbit(x))
+
+
+def test_dequant_special_exponents():
+    packed = np.full((1, 16, 64), 0x71, np.uint8)  # nibbles 1 (0.5) and 7 (6)
+    qs = np.zeros((1, 1, 4, 16, 4), np.uint8)
+    qs[0, 0, 0, 0, 0] = 0      # 2^-127
+    qs[0, 0, 1, 0, 0] = 255    # NaN
+    qs[0, 0, 2, 0, 0] = 254    # 2^127
+    qs[0, 0, 3, 0, 0] = 127
+    y = oracle.dequant_q(packed, qs)[0, 0]
+    assert y[0] == np.float32(0.5 * 2.0 ** -127) and y[1] == np.float32(6 * 2.0 ** -127)
+    assert np.isnan(y[32:64]).all()
+    assert y[64] == np.float32(0.5 * 2.0 ** 127)
+    assert y[96] == 0.5 and y[97] == 6.0
+
+
+def test_converter_vs_argmin_statistic_matches_page():
+    """Reproduce the one measurement printed on the pages: over 524,288
+    random bf16 values, hardware-semantics nibbles differ from an argmin
+    oracle (ties toward -inf, single +0) on 27,774 +-0 codes and 2,989
+    exact midpoints.  Pins the ceil exponent rule, the RNE ties and the
+    kept zero sign together (a floor exponent rule gives ~23,200 +-0)."""
+    g = json.load(open(os.path.join(GOLDEN, "aiter5484_converter_vs_argmin.json")))
+    n = g["n_values"]
+    rng = np.random.Generator(np.random.PCG64(0))
+    v = bf16_bits_to_f32(to_bf16_bits(rng.standard_normal(n, dtype=np.float32))).reshape(-1, 32)
+    e = oracle.group_exponents(v)
+    nib = oracle.e2m1_nibbles(v, np.repeat(e[:, None], 32, axis=1))
+    book = np.array([-6, -4, -3, -2, -1.5, -1, -0.5, 0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
+    m = v.astype(np.float64) * np.ldexp(1.0, 127 - e.astype(np.int64))[:, None]
+    val = book[np.argmin(np.abs(m[..., None] - book), axis=-1)]  # first index = toward -inf
+    code = np.searchsorted(GRID, np.abs(val)).astype(np.uint8)
+    anib = ((val < 0).astype(np.uint8) << 3) | code
+    diff = nib != anib
+    pm0 = diff & ((nib & 7) == 0) & ((anib & 7) == 0)
+    n_pm0, n_mid = int(pm0.sum()), int((diff & ~pm0).sum())
+    # 4 sigma of a binomial count around the page's figures
+    assert abs(n_pm0 - g["plus_minus_zero"]) <= 4 * np.sqrt(g["plus_minus_zero"]), n_pm0
+    assert abs(n_mid - g["exact_midpoints"]) <= 4 * np.sqrt(g["exact_midpoints"]), n_mid
+    assert abs(100.0 * (n_pm0 + n_mid) / n - g["fraction_percent"]) < 0.2

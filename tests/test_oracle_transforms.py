@@ -1,0 +1,190 @@
+"""Pins for the oracle's RoPE, Hadamard and key-RMSNorm steps.
+
+The exact fp32 evaluation order of these steps is a reading (the pages name
+the operations only), so what is pinned here is everything the mathematics
+fixes: special cases that must be exact, the pairing and slice (a wrong
+pairing fails by O(1)), and agreement with a float64 evaluation to within
+the bf16 rounding the pages require ("preserving the bf16 round-trip after
+RoPE", sgl-project/sglang PR 39656 Summary).
+"""
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle
+from pack_token_amd.workloads import bf16_bits_to_f32, cos_sin_table, to_bf16_bits
+
+
+def bf16_vals(x):
+    return bf16_bits_to_f32(to_bf16_bits(np.asarray(x, np.float32)))
+
+
+def bf16_ulp(x):
+    """Spacing of bf16 numbers at |x| (x float64); subnormal floor 2^-133."""
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.maximum(ax, 2.0 ** -126)))
+    return np.ldexp(1.0, (e - 7).astype(np.int64))
+
+
+def rope_f64(x, cs, rope_offset, is_neox):
+    """Float64 rotation of dims [o, o+64) by angle pairs: pair i uses cos_sin[:, i],
+    cos_sin[:, 32+i]; neox pairs (i, i+32), interleaved pairs (2i, 2i+1)."""
+    y = x.astype(np.float64).copy()
+    S = y[:, rope_offset:rope_offset + 64]
+    i = np.arange(32)
+    ia, ib = (i, i + 32) if is_neox else (2 * i, 2 * i + 1)
+    a, b = S[:, ia].copy(), S[:, ib].copy()
+    c, s = cs[:, :32].astype(np.float64), cs[:, 32:].astype(np.float64)
+    S[:, ia] = a * c - b * s
+    S[:, ib] = b * c + a * s
+    return y
+
+
+@pytest.mark.parametrize("is_neox", [True, False])
+@pytest.mark.parametrize("rope_offset", [0, 64])
+def test_rope_matches_float64_rotation(is_neox, rope_offset):
+    rng = np.random.default_rng(1)
+    n = 2000
+    x = bf16_vals(rng.standard_normal((n, 128)) * np.exp(rng.uniform(-5, 5, (n, 1))))
+    tab = cos_sin_table(40000)
+    cs = tab[rng.integers(0, 40000, n)]
+    got = oracle.rope_rows(x, cs, rope_offset, is_neox).astype(np.float64)
+    want = rope_f64(x, cs, rope_offset, is_neox)
+    # outside the slice: untouched, bit for bit
+    outside = np.ones(128, bool)
+    outside[rope_offset:rope_offset + 64] = False
+    assert np.array_equal(got[:, outside], x[:, outside].astype(np.float64))
+    # inside: every value is a bf16 number within 1 bf16 ulp of the exact rotation
+    sl = slice(rope_offset, rope_offset + 64)
+    assert np.array_equal(bf16_vals(got[:, sl]), got[:, sl].astype(np.float32))
+    err = np.abs(got[:, sl] - want[:, sl])
+    # fp32 products/sum add at most a few 2^-24 relative error before the bf16 rounding
+    mag = np.abs(x[:, sl]).max(axis=1, keepdims=True).astype(np.float64)
+    assert np.all(err <= bf16_ulp(want[:, sl]) + 4 * 2.0 ** -24 * mag)
+
+
+def test_rope_identity_row():
+    """cos = 1, sin = 0: every nonzero value is unchanged bit for bit; a zero
+    output has the IEEE sign of a sum of two zeros."""
+    rng = np.random.default_rng(2)
+    x = bf16_vals(rng.standard_normal((64, 128)))
+    x[:, 64:] *= rng.integers(0, 2, (64, 64))  # plant +0 results
+    x[::3, 64:70] = -0.0
+    cs = np.zeros((64, 64), np.float32)
+    cs[:, :32] = 1.0
+    for is_neox in (True, False):
+        got = oracle.rope_rows(x, cs, 64, is_neox)
+        assert np.array_equal(got[x != 0], x[x != 0])
+        # a' = a*1 - b*0, b' = b*1 + a*0 in IEEE: -0 only when both terms are -0
+        i = np.arange(32)
+        ia, ib = (i + 64, i + 96) if is_neox else (2 * i + 64, 2 * i + 65)
+        a, b = x[:, ia], x[:, ib]
+        za = a == 0
+        want_neg_a = np.signbit(a) & ~np.signbit(b)     # (-0) - (+0) = -0
+        assert np.array_equal(np.signbit(got[:, ia])[za], want_neg_a[za])
+        zb = b == 0
+        want_neg_b = np.signbit(b) & np.signbit(a)      # (-0) + (-0) = -0
+        assert np.array_equal(np.signbit(got[:, ib])[zb], want_neg_b[zb])
+
+
+def test_rope_quarter_turn_is_swap_with_negation():
+    rng = np.random.default_rng(3)
+    x = bf16_vals(rng.standard_normal((16, 128)))
+    cs = np.zeros((16, 64), np.float32)
+    cs[:, 32:] = 1.0
+    got = oracle.rope_rows(x, cs, 64, True)
+    assert np.array_equal(got[:, 64:96], -x[:, 96:128])
+    assert np.array_equal(got[:, 96:128], x[:, 64:96])
+    got = oracle.rope_rows(x, cs, 0, False)
+    assert np.array_equal(got[:, 0:64:2], -x[:, 1:64:2])
+    assert np.array_equal(got[:, 1:64:2], x[:, 0:64:2])
+
+
+def test_cos_sin_table_values():
+    tab = cos_sin_table(9)
+    f = 10000.0 ** (-np.arange(32) / 32.0)
+    assert np.allclose(tab[:, :32], np.cos(np.arange(9)[:, None] * f), atol=1e-7)
+    assert np.allclose(tab[:, 32:], np.sin(np.arange(9)[:, None] * f), atol=1e-7)
+    assert (tab[0, :32] == 1).all() and (tab[0, 32:] == 0).all()
+
+
+def test_hadamard_constant():
+    s = oracle.hadamard_scale()
+    assert np.float32(s).view(np.uint32) == 0x3DB504F3
+    assert abs(s - 1 / np.sqrt(128)) < 2 ** -27
+
+
+def test_hadamard_one_hot_rows():
+    """e_j -> bf16(fp32(1/sqrt(128))) * (-1)^popcount(i & j): Sylvester order."""
+    x = np.eye(128, dtype=np.float32)
+    got = oracle.fwht_rows(x)
+    H = scipy.linalg.hadamard(128).astype(np.float32)  # H[i,j] = (-1)^popcount(i&j)
+    mag = bf16_vals(np.float32(oracle.hadamard_scale()))
+    assert np.array_equal(got, H * mag)
+
+
+def test_hadamard_matches_dense_float64():
+    rng = np.random.default_rng(4)
+    x = bf16_vals(rng.standard_normal((500, 128)) * np.exp(rng.uniform(-8, 8, (500, 1))))
+    got = oracle.fwht_rows(x).astype(np.float64)
+    H = scipy.linalg.hadamard(128).astype(np.float64)
+    want = x.astype(np.float64) @ H.T / np.sqrt(128.0)
+    # 7 fp32 stages on magnitudes <= sum|x|, then one bf16 rounding
+    l1 = np.abs(x).sum(axis=1, keepdims=True).astype(np.float64)
+    assert np.all(np.abs(got - want) <= bf16_ulp(want) + 16 * 2.0 ** -24 * l1 / np.sqrt(128))
+    # applied twice is the identity up to the roundings
+    twice = oracle.fwht_rows(got.astype(np.float32)).astype(np.float64)
+    assert np.allclose(twice, x, rtol=0, atol=float(np.abs(x).max()) * 2 ** -6)
+
+
+def rms_f64(x, gamma, eps):
+    x64 = x.astype(np.float64)
+    r = 1.0 / np.sqrt((x64 ** 2).mean(axis=1, keepdims=True) + eps)
+    return x64 * r * gamma.astype(np.float64)
+
+
+def test_rmsnorm_constant_vector():
+    gamma_f = bf16_vals(np.linspace(0.5, 1.5, 128))
+    gamma = to_bf16_bits(gamma_f)
+    for c in [1.0, -3.0, 0.0078125, 250.0]:
+        x = np.full((1, 128), c, np.float32)
+        got = oracle.rmsnorm_rows(x, gamma, 1e-6)[0].astype(np.float64)
+        want = np.sign(c) * gamma_f.astype(np.float64) * abs(c) / np.sqrt(c * c + 1e-6)
+        assert np.all(np.abs(got - want) <= bf16_ulp(want) + 1e-7 * np.abs(want)), c
+
+
+def test_rmsnorm_matches_float64():
+    rng = np.random.default_rng(6)
+    gamma_f = bf16_vals(1.0 + 0.1 * rng.standard_normal(128))
+    gamma = to_bf16_bits(gamma_f)
+    x = bf16_vals(rng.standard_normal((400, 128)) * np.exp(rng.uniform(-6, 6, (400, 1))))
+    got = oracle.rmsnorm_rows(x, gamma, 1e-6).astype(np.float64)
+    want = rms_f64(x, gamma_f, 1e-6)
+    assert np.all(np.abs(got - want) <= bf16_ulp(want) + 8 * 2.0 ** -24 * np.abs(want))
+    # all-zero rows stay zero (r = 1/sqrt(eps) is finite)
+    z = oracle.rmsnorm_rows(np.zeros((1, 128), np.float32), gamma, 1e-6)
+    assert not z.any()
+
+
+def test_bf16_rounding_nearest_even():
+    """fp32 -> bf16: nearest of the two bracketing bf16 values (float64
+    distances), a tie goes to the one with an even last mantissa bit; also
+    equal to torch's CPU cast."""
+    rng = np.random.default_rng(12)
+    u = rng.integers(0, 1 << 32, 400000, dtype=np.uint64).astype(np.uint32)
+    u = u[((u >> 23) & 0xFF) != 0xFF]                      # finite
+    ties = (rng.integers(0, 1 << 16, 5000, dtype=np.uint32) << 16) | 0x8000
+    ties = ties[((ties >> 23) & 0xFF) < 0xFE]
+    u = np.concatenate([u, ties, np.array([0x00008000, 0x80018000, 0x7F7F8000 - 0x10000], np.uint32)])
+    x = u.view(np.float32)
+    got = oracle.bf16_round(x).astype(np.float64)
+    lo = (u & 0xFFFF0000).view(np.float32).astype(np.float64)            # toward zero
+    hi = ((u & 0xFFFF0000) + 0x10000).view(np.float32).astype(np.float64)  # away from zero
+    # past the largest bf16 the next step up is 2^128, and rounding there overflows to inf
+    hi_dist = np.where(np.isinf(hi), np.copysign(2.0 ** 128, lo), hi)
+    xd = x.astype(np.float64)
+    dlo, dhi = np.abs(xd - lo), np.abs(hi_dist - xd)
+    lo_even = ((u >> 16) & 1) == 0
+    want = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo_even, lo, hi)))
+    assert np.array_equal(got, want)
+    assert np.array_equal(got.astype(np.float32), bf16_vals(x))
