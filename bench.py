@@ -1,0 +1,213 @@
+"""Benchmark of the fused q+k RoPE / FP4 pack + paged store on one MI355X.
+
+One step = fp4idx_q_rope_pack + fp4idx_k_rope_pack_store on one stream over
+the large-prefill workload (T = 131072 tokens, H = 64 heads, D = 128, neox
+RoPE on dims 64..127, contiguous slots into 2048 cache blocks), inputs
+resident in HBM before timing starts.  Prints one JSON line.
+
+Algorithmic bytes (each input read once, each output written once):
+  query launch, per token: 256H (q) + 4H (weights) + 8 (position) + 256 (cos/sin
+      row) + 64H (q_out) + 64J (q scales) + 4H (weights_out)
+  key launch, per token:   256 (k) + 8 (slot) + 64 + 4 (cache); its own reads of
+      the position and the cos/sin row repeat the query launch's and are not credited
+  step total, per token:   query + key = 21,844 B at H = 64.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "pack_token_amd", "csrc", "fp4idx_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q_split_neox_large_prefill_traffic.json")
+
+
+def q_bytes_per_token(H: int) -> int:
+    J = ((H // 16) + 3) // 4 * 4
+    return 256 * H + 4 * H + 8 + 256 + 64 * H + 64 * J + 4 * H
+
+
+def k_bytes_per_token() -> int:
+    return 256 + 8 + 64 + 4
+
+
+def step_bytes_per_token(H: int) -> int:
+    return q_bytes_per_token(H) + k_bytes_per_token()
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(q_launch_bytes: int):
+    """HBM bytes of one query launch from committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE counts, if they were taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return int(rec["bytes_per_launch"])
+
+
+def cpu_baseline(wl, n_tokens: int, threads: int):
+    """The CPU oracle (test infrastructure) on the first n_tokens tokens of the
+    same workload, query + key path, timed on the host cores."""
+    import numpy as np
+
+    import oracle
+
+    sl = slice(0, n_tokens)
+    kv, ks = wl.empty_cache()
+    t0 = time.perf_counter()
+    oracle.q_rope_pack(wl.q[sl], wl.positions[sl], wl.cos_sin, wl.weights[sl],
+                       is_neox=wl.is_neox, rope_offset=wl.rope_offset, threads=threads)
+    oracle.k_rope_pack_store(wl.k[sl], wl.positions[sl], wl.cos_sin, wl.slot_mapping[sl], kv, ks,
+                             is_neox=wl.is_neox, rope_offset=wl.rope_offset, threads=threads)
+    dt = time.perf_counter() - t0
+    del np
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n_tokens} of {wl.T} tokens of the same workload (query + key "
+                      f"path), {threads} threads, {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--tokens", type=int, default=131072)
+    ap.add_argument("--heads", type=int, default=64)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=131072)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="instead of the benchmark, time one plain device copy of this many MiB "
+                         "(reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this path runs on one GPU only (every token is independent and no "
+              "collective is on the hot path); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from pack_token_amd import fp4idx, workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n}),
+              flush=True)
+        return
+
+    t_gen = time.perf_counter()
+    wl = workloads.large_prefill(T=args.tokens, H=args.heads)
+    print(f"bench: generated {wl.name} T={wl.T} H={wl.H} in {time.perf_counter() - t_gen:.1f}s",
+          file=sys.stderr, flush=True)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    q = up(wl.q.view(np.int16))
+    k = up(wl.k.view(np.int16))
+    pos = up(wl.positions)
+    cs = up(wl.cos_sin)
+    w = up(wl.weights)
+    slots = up(wl.slot_mapping)
+    T, H = wl.T, wl.H
+    J = wl.J
+    q_out = torch.empty((T, H, 64), dtype=torch.uint8, device=dev)
+    qs = torch.empty((T, 1, 4, 16, J), dtype=torch.uint8, device=dev)
+    w_out = torch.empty_like(w)
+    kv = torch.zeros((wl.NB, 1, 4, 64, 16), dtype=torch.uint8, device=dev)
+    ks = torch.zeros((wl.NB, 1, 4, 64), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def q_call():
+        fp4idx.q_rope_pack(q, pos, cs, w, q_out=q_out, q_scale_out=qs, weights_out=w_out,
+                           is_neox=wl.is_neox, rope_offset=wl.rope_offset, stream=stream)
+
+    def k_call():
+        fp4idx.k_rope_pack_store(k, pos, cs, slots, kv, ks, is_neox=wl.is_neox,
+                                 rope_offset=wl.rope_offset, stream=stream)
+
+    for _ in range(args.warmup):
+        q_call()
+        k_call()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        q_call()
+        ev[i][1].record(stream)
+        k_call()
+        ev[i][2].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    k_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ms_per_step = total_ms / K
+
+    q_launch_bytes = q_bytes_per_token(H) * T
+    step_bytes = step_bytes_per_token(H) * T
+    achieved = q_launch_bytes / (q_ms * 1e-3) / 1e9
+    traffic = measured_traffic(q_launch_bytes)
+    rec = {
+        "metric": "tokens/s and achieved HBM GB/s (% of peak), fused q+k RoPE/FP4 pack+store",
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16->e2m1",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": T, "heads": H, "head_dim": 128, "rope_dim": 64,
+                   "rope": "neox", "rope_offset": wl.rope_offset, "kv_blocks": wl.NB,
+                   "kv_block_size": 64, "slot_mapping": "contiguous"},
+        "step_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "step_frac_of_hbm_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "q_kernel_us": q_ms * 1e3,
+        "k_kernel_us": k_ms * 1e3,
+        "roofline": {"kernel": "q_split_kernel<neox>", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": q_launch_bytes},
+    }
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        rec["cpu_baseline"] = cpu_baseline(wl, min(args.cpu_sample_tokens, T), threads)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

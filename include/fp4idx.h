@@ -1,0 +1,176 @@
+/*
+ * fp4idx.h -- C ABI of libfp4idx, the fused FP4 sparse-indexer producer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Per token the library rotates the 64-dim RoPE slice of every 128-dim query
+ * head and of the single index key (optionally RMS-normalising the key and
+ * applying a 128-point Hadamard transform), quantizes each 32-element group
+ * to E2M1 with a UE8M0 block exponent, packs two codes per byte, and
+ * scatters the key into a paged FP4 index cache.
+ *
+ * Sources (web pages):
+ *   ROCm/aiter PR 5484 "[HIP] Add FP4 output mode to
+ *     indexer_qk_rope_quant_and_cache" -- sections "API", "Verification",
+ *     "One deliberate deviation";
+ *   sgl-project/sglang PR 39656 "dsv4.1: RoPE and FP4 packing kernels" --
+ *     "Summary" and the review by @BBuf;
+ *   ROCm/aiter PR 4029 "DeepSeek-V4 FP4: fused_compress FP4 scatter +
+ *     rmsnorm_rope_rotate FP4 KV-cache kernel" -- "Changes" and the review
+ *     by @zufayu.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument is a DEVICE pointer (memory from hipMalloc, e.g. a
+ *   torch tensor on the GPU) unless stated otherwise.  The caller allocates
+ *   and owns all buffers; the library allocates nothing, keeps no state other
+ *   than a thread-local error message, and never synchronizes.
+ * - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *   Work is enqueued on that stream only; outputs are valid once the caller
+ *   has synchronized with it.  Calls on different streams or threads are
+ *   independent (they must not share output buffers).
+ * - All tensors are dense and row-major (C-contiguous).
+ * - bf16 tensors hold IEEE bfloat16 bit patterns (uint16).
+ * - Supported shapes are exactly head_dim D = 128, rope_dim R = 64,
+ *   group_size = 32, kv block size BS = 64, and n_heads H a positive multiple
+ *   of 16 up to 2048 (ROCm/aiter PR 5484 "API": anything else is rejected on
+ *   the host with a specific message).
+ * - Block exponent of a 32-group: e = clamp(max(E(amax/6), E(scale_floor)),
+ *   1, 254) where E(x) is the biased exponent of x rounded up to a power of
+ *   two, (bits >> 23) + (mantissa != 0) (sgl-project/sglang PR 39656,
+ *   review).  `scale_floor` is the eps floor applied after the divide; 2^-126
+ *   (FLT_MIN) makes it coincide with the lower clamp.
+ * - Codes: each value v of the group becomes the E2M1 code of v * 2^(127-e)
+ *   rounded to nearest, ties to even, with the sign bit of v kept even when
+ *   the magnitude code is 0 (ROCm/aiter PR 5484 "One deliberate deviation").
+ *   Element 2b goes to the low nibble of byte b.
+ *
+ * Return codes
+ * ------------
+ *   FP4IDX_OK (0); FP4IDX_EINVAL (1): null or misaligned pointer, negative
+ *   size, flag outside {0,1}, inconsistent optional arguments, non-finite or
+ *   negative floor/eps; FP4IDX_EUNSUPPORTED (2): a shape outside the list
+ *   above, the message names the argument and its value; FP4IDX_EHIP (3): a
+ *   HIP launch error, the message carries the HIP error string.
+ *   All validation happens before anything is enqueued: on a non-zero return
+ *   nothing has been written.  T == 0 (rows == 0) is a successful no-op once
+ *   the shape arguments are valid.  fp4idx_last_error() describes the last
+ *   non-zero return on the calling thread.
+ *
+ * Caller errors that are NOT checked on the device
+ *   duplicate non-negative slots in one call (which writer wins is
+ *   unspecified); non-finite inputs.  Positions outside [0, max_pos) are
+ *   clamped into that range and slots outside [0, NB*BS) are skipped, so no
+ *   input value can make the library read or write out of bounds.
+ */
+#ifndef FP4IDX_H
+#define FP4IDX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP4IDX_OK 0
+#define FP4IDX_EINVAL 1
+#define FP4IDX_EUNSUPPORTED 2
+#define FP4IDX_EHIP 3
+
+/*
+ * fp4idx_q_rope_pack -- query side of the producer (ROCm/aiter PR 5484 "API":
+ * q_out u8 [num_tokens, n_heads, head_dim/2], q_scale_out u8
+ * [num_tokens, k_tiles, 4, 16, round_up(H/16, 4)], weights_out with the plain
+ * weight and nothing folded in).
+ *
+ *   q            bf16 [T, H, 128], 16-byte aligned.
+ *   positions    [T] int64 (positions_int64 = 1) or int32 (= 0), naturally
+ *                aligned.  Each is clamped to [0, max_pos).
+ *   cos_sin      fp32 [max_pos, 64], 16-byte aligned: columns 0..31 are
+ *                cos(p*f_i), 32..63 sin(p*f_i); pair i uses column i.
+ *   weights      fp32 [T, H] or NULL, 4-byte aligned.
+ *   T, H         tokens (>= 0), heads (multiple of 16, <= 2048).
+ *   D, R, group_size   must be 128, 64, 32.
+ *   rope_offset  first rotated dim: 64 (the "RoPE tail") or 0.
+ *   is_neox      1: pairs (i, i+32) of the slice; 0: pairs (2i, 2i+1).
+ *                Rotation a' = bf16(a*c - b*s), b' = bf16(b*c + a*s), each
+ *                product rounded to fp32 separately (no fused multiply-add).
+ *   apply_hadamard  1: after RoPE, a 128-point Walsh-Hadamard transform in
+ *                natural (Sylvester) order, butterflies of stride 1..64 in
+ *                fp32, then x * fp32(1/sqrt(128)) rounded to bf16.
+ *   scale_floor  eps floor of the block scale (>= 0, finite); 2^-126 default.
+ *   q_out        u8 [T, H, 64], 16-byte aligned.  Row (t,h) holds the codes
+ *                of the four 32-groups, 16 bytes each.
+ *   q_scale_out  u8 [T, 1, 4, 16, J], J = round_up(H/16, 4), 4-byte aligned.
+ *                Entry [t, 0, g, h % 16, h / 16] = e of group g of head h;
+ *                entries with h/16 >= H/16 are written as 0.
+ *   weights_out  fp32 [T, H] or NULL (must be NULL iff weights is NULL):
+ *                bit copy of weights.
+ */
+int fp4idx_q_rope_pack(const void* q, const void* positions, int positions_int64,
+                       const float* cos_sin, int64_t max_pos, const float* weights,
+                       int64_t T, int H, int D, int R, int rope_offset, int group_size,
+                       int is_neox, int apply_hadamard, float scale_floor,
+                       uint8_t* q_out, uint8_t* q_scale_out, float* weights_out, void* stream);
+
+/*
+ * fp4idx_k_rope_pack_store -- key side: optional RMSNorm, RoPE, optional
+ * Hadamard, quantize, and scatter into the paged index cache (ROCm/aiter PR
+ * 5484 "API": kv_cache u8 [num_blocks, k_tiles, 4, kv_block_size, 16],
+ * kv_cache_scale u8 [num_blocks, k_tiles, 4, kv_block_size]; ROCm/aiter PR
+ * 4029 "Changes": scales interleaved at (pos%16)*(kv_block_size/16)+pos/16;
+ * sgl-project/sglang PR 39656 "Summary": RMSNorm, RoPE, quantize and store
+ * fused in one launch).
+ *
+ *   k            bf16 [T, 128], 16-byte aligned.
+ *   positions, positions_int64, cos_sin, max_pos, rope_offset, is_neox,
+ *   apply_hadamard, scale_floor, D, R, group_size: as for the query call.
+ *   slot_mapping int64 [T], 8-byte aligned.  Token t goes to block
+ *                slot/64, position slot%64; a slot outside [0, NB*64)
+ *                (e.g. -1) writes nothing for that token.
+ *   k_norm_gamma bf16 [128] (16-byte aligned) or NULL = no RMSNorm.  With it:
+ *                ss = sum of x_i^2 folded by halves (i with i+64, then +32,
+ *                ..., +1), r = 1/sqrt(ss/128 + k_norm_eps) with correctly
+ *                rounded sqrt and divide, x_i = bf16((x_i*r)*gamma_i).
+ *   k_norm_eps   >= 0 and finite when k_norm_gamma is given.
+ *   kv_cache     u8 [NB, 1, 4, 64, 16], 16-byte aligned:
+ *                [blk, 0, g, pos, :] = the 16 code bytes of group g.
+ *   kv_cache_scale u8 [NB, 1, 4, 64], 4-byte aligned:
+ *                [blk, 0, g, (pos%16)*4 + pos/16] = e of group g.
+ *   NB, BS       number of blocks (>= 0) and block size (must be 64).
+ * Bytes of slots that no token maps to are left untouched.
+ */
+int fp4idx_k_rope_pack_store(const void* k, const void* positions, int positions_int64,
+                             const float* cos_sin, int64_t max_pos, const int64_t* slot_mapping,
+                             const void* k_norm_gamma, float k_norm_eps,
+                             int64_t T, int D, int R, int rope_offset, int group_size,
+                             int is_neox, int apply_hadamard, float scale_floor,
+                             uint8_t* kv_cache, uint8_t* kv_cache_scale, int64_t NB, int BS,
+                             void* stream);
+
+/*
+ * fp4idx_dequant_debug -- reader side, for tests and debugging: expands
+ * codes back to fp32, value = E2M1(nibble) * 2^(e-127) with E2M1 magnitudes
+ * {0, .5, 1, 1.5, 2, 3, 4, 6} and bit 3 the sign; e = 0 gives 2^-127 and
+ * e = 255 gives NaN (OCP MX e8m0).
+ *
+ *   which = 0 (Q):      packed = q_out [rows=T, H, 64], scales = q_scale_out
+ *                       [T, 1, 4, 16, J]; out fp32 [T, H, 128].
+ *   which = 1 (KCACHE): packed = kv_cache [NB, 1, 4, 64, 16], scales =
+ *                       kv_cache_scale [NB, 1, 4, 64]; slots int64 [rows]
+ *                       (or NULL: row r reads slot r); out fp32 [rows, 128];
+ *                       a slot outside [0, NB*64) gives a row of zeros.
+ *   H is used only for which = 0; NB and BS (= 64) only for which = 1.
+ *   out must be 16-byte aligned.
+ */
+int fp4idx_dequant_debug(int which, const uint8_t* packed, const uint8_t* scales, int64_t rows,
+                         int H, const int64_t* slots, int64_t NB, int BS, float* out, void* stream);
+
+/* Message describing the last non-zero return on the calling thread
+ * (thread-local; "" if there was none).  Owned by the library. */
+const char* fp4idx_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4IDX_H */

@@ -1,0 +1,257 @@
+// fp4idx_api.cpp -- extern "C" entry points of libfp4idx (declared and
+// documented in include/fp4idx.h): argument validation, error reporting and
+// kernel launch on the caller's stream.
+//
+// Host-side rejection follows ROCm/aiter PR 5484 "API": anything outside
+// head_dim 128, rope_dim 64, group 32, kv block 64 and n_heads % 16 == 0 is
+// refused with a message that names the argument.  Every check runs before
+// anything is enqueued, so a rejected call writes nothing and makes no HIP
+// call at all.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "fp4idx.h"
+#include "fp4idx_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr int kHeadDim = 128;
+constexpr int kRopeDim = 64;
+constexpr int kGroup = 32;
+constexpr int kKvBlock = 64;
+constexpr int kMaxHeads = 2048;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool is_flag(int v) { return v == 0 || v == 1; }
+
+// biased exponent of ceil_pow2(x) for x >= 0: (bits >> 23) + (mantissa != 0)
+int ceil_pow2_exponent(float x) {
+    uint32_t b;
+    std::memcpy(&b, &x, 4);
+    return (int)(b >> 23) + ((b & 0x7FFFFFu) != 0u ? 1 : 0);
+}
+
+int floor_exponent(float scale_floor) {
+    int e = ceil_pow2_exponent(scale_floor);
+    return e < 1 ? 1 : (e > 254 ? 254 : e);
+}
+
+// Shape checks shared by the q and k calls.
+int check_common(const char* fn, int D, int R, int group_size, int rope_offset, int positions_int64,
+                 int is_neox, int apply_hadamard, float scale_floor, int64_t T, int64_t max_pos) {
+    if (D != kHeadDim)
+        return fail(FP4IDX_EUNSUPPORTED, "%s: head_dim D must be 128 (got %d)", fn, D);
+    if (R != kRopeDim)
+        return fail(FP4IDX_EUNSUPPORTED, "%s: rope_dim R must be 64 (got %d)", fn, R);
+    if (group_size != kGroup)
+        return fail(FP4IDX_EUNSUPPORTED, "%s: group_size must be 32 (got %d)", fn, group_size);
+    if (rope_offset != 0 && rope_offset != kHeadDim - kRopeDim)
+        return fail(FP4IDX_EUNSUPPORTED, "%s: rope_offset must be 0 or 64 (got %d)", fn,
+                    rope_offset);
+    if (!is_flag(positions_int64))
+        return fail(FP4IDX_EINVAL, "%s: positions_int64 must be 0 or 1 (got %d)", fn,
+                    positions_int64);
+    if (!is_flag(is_neox))
+        return fail(FP4IDX_EINVAL, "%s: is_neox must be 0 or 1 (got %d)", fn, is_neox);
+    if (!is_flag(apply_hadamard))
+        return fail(FP4IDX_EINVAL, "%s: apply_hadamard must be 0 or 1 (got %d)", fn,
+                    apply_hadamard);
+    if (!std::isfinite(scale_floor) || scale_floor < 0.0f)
+        return fail(FP4IDX_EINVAL, "%s: scale_floor must be finite and >= 0 (got %g)", fn,
+                    (double)scale_floor);
+    if (T < 0) return fail(FP4IDX_EINVAL, "%s: T must be >= 0 (got %lld)", fn, (long long)T);
+    if (max_pos <= 0)
+        return fail(FP4IDX_EINVAL, "%s: max_pos must be > 0 (got %lld)", fn, (long long)max_pos);
+    if (max_pos > INT64_MAX / (kRopeDim * 4))
+        return fail(FP4IDX_EINVAL, "%s: max_pos too large (%lld)", fn, (long long)max_pos);
+    return FP4IDX_OK;
+}
+
+int check_ptr(const char* fn, const char* name, const void* p, uintptr_t align) {
+    if (p == nullptr) return fail(FP4IDX_EINVAL, "%s: %s must not be NULL", fn, name);
+    if (!aligned(p, align))
+        return fail(FP4IDX_EINVAL, "%s: %s must be %u-byte aligned (got %p)", fn, name,
+                    (unsigned)align, p);
+    return FP4IDX_OK;
+}
+
+#define FP4IDX_TRY(expr)                   \
+    do {                                   \
+        int rc_ = (expr);                  \
+        if (rc_ != FP4IDX_OK) return rc_;  \
+    } while (0)
+
+int hip_fail(const char* fn, hipError_t err) {
+    return fail(FP4IDX_EHIP, "%s: kernel launch failed: %s (%d)", fn, hipGetErrorString(err),
+                (int)err);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp4idx_q_rope_pack(const void* q, const void* positions, int positions_int64,
+                       const float* cos_sin, int64_t max_pos, const float* weights, int64_t T,
+                       int H, int D, int R, int rope_offset, int group_size, int is_neox,
+                       int apply_hadamard, float scale_floor, uint8_t* q_out,
+                       uint8_t* q_scale_out, float* weights_out, void* stream) {
+    static const char* fn = "fp4idx_q_rope_pack";
+    FP4IDX_TRY(check_common(fn, D, R, group_size, rope_offset, positions_int64, is_neox,
+                            apply_hadamard, scale_floor, T, max_pos));
+    if (H <= 0 || H % 16 != 0 || H > kMaxHeads)
+        return fail(FP4IDX_EUNSUPPORTED,
+                    "%s: n_heads H must be a positive multiple of 16 and <= %d (got %d)", fn,
+                    kMaxHeads, H);
+    if ((weights == nullptr) != (weights_out == nullptr))
+        return fail(FP4IDX_EINVAL, "%s: weights and weights_out must both be given or both NULL",
+                    fn);
+    if (T > INT64_MAX / ((int64_t)H * kHeadDim * 2))
+        return fail(FP4IDX_EINVAL, "%s: T too large (%lld)", fn, (long long)T);
+    if (T == 0) return FP4IDX_OK;
+    FP4IDX_TRY(check_ptr(fn, "q", q, 16));
+    FP4IDX_TRY(check_ptr(fn, "positions", positions, positions_int64 ? 8 : 4));
+    FP4IDX_TRY(check_ptr(fn, "cos_sin", cos_sin, 16));
+    FP4IDX_TRY(check_ptr(fn, "q_out", q_out, 16));
+    FP4IDX_TRY(check_ptr(fn, "q_scale_out", q_scale_out, 4));
+    if (weights != nullptr) {
+        FP4IDX_TRY(check_ptr(fn, "weights", weights, 4));
+        FP4IDX_TRY(check_ptr(fn, "weights_out", weights_out, 4));
+    }
+    fp4idx::QArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.positions = positions;
+    a.cos_sin = cos_sin;
+    a.weights = weights;
+    a.q_out = q_out;
+    a.q_scale_out = q_scale_out;
+    a.weights_out = weights_out;
+    a.T = T;
+    a.max_pos = max_pos;
+    a.H = H;
+    a.J = ((H / 16) + 3) / 4 * 4;
+    a.pos64 = positions_int64;
+    a.rope_offset = rope_offset;
+    a.e_lo = floor_exponent(scale_floor);
+    hipError_t err = fp4idx::launch_q_rope_pack(a, is_neox != 0, apply_hadamard != 0,
+                                                static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(fn, err);
+    return FP4IDX_OK;
+}
+
+int fp4idx_k_rope_pack_store(const void* k, const void* positions, int positions_int64,
+                             const float* cos_sin, int64_t max_pos, const int64_t* slot_mapping,
+                             const void* k_norm_gamma, float k_norm_eps, int64_t T, int D, int R,
+                             int rope_offset, int group_size, int is_neox, int apply_hadamard,
+                             float scale_floor, uint8_t* kv_cache, uint8_t* kv_cache_scale,
+                             int64_t NB, int BS, void* stream) {
+    static const char* fn = "fp4idx_k_rope_pack_store";
+    FP4IDX_TRY(check_common(fn, D, R, group_size, rope_offset, positions_int64, is_neox,
+                            apply_hadamard, scale_floor, T, max_pos));
+    if (BS != kKvBlock)
+        return fail(FP4IDX_EUNSUPPORTED, "%s: kv_block_size BS must be 64 (got %d)", fn, BS);
+    if (NB < 0) return fail(FP4IDX_EINVAL, "%s: NB must be >= 0 (got %lld)", fn, (long long)NB);
+    if (NB > INT64_MAX / ((int64_t)kKvBlock * kHeadDim))
+        return fail(FP4IDX_EINVAL, "%s: NB too large (%lld)", fn, (long long)NB);
+    if (k_norm_gamma != nullptr && (!std::isfinite(k_norm_eps) || k_norm_eps < 0.0f))
+        return fail(FP4IDX_EINVAL, "%s: k_norm_eps must be finite and >= 0 (got %g)", fn,
+                    (double)k_norm_eps);
+    if (T > INT64_MAX / (kHeadDim * 2))
+        return fail(FP4IDX_EINVAL, "%s: T too large (%lld)", fn, (long long)T);
+    if (T == 0) return FP4IDX_OK;
+    FP4IDX_TRY(check_ptr(fn, "k", k, 16));
+    FP4IDX_TRY(check_ptr(fn, "positions", positions, positions_int64 ? 8 : 4));
+    FP4IDX_TRY(check_ptr(fn, "cos_sin", cos_sin, 16));
+    FP4IDX_TRY(check_ptr(fn, "slot_mapping", slot_mapping, 8));
+    if (k_norm_gamma != nullptr) FP4IDX_TRY(check_ptr(fn, "k_norm_gamma", k_norm_gamma, 16));
+    if (NB > 0) {
+        FP4IDX_TRY(check_ptr(fn, "kv_cache", kv_cache, 16));
+        FP4IDX_TRY(check_ptr(fn, "kv_cache_scale", kv_cache_scale, 4));
+    }
+    fp4idx::KArgs a{};
+    a.k = static_cast<const uint16_t*>(k);
+    a.positions = positions;
+    a.cos_sin = cos_sin;
+    a.slot_mapping = slot_mapping;
+    a.gamma = static_cast<const uint16_t*>(k_norm_gamma);
+    a.kv_cache = kv_cache;
+    a.kv_cache_scale = kv_cache_scale;
+    a.T = T;
+    a.max_pos = max_pos;
+    a.nslots = NB * kKvBlock;
+    a.eps = k_norm_eps;
+    a.pos64 = positions_int64;
+    a.rope_offset = rope_offset;
+    a.e_lo = floor_exponent(scale_floor);
+    hipError_t err = fp4idx::launch_k_rope_pack_store(a, is_neox != 0, apply_hadamard != 0,
+                                                      static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(fn, err);
+    return FP4IDX_OK;
+}
+
+int fp4idx_dequant_debug(int which, const uint8_t* packed, const uint8_t* scales, int64_t rows,
+                         int H, const int64_t* slots, int64_t NB, int BS, float* out,
+                         void* stream) {
+    static const char* fn = "fp4idx_dequant_debug";
+    if (which != 0 && which != 1)
+        return fail(FP4IDX_EINVAL, "%s: which must be 0 (Q) or 1 (KCACHE) (got %d)", fn, which);
+    if (rows < 0) return fail(FP4IDX_EINVAL, "%s: rows must be >= 0 (got %lld)", fn, (long long)rows);
+    fp4idx::DArgs a{};
+    a.which = which;
+    a.rows = rows;
+    if (which == 0) {
+        if (H <= 0 || H % 16 != 0 || H > kMaxHeads)
+            return fail(FP4IDX_EUNSUPPORTED,
+                        "%s: n_heads H must be a positive multiple of 16 and <= %d (got %d)", fn,
+                        kMaxHeads, H);
+        if (rows > INT64_MAX / ((int64_t)H * kHeadDim * 4))
+            return fail(FP4IDX_EINVAL, "%s: rows too large (%lld)", fn, (long long)rows);
+        a.H = H;
+        a.J = ((H / 16) + 3) / 4 * 4;
+    } else {
+        if (BS != kKvBlock)
+            return fail(FP4IDX_EUNSUPPORTED, "%s: kv_block_size BS must be 64 (got %d)", fn, BS);
+        if (NB < 0 || NB > INT64_MAX / ((int64_t)kKvBlock * kHeadDim))
+            return fail(FP4IDX_EINVAL, "%s: NB out of range (%lld)", fn, (long long)NB);
+        if (rows > INT64_MAX / (kHeadDim * 4))
+            return fail(FP4IDX_EINVAL, "%s: rows too large (%lld)", fn, (long long)rows);
+        a.nslots = NB * kKvBlock;
+    }
+    if (rows == 0) return FP4IDX_OK;
+    FP4IDX_TRY(check_ptr(fn, "out", out, 16));
+    // with an empty cache every slot is out of range and no code byte is read
+    if (which == 0 || NB > 0) {
+        FP4IDX_TRY(check_ptr(fn, "packed", packed, 4));
+        FP4IDX_TRY(check_ptr(fn, "scales", scales, 1));
+    }
+    if (slots != nullptr) FP4IDX_TRY(check_ptr(fn, "slots", slots, 8));
+    a.packed = packed;
+    a.scales = scales;
+    a.slots = which == 1 ? slots : nullptr;
+    a.out = out;
+    hipError_t err = fp4idx::launch_dequant(a, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(fn, err);
+    return FP4IDX_OK;
+}
+
+const char* fp4idx_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// fp4idx_internal.h -- launch descriptors shared by the C-ABI layer
+// (fp4idx_api.cpp) and the kernels (fp4idx_kernels.hip).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace fp4idx {
+
+// Arguments of one query launch.  All pointers are device pointers that the
+// C-ABI layer has already validated (non-null, aligned, sizes consistent).
+struct QArgs {
+    const uint16_t* q;          // bf16 [T, H, 128]
+    const void* positions;      // int32 or int64 [T]
+    const float* cos_sin;       // fp32 [max_pos, 64]
+    const float* weights;       // fp32 [T, H] or nullptr
+    uint8_t* q_out;             // u8 [T, H, 64]
+    uint8_t* q_scale_out;       // u8 [T, 1, 4, 16, J]
+    float* weights_out;         // fp32 [T, H] or nullptr
+    int64_t T;
+    int64_t max_pos;
+    int H;
+    int J;                      // round_up(H/16, 4)
+    int pos64;                  // positions are int64
+    int rope_offset;            // 0 or 64
+    int e_lo;                   // clamp(E(scale_floor), 1, 254)
+};
+
+struct KArgs {
+    const uint16_t* k;          // bf16 [T, 128]
+    const void* positions;
+    const float* cos_sin;
+    const int64_t* slot_mapping;  // [T]
+    const uint16_t* gamma;      // bf16 [128] or nullptr
+    uint8_t* kv_cache;          // u8 [NB, 1, 4, 64, 16]
+    uint8_t* kv_cache_scale;    // u8 [NB, 1, 4, 64]
+    int64_t T;
+    int64_t max_pos;
+    int64_t nslots;             // NB * 64
+    float eps;
+    int pos64;
+    int rope_offset;
+    int e_lo;
+};
+
+struct DArgs {
+    const uint8_t* packed;
+    const uint8_t* scales;
+    const int64_t* slots;       // KCACHE only, may be nullptr
+    float* out;
+    int64_t rows;
+    int64_t nslots;             // KCACHE: NB * 64
+    int which;                  // 0 = Q, 1 = KCACHE
+    int H;
+    int J;
+};
+
+hipError_t launch_q_rope_pack(const QArgs& a, bool is_neox, bool hadamard, hipStream_t stream);
+hipError_t launch_k_rope_pack_store(const KArgs& a, bool is_neox, bool hadamard,
+                                    hipStream_t stream);
+hipError_t launch_dequant(const DArgs& a, hipStream_t stream);
+
+}  // namespace fp4idx

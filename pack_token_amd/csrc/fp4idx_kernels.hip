@@ -1,0 +1,554 @@
+// fp4idx_kernels.hip -- gfx950 kernels of the fused FP4 indexer producer.
+//
+// What is computed (per token; ROCm/aiter PR 5484 "API" and "One deliberate
+// deviation", sgl-project/sglang PR 39656 "Summary" and review, ROCm/aiter
+// PR 4029 "Changes"):
+//   optional key RMSNorm -> RoPE on a 64-wide slice (bf16 round trip) ->
+//   optional 128-point Hadamard (bf16) -> per 32-group UE8M0 exponent ->
+//   E2M1 codes (RNE, sign kept on zero) -> two codes per byte -> q_out /
+//   q_scale_out / weights_out, or the paged key cache and its interleaved
+//   scale row.
+//
+// Data layout in registers.  A 128-dim bf16 row is 16 chunks of 8 values
+// (16 bytes).  Every lane loads one chunk with a 16-byte load.  Lanes are
+// mapped to chunks so that every cross-lane step of the method is a single
+// DPP lane pattern that can be fused into the consuming VALU op:
+//     chunk(L) = L ^ (bit2(L) ? 3 : 0)          (L = lane within 16)
+// so chunk c ^ 1 sits at lane L ^ 1 (DPP quad_perm), c ^ 2 at L ^ 2
+// (quad_perm), c ^ 4 at L ^ 7 (row_half_mirror) and c ^ 8 at L ^ 8
+// (row_ror:8).  The 4 chunks of a 32-group are always one quad of lanes,
+// the neox RoPE partner (slice element i <-> i+32, i.e. chunk c ^ 4) is the
+// half-row mirror, and the Hadamard strides 8/16/32/64 and the RMSNorm
+// fold-by-halves steps map to the four patterns above.
+//
+// Nothing here is a dense contraction, so there is no MFMA: the path is
+// bound by HBM bandwidth, and the kernels are written to stream q once with
+// 16-byte loads and to issue no more VALU work than the stream can hide.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp4idx_internal.h"
+
+namespace fp4idx {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+// DPP lane patterns (CDNA data-parallel primitives).
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]: lane i <- i ^ 1
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]: lane i <- i ^ 2
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror: lane i <- i ^ 7 (within 8)
+constexpr int kDppRor8 = 0x128;       // row_ror:8: lane i <- i ^ 8 (within 16)
+
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlock = 64 * kWavesPerBlock;
+
+// fp32(1/sqrt(128)), the orthonormal Hadamard scale.
+constexpr uint32_t kHadamardScaleBits = 0x3DB504F3u;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+    return __uint_as_float(dpp<CTRL>(__float_as_uint(v)));
+}
+
+__device__ __forceinline__ int chunk_of(int lane16) {
+    return lane16 ^ (((lane16 >> 2) & 1) * 3);
+}
+
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint4 load16(const void* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+// ---- bf16 <-> fp32 ---------------------------------------------------------
+
+__device__ __forceinline__ void unpack8(uint4 v, float x[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+
+// two fp32 -> packed bf16x2 (a in the low half), round to nearest even
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+__device__ __forceinline__ uint4 pack8(const float x[8]) {
+    return make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                      pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
+}
+
+__device__ __forceinline__ uint4 select4(bool c, uint4 a, uint4 b) {
+    return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+}
+
+// ---- quantizer ---------------------------------------------------------------
+// UE8M0 exponent of a group whose largest |value| is the bf16 number with
+// magnitude bits m: the least e with amax <= 6 * 2^(e-127), which equals the
+// biased exponent of ceil_pow2(fl(amax / 6)) for every bf16 amax, i.e.
+// ((m + 0x3F) >> 7) - 2, then raised to the floor's exponent e_lo >= 1.
+// Codes come from the gfx950 scaled converter, which divides by the
+// power-of-two scale 2^(e-127) exactly and rounds to the E2M1 grid with ties
+// to even, keeping the sign of zero.
+
+struct Q8 {
+    uint32_t codes;  // 8 nibbles: element 2b low, 2b+1 high nibble of byte b
+    int e;
+};
+
+__device__ __forceinline__ Q8 quant8(uint4 v, int e_lo) {
+    const u16x2_t a0 = __builtin_bit_cast(u16x2_t, v.x & 0x7FFF7FFFu);
+    const u16x2_t a1 = __builtin_bit_cast(u16x2_t, v.y & 0x7FFF7FFFu);
+    const u16x2_t a2 = __builtin_bit_cast(u16x2_t, v.z & 0x7FFF7FFFu);
+    const u16x2_t a3 = __builtin_bit_cast(u16x2_t, v.w & 0x7FFF7FFFu);
+    const u16x2_t m2 = __builtin_elementwise_max(__builtin_elementwise_max(a0, a1),
+                                                 __builtin_elementwise_max(a2, a3));
+    uint32_t m = max((uint32_t)m2.x, (uint32_t)m2.y);
+    m = max(m, dpp<kDppXor1>(m));
+    m = max(m, dpp<kDppXor2>(m));
+    const int e = max((int)((m + 0x3Fu) >> 7) - 2, e_lo);
+    const float scale = __uint_as_float((uint32_t)e << 23);
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, v.x), scale, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, v.y), scale, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, v.z), scale, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, v.w), scale, 3);
+    return {r, e};
+}
+
+// ---- RoPE ------------------------------------------------------------------
+// Slice chunk j (0..7) of the 64-wide rotated slice holds slice elements
+// 8j..8j+7.  Every element is updated as x' = bf16(fl(x*C) + fl(p*S)) where p
+// is its pair partner; with S = -s for the first element of a pair this is
+// a' = a*c - b*s and b' = b*c + a*s exactly (negation is exact).
+//   neox:        pair (i, i+32): chunk j <-> j ^ 4, same element, C = cos[i],
+//                S = -+sin[i] with i = 8 (j & 3) + e
+//   interleaved: pair (2i, 2i+1) inside the lane, i = 4j + e/2
+template <bool NEOX>
+__device__ __forceinline__ void rope_coeffs(const float* cs_row, int j, float C[8], float S[8]) {
+    if (NEOX) {
+        const int i0 = 8 * (j & 3);
+        const float4 c0 = *reinterpret_cast<const float4*>(cs_row + i0);
+        const float4 c1 = *reinterpret_cast<const float4*>(cs_row + i0 + 4);
+        const float4 s0 = *reinterpret_cast<const float4*>(cs_row + 32 + i0);
+        const float4 s1 = *reinterpret_cast<const float4*>(cs_row + 32 + i0 + 4);
+        const uint32_t neg = (j < 4) ? 0x80000000u : 0u;
+        const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            C[e] = c[e];
+            S[e] = __uint_as_float(__float_as_uint(s[e]) ^ neg);
+        }
+    } else {
+        const int i0 = 4 * j;
+        const float4 c4 = *reinterpret_cast<const float4*>(cs_row + i0);
+        const float4 s4 = *reinterpret_cast<const float4*>(cs_row + 32 + i0);
+        const float c[4] = {c4.x, c4.y, c4.z, c4.w};
+        const float s[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            C[2 * p] = c[p];
+            C[2 * p + 1] = c[p];
+            S[2 * p] = -s[p];
+            S[2 * p + 1] = s[p];
+        }
+    }
+}
+
+template <bool NEOX>
+__device__ __forceinline__ uint4 rope8(uint4 v, const float C[8], const float S[8]) {
+    float x[8], p[8];
+    unpack8(v, x);
+    if (NEOX) {
+        const uint4 pv = make_uint4(dpp<kDppHalfMirror>(v.x), dpp<kDppHalfMirror>(v.y),
+                                    dpp<kDppHalfMirror>(v.z), dpp<kDppHalfMirror>(v.w));
+        unpack8(pv, p);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = x[e ^ 1];
+    }
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float xc = x[e] * C[e];
+        const float ps = p[e] * S[e];
+        y[e] = xc + ps;
+    }
+    return pack8(y);
+}
+
+// ---- Hadamard (row of 16 lanes) ----------------------------------------------
+// Natural-order FWHT: butterflies of stride 1, 2, 4 inside the lane, then
+// strides 8, 16, 32, 64 across lanes (chunk bits 0..3).  The lower element
+// of a pair becomes u + w and the upper u - w; the upper lane computes it as
+// partner + (-mine), which is the same IEEE operation.
+template <int CTRL>
+__device__ __forceinline__ void fwht_cross(float x[8], bool upper) {
+    const uint32_t neg = upper ? 0x80000000u : 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float p = dppf<CTRL>(x[e]);
+        const float m = __uint_as_float(__float_as_uint(x[e]) ^ neg);
+        x[e] = p + m;
+    }
+}
+
+__device__ __forceinline__ uint4 hadamard8(uint4 v, int c) {
+    float x[8];
+    unpack8(v, x);
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (j & h) continue;
+            const float u = x[j], w = x[j + h];
+            x[j] = u + w;
+            x[j + h] = u - w;
+        }
+    }
+    fwht_cross<kDppXor1>(x, (c & 1) != 0);
+    fwht_cross<kDppXor2>(x, (c & 2) != 0);
+    fwht_cross<kDppHalfMirror>(x, (c & 4) != 0);
+    fwht_cross<kDppRor8>(x, (c & 8) != 0);
+    const float sc = __uint_as_float(kHadamardScaleBits);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = x[e] * sc;
+    return pack8(x);
+}
+
+// ---- key RMSNorm (row of 16 lanes) -------------------------------------------
+// Correctly rounded fp32 sqrt and reciprocal: a float64 candidate, then an
+// exact check against the midpoints to the neighbouring floats (products of
+// <= 25-bit significands are exact in float64).
+__device__ __forceinline__ float sqrt_rn(float v) {
+    if (!(v > 0.0f)) return __builtin_sqrtf(v);
+    float s = (float)__builtin_sqrt((double)v);
+    const uint32_t b = __float_as_uint(s);
+    const double hi = 0.5 * ((double)s + (double)__uint_as_float(b + 1));
+    const double lo = 0.5 * ((double)s + (double)__uint_as_float(b - 1));
+    if ((double)v > hi * hi) s = __uint_as_float(b + 1);
+    else if ((double)v < lo * lo) s = __uint_as_float(b - 1);
+    return s;
+}
+
+__device__ __forceinline__ float rcp_rn(float d) {
+    float r = (float)(1.0 / (double)d);
+    const uint32_t b = __float_as_uint(r);
+    if (!(r > 0.0f) || b >= 0x7F800000u) return r;
+    const double hi = 0.5 * ((double)r + (double)__uint_as_float(b + 1));
+    const double lo = 0.5 * ((double)r + (double)__uint_as_float(b - 1));
+    if ((double)d * hi < 1.0) r = __uint_as_float(b + 1);
+    else if ((double)d * lo > 1.0) r = __uint_as_float(b - 1);
+    return r;
+}
+
+// Sum of squares folded by halves (element i with i+64, then +32, +16, +8
+// across lanes, +4, +2, +1 inside the lane).  Both lanes of every cross-lane
+// pair compute the same sum, so every lane of the row ends with the same ss.
+__device__ __forceinline__ uint4 rmsnorm8(uint4 v, const float G[8], float eps) {
+    float x[8], p[8];
+    unpack8(v, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = x[e] * x[e];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = p[e] + dppf<kDppRor8>(p[e]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = p[e] + dppf<kDppHalfMirror>(p[e]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = p[e] + dppf<kDppXor2>(p[e]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = p[e] + dppf<kDppXor1>(p[e]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] = p[e] + p[e + 4];
+    p[0] = p[0] + p[2];
+    p[1] = p[1] + p[3];
+    p[0] = p[0] + p[1];
+    const float mean = p[0] * 0.0078125f;  // ss / 128, exact scaling
+    const float r = rcp_rn(sqrt_rn(mean + eps));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float y = x[e] * r;
+        x[e] = y * G[e];
+    }
+    return pack8(x);
+}
+
+__device__ __forceinline__ int64_t clamped_position(const void* positions, int pos64, int64_t t,
+                                                    int64_t max_pos) {
+    int64_t p = pos64 ? reinterpret_cast<const int64_t*>(positions)[t]
+                      : (int64_t) reinterpret_cast<const int32_t*>(positions)[t];
+    p = p < 0 ? 0 : p;
+    return p >= max_pos ? max_pos - 1 : p;
+}
+
+// ---- query kernels ------------------------------------------------------------
+// One wavefront per token.  The token's scale bytes are gathered in LDS
+// ([4][16][J] bytes, pads zero) and written out as whole dwords at the end.
+
+__device__ __forceinline__ void q_token_prologue(const QArgs& a, int64_t t, int lane,
+                                                 uint32_t* sc) {
+    for (int i = lane; i < 16 * a.J; i += 64) sc[i] = 0u;
+    if (a.weights != nullptr) {
+        const float* w = a.weights + t * a.H;
+        float* wo = a.weights_out + t * a.H;
+        for (int h = lane; h < a.H; h += 64) wo[h] = w[h];
+    }
+}
+
+__device__ __forceinline__ void q_token_epilogue(const QArgs& a, int64_t t, int lane,
+                                                 const uint32_t* sc) {
+    wave_sync();
+    uint32_t* dst = reinterpret_cast<uint32_t*>(a.q_scale_out + t * 64 * (int64_t)a.J);
+    for (int i = lane; i < 16 * a.J; i += 64) dst[i] = sc[i];
+}
+
+// Without the Hadamard, the rotated and the plain halves of a head never mix,
+// so every 16-byte load of a wave covers one half (128 bytes) of 8 heads:
+// lanes 8k..8k+7 take head hb+k.  Rotated and plain halves go through
+// separate instruction streams and no lane computes a RoPE it throws away.
+template <bool NEOX>
+__global__ __launch_bounds__(kBlock) void q_split_kernel(QArgs a) {
+    extern __shared__ uint32_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    if (t >= a.T) return;
+    const int H = a.H;
+    const int J = a.J;
+    uint32_t* sc = smem + wave * 16 * J;
+    uint8_t* scb = reinterpret_cast<uint8_t*>(sc);
+    q_token_prologue(a, t, lane, sc);
+
+    const int64_t pos = clamped_position(a.positions, a.pos64, t, a.max_pos);
+    const int c = chunk_of(lane & 7);  // chunk within the 64-wide half
+    const int hsub = lane >> 3;
+    float C[8], S[8];
+    rope_coeffs<NEOX>(a.cos_sin + pos * 64, c, C, S);
+
+    const int ro = a.rope_offset;
+    const int nro = 64 - ro;
+    const int g_rot = ro / 32 + (c >> 2);
+    const int g_pln = nro / 32 + (c >> 2);
+    const bool writer = (lane & 3) == 0;
+    const uint16_t* qt = a.q + t * (int64_t)H * 128;
+    uint8_t* ot = a.q_out + t * (int64_t)H * 64;
+
+    for (int hb = 0; hb < H; hb += 16) {
+        const int h0 = hb + hsub;
+        const int h1 = h0 + 8;
+        const uint4 p0 = load16(qt + h0 * 128 + nro + 8 * c);
+        const uint4 r0 = load16(qt + h0 * 128 + ro + 8 * c);
+        const uint4 p1 = load16(qt + h1 * 128 + nro + 8 * c);
+        const uint4 r1 = load16(qt + h1 * 128 + ro + 8 * c);
+        const Q8 qp0 = quant8(p0, a.e_lo);
+        const Q8 qr0 = quant8(rope8<NEOX>(r0, C, S), a.e_lo);
+        const Q8 qp1 = quant8(p1, a.e_lo);
+        const Q8 qr1 = quant8(rope8<NEOX>(r1, C, S), a.e_lo);
+        *reinterpret_cast<uint32_t*>(ot + h0 * 64 + nro / 2 + 4 * c) = qp0.codes;
+        *reinterpret_cast<uint32_t*>(ot + h0 * 64 + ro / 2 + 4 * c) = qr0.codes;
+        *reinterpret_cast<uint32_t*>(ot + h1 * 64 + nro / 2 + 4 * c) = qp1.codes;
+        *reinterpret_cast<uint32_t*>(ot + h1 * 64 + ro / 2 + 4 * c) = qr1.codes;
+        if (writer) {
+            scb[(g_pln * 16 + (h0 & 15)) * J + (h0 >> 4)] = (uint8_t)qp0.e;
+            scb[(g_rot * 16 + (h0 & 15)) * J + (h0 >> 4)] = (uint8_t)qr0.e;
+            scb[(g_pln * 16 + (h1 & 15)) * J + (h1 >> 4)] = (uint8_t)qp1.e;
+            scb[(g_rot * 16 + (h1 & 15)) * J + (h1 >> 4)] = (uint8_t)qr1.e;
+        }
+    }
+    q_token_epilogue(a, t, lane, sc);
+}
+
+// With the Hadamard every output mixes the whole 128-row, so a wave-load is 4
+// full heads (16 lanes each); RoPE is computed on every lane and kept only on
+// the lanes of the rotated slice.
+template <bool NEOX>
+__global__ __launch_bounds__(kBlock) void q_row_kernel(QArgs a) {
+    extern __shared__ uint32_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    if (t >= a.T) return;
+    const int H = a.H;
+    const int J = a.J;
+    uint32_t* sc = smem + wave * 16 * J;
+    uint8_t* scb = reinterpret_cast<uint8_t*>(sc);
+    q_token_prologue(a, t, lane, sc);
+
+    const int64_t pos = clamped_position(a.positions, a.pos64, t, a.max_pos);
+    const int c = chunk_of(lane & 15);
+    const int hsub = lane >> 4;
+    const bool rot_lane = (c >> 3) == (a.rope_offset >> 6);
+    float C[8], S[8];
+    rope_coeffs<NEOX>(a.cos_sin + pos * 64, c & 7, C, S);
+    const int g = c >> 2;
+    const bool writer = (lane & 3) == 0;
+    const uint16_t* qt = a.q + t * (int64_t)H * 128;
+    uint8_t* ot = a.q_out + t * (int64_t)H * 64;
+
+    for (int hb = 0; hb < H; hb += 8) {
+        const int h0 = hb + hsub;
+        const int h1 = h0 + 4;
+        const uint4 v0 = load16(qt + h0 * 128 + 8 * c);
+        const uint4 v1 = load16(qt + h1 * 128 + 8 * c);
+        const uint4 w0 = hadamard8(select4(rot_lane, rope8<NEOX>(v0, C, S), v0), c);
+        const uint4 w1 = hadamard8(select4(rot_lane, rope8<NEOX>(v1, C, S), v1), c);
+        const Q8 q0 = quant8(w0, a.e_lo);
+        const Q8 q1 = quant8(w1, a.e_lo);
+        *reinterpret_cast<uint32_t*>(ot + h0 * 64 + 4 * c) = q0.codes;
+        *reinterpret_cast<uint32_t*>(ot + h1 * 64 + 4 * c) = q1.codes;
+        if (writer) {
+            scb[(g * 16 + (h0 & 15)) * J + (h0 >> 4)] = (uint8_t)q0.e;
+            scb[(g * 16 + (h1 & 15)) * J + (h1 >> 4)] = (uint8_t)q1.e;
+        }
+    }
+    q_token_epilogue(a, t, lane, sc);
+}
+
+// ---- key kernel ----------------------------------------------------------------
+// 16 lanes per token, 4 tokens per wavefront.  A token whose slot is outside
+// the cache leaves as a whole row of 16 lanes, so the DPP patterns (all
+// within a row) only ever read lanes of the same token.
+template <bool NEOX, bool NORM, bool HAD>
+__global__ __launch_bounds__(kBlock) void k_row_kernel(KArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * (kBlock / 16) + (threadIdx.x >> 4);
+    if (t >= a.T) return;
+    const int64_t slot = a.slot_mapping[t];
+    if (slot < 0 || slot >= a.nslots) return;
+    const int64_t pos = clamped_position(a.positions, a.pos64, t, a.max_pos);
+    const int c = chunk_of(lane & 15);
+
+    uint4 v = load16(a.k + t * 128 + 8 * c);
+    if (NORM) {
+        float G[8];
+        unpack8(load16(a.gamma + 8 * c), G);
+        v = rmsnorm8(v, G, a.eps);
+    }
+    float C[8], S[8];
+    rope_coeffs<NEOX>(a.cos_sin + pos * 64, c & 7, C, S);
+    const bool rot_lane = (c >> 3) == (a.rope_offset >> 6);
+    v = select4(rot_lane, rope8<NEOX>(v, C, S), v);
+    if (HAD) v = hadamard8(v, c);
+    const Q8 q = quant8(v, a.e_lo);
+
+    const int64_t blk = slot >> 6;
+    const int p = (int)(slot & 63);
+    const int g = c >> 2;
+    const int64_t row = blk * 4 + g;
+    *reinterpret_cast<uint32_t*>(a.kv_cache + (row * 64 + p) * 16 + 4 * (c & 3)) = q.codes;
+    if ((c & 3) == 0) a.kv_cache_scale[row * 64 + (p & 15) * 4 + (p >> 4)] = (uint8_t)q.e;
+}
+
+// ---- dequantization (debug reader) -------------------------------------------
+// One thread per 8 consecutive values (4 code bytes).
+__device__ __forceinline__ float e2m1_value(uint32_t nib) {
+    // magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6} in half units: 0,1,2,3,4,6,8,12
+    const uint32_t half_units = (0xC8643210u >> (4 * (nib & 7))) & 0xF;
+    const float v = (float)half_units * 0.5f;
+    return (nib & 8) ? -v : v;
+}
+
+__device__ __forceinline__ float e8m0_value(uint32_t e) {
+    if (e == 255u) return __uint_as_float(0x7FC00000u);
+    if (e == 0u) return __uint_as_float(0x00400000u);  // 2^-127
+    return __uint_as_float(e << 23);
+}
+
+__global__ __launch_bounds__(256) void dequant_kernel(DArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t chunks_per_row = (a.which == 0) ? (int64_t)a.H * 16 : 16;
+    if (i >= a.rows * chunks_per_row) return;
+    const int64_t row = i / chunks_per_row;
+    const int c = (int)(i % 16);
+    const int g = c >> 2;
+    uint32_t codes = 0, e = 0;
+    bool zero = false;
+    float* out;
+    if (a.which == 0) {
+        const int h = (int)((i / 16) % a.H);
+        const int64_t t = row;
+        codes = *reinterpret_cast<const uint32_t*>(a.packed + (t * a.H + h) * 64 + 4 * c);
+        e = a.scales[t * 64 * (int64_t)a.J + (g * 16 + (h & 15)) * a.J + (h >> 4)];
+        out = a.out + (t * a.H + h) * 128 + 8 * c;
+    } else {
+        const int64_t slot = a.slots ? a.slots[row] : row;
+        out = a.out + row * 128 + 8 * c;
+        if (slot < 0 || slot >= a.nslots) {
+            zero = true;
+        } else {
+            const int64_t r = (slot >> 6) * 4 + g;
+            const int p = (int)(slot & 63);
+            codes = *reinterpret_cast<const uint32_t*>(a.packed + (r * 64 + p) * 16 + 4 * (c & 3));
+            e = a.scales[r * 64 + (p & 15) * 4 + (p >> 4)];
+        }
+    }
+    float y[8];
+    const float s = e8m0_value(e);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = zero ? 0.0f : e2m1_value(codes >> (4 * k)) * s;
+    reinterpret_cast<float4*>(out)[0] = make_float4(y[0], y[1], y[2], y[3]);
+    reinterpret_cast<float4*>(out)[1] = make_float4(y[4], y[5], y[6], y[7]);
+}
+
+template <typename K, typename A>
+hipError_t launch(K kernel, int64_t blocks, size_t lds, hipStream_t stream, const A& a) {
+    A copy = a;
+    void* args[] = {&copy};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)blocks),
+                           dim3(kBlock), args, lds, stream);
+}
+
+}  // namespace
+
+hipError_t launch_q_rope_pack(const QArgs& a, bool is_neox, bool hadamard, hipStream_t stream) {
+    if (a.T == 0) return hipSuccess;
+    const int64_t blocks = (a.T + kWavesPerBlock - 1) / kWavesPerBlock;
+    const size_t lds = (size_t)kWavesPerBlock * 16 * a.J * sizeof(uint32_t);
+    if (hadamard)
+        return is_neox ? launch(q_row_kernel<true>, blocks, lds, stream, a)
+                       : launch(q_row_kernel<false>, blocks, lds, stream, a);
+    return is_neox ? launch(q_split_kernel<true>, blocks, lds, stream, a)
+                   : launch(q_split_kernel<false>, blocks, lds, stream, a);
+}
+
+hipError_t launch_k_rope_pack_store(const KArgs& a, bool is_neox, bool hadamard,
+                                    hipStream_t stream) {
+    if (a.T == 0) return hipSuccess;
+    const int64_t blocks = (a.T + kBlock / 16 - 1) / (kBlock / 16);
+    const bool norm = a.gamma != nullptr;
+    const int sel = (is_neox ? 4 : 0) | (norm ? 2 : 0) | (hadamard ? 1 : 0);
+    switch (sel) {
+        case 0: return launch(k_row_kernel<false, false, false>, blocks, 0, stream, a);
+        case 1: return launch(k_row_kernel<false, false, true>, blocks, 0, stream, a);
+        case 2: return launch(k_row_kernel<false, true, false>, blocks, 0, stream, a);
+        case 3: return launch(k_row_kernel<false, true, true>, blocks, 0, stream, a);
+        case 4: return launch(k_row_kernel<true, false, false>, blocks, 0, stream, a);
+        case 5: return launch(k_row_kernel<true, false, true>, blocks, 0, stream, a);
+        case 6: return launch(k_row_kernel<true, true, false>, blocks, 0, stream, a);
+        default: return launch(k_row_kernel<true, true, true>, blocks, 0, stream, a);
+    }
+}
+
+hipError_t launch_dequant(const DArgs& a, hipStream_t stream) {
+    const int64_t chunks = a.rows * (a.which == 0 ? (int64_t)a.H * 16 : 16);
+    if (chunks == 0) return hipSuccess;
+    return launch(dequant_kernel, (chunks + 255) / 256, 0, stream, a);
+}
+
+}  // namespace fp4idx

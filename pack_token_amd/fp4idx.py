@@ -1,0 +1,183 @@
+"""Thin ctypes binding of libfp4idx (C ABI in include/fp4idx.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libfp4idx.so.  Tensors are torch tensors on the GPU; outputs the
+caller does not pass are allocated with torch (device memory is torch's job
+here).  Work is enqueued on torch's current stream unless `stream` is given.
+The library must be built (``python -m pack_token_amd.build`` or
+``__graft_entry__.build()``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp4idx.so")
+
+OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
+HEAD_DIM, ROPE_DIM, GROUP, KV_BLOCK = 128, 64, 32, 64
+DEFAULT_SCALE_FLOOR = 2.0 ** -126
+
+_lib = None
+_lock = threading.Lock()
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_i64 = ctypes.c_int64
+_f = ctypes.c_float
+
+
+class Fp4IdxError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[code {code}] {message}")
+        self.code = code
+        self.message = message
+
+
+def lib():
+    """Load libfp4idx.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with `python -m pack_token_amd.build` "
+                    "(the FP4 indexer has no CPU or PyTorch fallback)")
+            L = ctypes.CDLL(LIB_PATH)
+            L.fp4idx_q_rope_pack.argtypes = [_p, _p, _i, _p, _i64, _p, _i64, _i, _i, _i, _i, _i, _i,
+                                             _i, _f, _p, _p, _p, _p]
+            L.fp4idx_q_rope_pack.restype = _i
+            L.fp4idx_k_rope_pack_store.argtypes = [_p, _p, _i, _p, _i64, _p, _p, _f, _i64, _i, _i,
+                                                   _i, _i, _i, _i, _f, _p, _p, _i64, _i, _p]
+            L.fp4idx_k_rope_pack_store.restype = _i
+            L.fp4idx_dequant_debug.argtypes = [_i, _p, _p, _i64, _i, _p, _i64, _i, _p, _p]
+            L.fp4idx_dequant_debug.restype = _i
+            L.fp4idx_last_error.argtypes = []
+            L.fp4idx_last_error.restype = ctypes.c_char_p
+            _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().fp4idx_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise Fp4IdxError(rc, last_error())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
+
+
+def _require(t, name, dtypes, device=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}; expected one of {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def q_scale_cols(H: int) -> int:
+    return ((H // 16) + 3) // 4 * 4
+
+
+def q_rope_pack(q, positions, cos_sin, weights=None, *, q_out=None, q_scale_out=None,
+                weights_out=None, is_neox=True, rope_offset=64, apply_hadamard=False,
+                scale_floor=DEFAULT_SCALE_FLOOR, stream=None):
+    """fp4idx_q_rope_pack.  q bf16 [T,H,128]; positions int32/int64 [T]; cos_sin fp32
+    [max_pos,64]; weights fp32 [T,H] or None.  Returns (q_out, q_scale_out, weights_out)."""
+    T, H, D = q.shape
+    dev = q.device
+    _require(q, "q", (torch.bfloat16, torch.int16, torch.uint16))
+    _require(positions, "positions", (torch.int32, torch.int64), dev)
+    _require(cos_sin, "cos_sin", (torch.float32,), dev)
+    _require(weights, "weights", (torch.float32,), dev)
+    J = q_scale_cols(H)
+    if q_out is None:
+        q_out = torch.empty((T, H, D // 2), dtype=torch.uint8, device=dev)
+    if q_scale_out is None:
+        q_scale_out = torch.empty((T, D // 128 if D >= 128 else 1, 4, 16, J), dtype=torch.uint8,
+                                  device=dev)
+    if weights is not None and weights_out is None:
+        weights_out = torch.empty_like(weights)
+    _require(q_out, "q_out", (torch.uint8,), dev)
+    _require(q_scale_out, "q_scale_out", (torch.uint8,), dev)
+    _require(weights_out, "weights_out", (torch.float32,), dev)
+    rc = lib().fp4idx_q_rope_pack(
+        _ptr(q), _ptr(positions), int(positions.dtype == torch.int64), _ptr(cos_sin),
+        cos_sin.shape[0], _ptr(weights), T, H, D, ROPE_DIM, rope_offset, GROUP, int(is_neox),
+        int(apply_hadamard), scale_floor, _ptr(q_out), _ptr(q_scale_out), _ptr(weights_out),
+        _stream_handle(stream))
+    _check(rc)
+    return q_out, q_scale_out, weights_out
+
+
+def k_rope_pack_store(k, positions, cos_sin, slot_mapping, kv_cache, kv_cache_scale, *,
+                      k_norm_gamma=None, k_norm_eps=1e-6, is_neox=True, rope_offset=64,
+                      apply_hadamard=False, scale_floor=DEFAULT_SCALE_FLOOR, stream=None):
+    """fp4idx_k_rope_pack_store.  k bf16 [T,128]; slot_mapping int64 [T]; kv_cache u8
+    [NB,1,4,64,16] and kv_cache_scale u8 [NB,1,4,64] are updated in place."""
+    T, D = k.shape
+    dev = k.device
+    _require(k, "k", (torch.bfloat16, torch.int16, torch.uint16))
+    _require(positions, "positions", (torch.int32, torch.int64), dev)
+    _require(cos_sin, "cos_sin", (torch.float32,), dev)
+    _require(slot_mapping, "slot_mapping", (torch.int64,), dev)
+    _require(kv_cache, "kv_cache", (torch.uint8,), dev)
+    _require(kv_cache_scale, "kv_cache_scale", (torch.uint8,), dev)
+    _require(k_norm_gamma, "k_norm_gamma", (torch.bfloat16, torch.int16, torch.uint16), dev)
+    NB = kv_cache.shape[0]
+    rc = lib().fp4idx_k_rope_pack_store(
+        _ptr(k), _ptr(positions), int(positions.dtype == torch.int64), _ptr(cos_sin),
+        cos_sin.shape[0], _ptr(slot_mapping), _ptr(k_norm_gamma), k_norm_eps, T, D, ROPE_DIM,
+        rope_offset, GROUP, int(is_neox), int(apply_hadamard), scale_floor, _ptr(kv_cache),
+        _ptr(kv_cache_scale), NB, KV_BLOCK, _stream_handle(stream))
+    _check(rc)
+    return kv_cache, kv_cache_scale
+
+
+def dequant_q(q_out, q_scale_out, *, out=None, stream=None):
+    """fp4idx_dequant_debug(which=0): fp32 [T,H,128]."""
+    T, H, _ = q_out.shape
+    if out is None:
+        out = torch.empty((T, H, HEAD_DIM), dtype=torch.float32, device=q_out.device)
+    _require(q_out, "q_out", (torch.uint8,))
+    _require(q_scale_out, "q_scale_out", (torch.uint8,), q_out.device)
+    _require(out, "out", (torch.float32,), q_out.device)
+    _check(lib().fp4idx_dequant_debug(0, _ptr(q_out), _ptr(q_scale_out), T, H, None, 0, KV_BLOCK,
+                                      _ptr(out), _stream_handle(stream)))
+    return out
+
+
+def dequant_kcache(kv_cache, kv_cache_scale, slots=None, *, out=None, stream=None):
+    """fp4idx_dequant_debug(which=1): fp32 [rows,128] for the given slots (or all slots)."""
+    NB = kv_cache.shape[0]
+    rows = NB * KV_BLOCK if slots is None else slots.shape[0]
+    if out is None:
+        out = torch.empty((rows, HEAD_DIM), dtype=torch.float32, device=kv_cache.device)
+    _require(kv_cache, "kv_cache", (torch.uint8,))
+    _require(kv_cache_scale, "kv_cache_scale", (torch.uint8,), kv_cache.device)
+    _require(slots, "slots", (torch.int64,), kv_cache.device)
+    _require(out, "out", (torch.float32,), kv_cache.device)
+    _check(lib().fp4idx_dequant_debug(1, _ptr(kv_cache), _ptr(kv_cache_scale), rows, 0,
+                                      _ptr(slots), NB, KV_BLOCK, _ptr(out), _stream_handle(stream)))
+    return out

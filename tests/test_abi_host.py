@@ -1,0 +1,167 @@
+"""CPU-only checks of the C ABI: the library loads, exports every entry point
+declared in include/fp4idx.h, and rejects bad arguments on the host with a
+specific message before any GPU work (ROCm/aiter PR 5484 "API": shapes
+outside head_dim 128, rope_dim 64, group 32, kv block 64, n_heads % 16 are
+refused on the host).  These calls never reach a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from pack_token_amd import fp4idx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4idx.h")
+
+ALIGNED = 1 << 20       # a fake, well-aligned non-null address; never dereferenced
+MISALIGNED = ALIGNED + 2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(fp4idx_\w+)\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert names == ["fp4idx_dequant_debug", "fp4idx_k_rope_pack_store", "fp4idx_last_error",
+                     "fp4idx_q_rope_pack"]
+    lib = ctypes.CDLL(fp4idx.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def q_call(**over):
+    a = dict(q=ALIGNED, positions=ALIGNED, positions_int64=1, cos_sin=ALIGNED, max_pos=16,
+             weights=None, T=4, H=32, D=128, R=64, rope_offset=64, group_size=32, is_neox=1,
+             apply_hadamard=0, scale_floor=2.0 ** -126, q_out=ALIGNED, q_scale_out=ALIGNED,
+             weights_out=None, stream=None)
+    a.update(over)
+    return fp4idx.lib().fp4idx_q_rope_pack(*a.values())
+
+
+def k_call(**over):
+    a = dict(k=ALIGNED, positions=ALIGNED, positions_int64=1, cos_sin=ALIGNED, max_pos=16,
+             slot_mapping=ALIGNED, k_norm_gamma=None, k_norm_eps=1e-6, T=4, D=128, R=64,
+             rope_offset=64, group_size=32, is_neox=1, apply_hadamard=0,
+             scale_floor=2.0 ** -126, kv_cache=ALIGNED, kv_cache_scale=ALIGNED, NB=2, BS=64,
+             stream=None)
+    a.update(over)
+    return fp4idx.lib().fp4idx_k_rope_pack_store(*a.values())
+
+
+def d_call(**over):
+    a = dict(which=0, packed=ALIGNED, scales=ALIGNED, rows=4, H=32, slots=None, NB=2, BS=64,
+             out=ALIGNED, stream=None)
+    a.update(over)
+    return fp4idx.lib().fp4idx_dequant_debug(*a.values())
+
+
+Q_REJECT = [
+    (dict(D=64), fp4idx.EUNSUPPORTED, "head_dim"),
+    (dict(R=32), fp4idx.EUNSUPPORTED, "rope_dim"),
+    (dict(group_size=16), fp4idx.EUNSUPPORTED, "group_size"),
+    (dict(H=24), fp4idx.EUNSUPPORTED, "n_heads"),
+    (dict(H=0), fp4idx.EUNSUPPORTED, "n_heads"),
+    (dict(H=4096), fp4idx.EUNSUPPORTED, "n_heads"),
+    (dict(rope_offset=32), fp4idx.EUNSUPPORTED, "rope_offset"),
+    (dict(is_neox=2), fp4idx.EINVAL, "is_neox"),
+    (dict(apply_hadamard=-1), fp4idx.EINVAL, "apply_hadamard"),
+    (dict(positions_int64=3), fp4idx.EINVAL, "positions_int64"),
+    (dict(T=-1), fp4idx.EINVAL, "T must be"),
+    (dict(max_pos=0), fp4idx.EINVAL, "max_pos"),
+    (dict(scale_floor=-1.0), fp4idx.EINVAL, "scale_floor"),
+    (dict(scale_floor=float("nan")), fp4idx.EINVAL, "scale_floor"),
+    (dict(scale_floor=float("inf")), fp4idx.EINVAL, "scale_floor"),
+    (dict(weights=ALIGNED), fp4idx.EINVAL, "weights and weights_out"),
+    (dict(weights_out=ALIGNED), fp4idx.EINVAL, "weights and weights_out"),
+    (dict(q=None), fp4idx.EINVAL, "q must not be NULL"),
+    (dict(q=MISALIGNED), fp4idx.EINVAL, "q must be 16-byte aligned"),
+    (dict(positions=ALIGNED + 4), fp4idx.EINVAL, "positions must be 8-byte"),
+    (dict(cos_sin=ALIGNED + 4), fp4idx.EINVAL, "cos_sin must be 16-byte"),
+    (dict(q_out=ALIGNED + 8), fp4idx.EINVAL, "q_out must be 16-byte"),
+    (dict(q_scale_out=ALIGNED + 1), fp4idx.EINVAL, "q_scale_out must be 4-byte"),
+    (dict(q_scale_out=None), fp4idx.EINVAL, "q_scale_out must not be NULL"),
+    (dict(weights=ALIGNED + 1, weights_out=ALIGNED), fp4idx.EINVAL, "weights must be 4-byte"),
+    (dict(T=1 << 58), fp4idx.EINVAL, "T too large"),
+]
+
+
+@pytest.mark.parametrize("over,code,msg", Q_REJECT)
+def test_q_rejections(over, code, msg):
+    assert q_call(**over) == code
+    assert msg in fp4idx.last_error(), fp4idx.last_error()
+    assert fp4idx.last_error().startswith("fp4idx_q_rope_pack:")
+
+
+K_REJECT = [
+    (dict(D=256), fp4idx.EUNSUPPORTED, "head_dim"),
+    (dict(BS=128), fp4idx.EUNSUPPORTED, "kv_block_size"),
+    (dict(rope_offset=1), fp4idx.EUNSUPPORTED, "rope_offset"),
+    (dict(NB=-1), fp4idx.EINVAL, "NB must be"),
+    (dict(k_norm_gamma=ALIGNED, k_norm_eps=-1.0), fp4idx.EINVAL, "k_norm_eps"),
+    (dict(k_norm_gamma=ALIGNED, k_norm_eps=float("nan")), fp4idx.EINVAL, "k_norm_eps"),
+    (dict(k_norm_gamma=ALIGNED + 2), fp4idx.EINVAL, "k_norm_gamma must be 16-byte"),
+    (dict(slot_mapping=None), fp4idx.EINVAL, "slot_mapping must not be NULL"),
+    (dict(slot_mapping=ALIGNED + 4), fp4idx.EINVAL, "slot_mapping must be 8-byte"),
+    (dict(kv_cache=ALIGNED + 4), fp4idx.EINVAL, "kv_cache must be 16-byte"),
+    (dict(kv_cache_scale=ALIGNED + 2), fp4idx.EINVAL, "kv_cache_scale must be 4-byte"),
+    (dict(k=None), fp4idx.EINVAL, "k must not be NULL"),
+    (dict(positions_int64=0, positions=ALIGNED + 2), fp4idx.EINVAL, "positions must be 4-byte"),
+]
+
+
+@pytest.mark.parametrize("over,code,msg", K_REJECT)
+def test_k_rejections(over, code, msg):
+    assert k_call(**over) == code
+    assert msg in fp4idx.last_error(), fp4idx.last_error()
+
+
+D_REJECT = [
+    (dict(which=2), fp4idx.EINVAL, "which"),
+    (dict(rows=-1), fp4idx.EINVAL, "rows"),
+    (dict(H=8), fp4idx.EUNSUPPORTED, "n_heads"),
+    (dict(which=1, BS=32), fp4idx.EUNSUPPORTED, "kv_block_size"),
+    (dict(out=ALIGNED + 4), fp4idx.EINVAL, "out must be 16-byte"),
+    (dict(which=1, slots=ALIGNED + 4), fp4idx.EINVAL, "slots must be 8-byte"),
+    (dict(packed=None), fp4idx.EINVAL, "packed must not be NULL"),
+]
+
+
+@pytest.mark.parametrize("over,code,msg", D_REJECT)
+def test_dequant_rejections(over, code, msg):
+    assert d_call(**over) == code
+    assert msg in fp4idx.last_error(), fp4idx.last_error()
+
+
+def test_zero_tokens_is_a_noop_even_with_null_buffers():
+    assert q_call(T=0, q=None, positions=None, cos_sin=None, q_out=None, q_scale_out=None) == 0
+    assert k_call(T=0, k=None, positions=None, cos_sin=None, slot_mapping=None, kv_cache=None,
+                  kv_cache_scale=None) == 0
+    assert d_call(rows=0, packed=None, scales=None, out=None) == 0
+    # but shapes are still checked first
+    assert q_call(T=0, D=64) == fp4idx.EUNSUPPORTED
+
+
+def test_error_message_is_thread_local():
+    import threading
+
+    assert q_call(D=64) == fp4idx.EUNSUPPORTED
+    seen = {}
+
+    def other():
+        seen["msg"] = fp4idx.last_error()
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["msg"] == ""
+    assert "head_dim" in fp4idx.last_error()
+
+
+def test_binding_refuses_missing_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(fp4idx, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(fp4idx, "_lib", None)
+    with pytest.raises(RuntimeError, match="no CPU or PyTorch fallback"):
+        fp4idx.lib()

@@ -1,0 +1,207 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, byte
+for byte on all five outputs, on the five workloads and a sweep of shapes and
+modes (tokens x heads x is_neox x rotated slice, mirroring the 16-config
+matrix of ROCm/aiter PR 5484 "Verification")."""
+import numpy as np
+import pytest
+
+import oracle
+from pack_token_amd import workloads
+from pack_token_amd.workloads import SENTINEL
+from harness import assert_all_same, assert_same, gpu_run, oracle_run, say
+
+pytestmark = pytest.mark.gpu
+
+
+def check(wl, **kw):
+    say(f"case {wl.name}: T={wl.T} H={wl.H} neox={wl.is_neox} ro={wl.rope_offset} "
+        f"had={wl.apply_hadamard} norm={wl.k_norm_gamma is not None}")
+    got = gpu_run(wl, **kw)
+    ref = oracle_run(wl, with_weights=kw.get("with_weights", True))
+    assert_all_same(got, ref)
+    return got
+
+
+def test_tiny():
+    check(workloads.tiny())
+
+
+@pytest.mark.parametrize("pos32", [False, True])
+def test_edge_mix(pos32):
+    check(workloads.edge_mix(positions_int32=pos32))
+
+
+@pytest.mark.parametrize("T", [8, 32])
+@pytest.mark.parametrize("H", [32, 64])
+@pytest.mark.parametrize("is_neox", [True, False])
+@pytest.mark.parametrize("rope_offset", [0, 64])
+def test_sweep(T, H, is_neox, rope_offset):
+    check(workloads.sweep_case(100 + T + H, T, H, is_neox, rope_offset))
+
+
+@pytest.mark.parametrize("is_neox", [True, False])
+@pytest.mark.parametrize("rope_offset", [0, 64])
+@pytest.mark.parametrize("norm", [False, True])
+@pytest.mark.parametrize("had", [False, True])
+def test_modes_ragged(is_neox, rope_offset, norm, had):
+    """Every kernel variant on a ragged token count (not a multiple of the 4
+    or 16 tokens a block covers) and 16, 48 and 80 heads."""
+    for T, H in [(1, 16), (37, 48), (301, 80)]:
+        wl = workloads.sweep_case(7 * T + H, T, H, is_neox, rope_offset)
+        wl.apply_hadamard = had
+        if norm:
+            rng = np.random.default_rng(T)
+            wl.k_norm_gamma = workloads.to_bf16_bits((1 + 0.1 * rng.standard_normal(128)).astype(np.float32))
+        check(wl)
+
+
+def test_no_weights_and_scale_floor():
+    wl = workloads.edge_mix(seed=21, T=64)
+    wl.scale_floor = float(np.float32(1e-10))   # all-zero groups get e = 94
+    check(wl, with_weights=False)
+
+
+def test_out_of_range_positions_and_slots():
+    wl = workloads.sweep_case(5, 40, 32, True, 64)
+    wl.positions[:4] = [-3, wl.max_pos, wl.max_pos + 99, 2 ** 40]
+    wl.slot_mapping[4:8] = [-1, -5, wl.NB * 64, wl.NB * 64 + 12345]
+    check(wl)
+
+
+def test_decode_with_background_cache():
+    wl = workloads.decode()
+    got = check(wl)
+    # every slot was written by the background keys: no sentinel row is left
+    assert not (got[4] == SENTINEL).all(axis=-1).any()
+
+
+def test_prefill_norm_rotate():
+    check(workloads.prefill_norm_rotate())
+
+
+def test_non_default_stream():
+    import torch
+
+    s = torch.cuda.Stream()
+    wl = workloads.sweep_case(9, 96, 64, True, 64)
+    with torch.cuda.stream(s):
+        got = gpu_run(wl, stream=s)
+    assert_all_same(got, oracle_run(wl))
+
+
+def test_empty_batch():
+    import torch
+
+    from pack_token_amd import fp4idx
+
+    dev = "cuda:0"
+    q = torch.empty((0, 32, 128), dtype=torch.bfloat16, device=dev)
+    pos = torch.empty(0, dtype=torch.int64, device=dev)
+    cs = torch.zeros((1, 64), dtype=torch.float32, device=dev)
+    q_out, qs, _ = fp4idx.q_rope_pack(q, pos, cs)
+    kv = torch.full((1, 1, 4, 64, 16), SENTINEL, dtype=torch.uint8, device=dev)
+    ks = torch.full((1, 1, 4, 64), SENTINEL, dtype=torch.uint8, device=dev)
+    fp4idx.k_rope_pack_store(torch.empty((0, 128), dtype=torch.bfloat16, device=dev), pos, cs,
+                             torch.empty(0, dtype=torch.int64, device=dev), kv, ks)
+    torch.cuda.synchronize()
+    assert q_out.shape == (0, 32, 64) and (kv == SENTINEL).all() and (ks == SENTINEL).all()
+
+
+def test_converter_exhaustive():
+    """Every finite bf16 value under every block exponent e in [1, 253] it can
+    meet (|v| <= 6 * 2^(e-127)), through the unrotated groups of the query
+    path: one anchor element per group forces e, the other 31 carry the test
+    values.  Compares codes and exponents with the oracle."""
+    import torch
+
+    from pack_token_amd import fp4idx
+
+    allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = allb[((allb.astype(np.uint32) >> 7) & 0xFF) != 0xFF]
+    mag = finite & 0x7FFF
+    groups = []
+    for e in range(1, 254):
+        anchor = 0x7F7F if e == 253 else int(workloads.to_bf16_bits(
+            np.array([6.0 * 2.0 ** (e - 127)], np.float32))[0])
+        vals = finite[mag <= anchor]
+        n = -(-vals.size // 31) * 31
+        vals = np.concatenate([vals, np.zeros(n - vals.size, np.uint16)]).reshape(-1, 31)
+        g = np.empty((vals.shape[0], 32), np.uint16)
+        g[:, 0] = anchor
+        g[:, 1:] = vals
+        groups.append(g)
+    groups = np.concatenate(groups)
+    H = 64
+    rows = -(-groups.shape[0] // 2)
+    T = -(-rows // H)
+    q = np.zeros((T * H, 128), np.uint16)
+    flat = np.zeros((T * H * 2, 32), np.uint16)
+    flat[: groups.shape[0]] = groups
+    q[:, :64] = flat.reshape(T * H, 64)           # groups 0 and 1: not rotated (rope_offset 64)
+    q = q.reshape(T, H, 128)
+    pos = np.zeros(T, np.int64)
+    cs = workloads.cos_sin_table(1)
+    say(f"case converter_exhaustive: {groups.shape[0]} groups, T={T} H={H}")
+    dev = "cuda:0"
+    q_out, qs, _ = fp4idx.q_rope_pack(torch.from_numpy(q.view(np.int16)).to(dev),
+                                      torch.from_numpy(pos).to(dev), torch.from_numpy(cs).to(dev))
+    torch.cuda.synchronize()
+    ref_q, ref_qs, _ = oracle.q_rope_pack(q, pos, cs, None, threads=8)
+    assert_same("q_out", q_out.cpu().numpy(), ref_q)
+    assert_same("q_scale_out", qs.cpu().numpy(), ref_qs)
+
+
+def test_dequant_debug_matches_oracle():
+    import torch
+
+    from pack_token_amd import fp4idx
+
+    wl = workloads.edge_mix(seed=33, T=120)
+    got = gpu_run(wl)
+    q_out, qs, _, kv, ks = got
+    dev = "cuda:0"
+    qd = fp4idx.dequant_q(torch.from_numpy(q_out).to(dev), torch.from_numpy(qs).to(dev))
+    slots = np.concatenate([wl.slot_mapping, np.array([-1, wl.NB * 64, 3], np.int64)])
+    kd = fp4idx.dequant_kcache(torch.from_numpy(kv).to(dev), torch.from_numpy(ks).to(dev),
+                               torch.from_numpy(slots).to(dev))
+    kall = fp4idx.dequant_kcache(torch.from_numpy(kv).to(dev), torch.from_numpy(ks).to(dev))
+    torch.cuda.synchronize()
+    assert_same("dequant_q", qd.cpu().numpy(), oracle.dequant_q(q_out, qs))
+    assert_same("dequant_k", kd.cpu().numpy(), oracle.dequant_kcache(kv, ks, slots))
+    assert_same("dequant_k_all", kall.cpu().numpy(), oracle.dequant_kcache(kv, ks))
+
+
+def test_large_prefill_full_size_sampled():
+    """T = 131072, H = 64 in the launch configuration the benchmark times:
+    4,099 sampled tokens (including the first, the last and outlier rows)
+    against the oracle on all five outputs; at full size, every cache slot is
+    written and every exponent lies in [1, 253]."""
+    import torch
+
+    from pack_token_amd import fp4idx
+
+    wl = workloads.large_prefill()
+    say(f"case {wl.name}: T={wl.T} H={wl.H} (inputs generated)")
+    rng = np.random.default_rng(123)
+    idx = np.unique(np.concatenate([rng.choice(wl.T, 4096, replace=False), [0, 1, wl.T - 1]]))
+    got = gpu_run(wl)
+    q_out, qs, w_out, kv, ks = got
+    say("case large_prefill: GPU outputs copied back")
+    ref_q, ref_qs, ref_w = oracle.q_rope_pack(wl.q[idx], wl.positions[idx], wl.cos_sin, wl.weights[idx],
+                                              is_neox=wl.is_neox, threads=16)
+    assert_same("q_out[sample]", q_out[idx], ref_q)
+    assert_same("q_scale_out[sample]", qs[idx], ref_qs)
+    assert_same("weights_out[sample]", w_out[idx], ref_w)
+    kv_ref, ks_ref = wl.empty_cache()
+    oracle.k_rope_pack_store(wl.k[idx], wl.positions[idx], wl.cos_sin, wl.slot_mapping[idx],
+                             kv_ref, ks_ref, is_neox=wl.is_neox)
+    s = wl.slot_mapping[idx]
+    blk, p = s // 64, s % 64
+    assert_same("kv_cache[sample]", kv[blk, 0, :, p], kv_ref[blk, 0, :, p])
+    il = (p % 16) * 4 + p // 16
+    assert_same("kv_cache_scale[sample]", ks[blk, 0, :, il], ks_ref[blk, 0, :, il])
+    # full-size properties
+    assert (kv.reshape(wl.NB, 4, 64, 16) != SENTINEL).any(axis=-1).all()
+    assert ks.min() >= 1 and ks.max() <= 253
+    assert qs.min() >= 1 and qs.max() <= 253
+    assert np.array_equal(w_out.view(np.uint32), wl.weights.view(np.uint32))
