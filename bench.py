@@ -1,9 +1,11 @@
 """Benchmark of the fused q+k RoPE / FP4 pack + paged store on one MI355X.
 
-One step = fp4idx_q_rope_pack + fp4idx_k_rope_pack_store on one stream over
+One step = fp4idx_qk_rope_pack_store (query and key sides in one launch) over
 the large-prefill workload (T = 131072 tokens, H = 64 heads, D = 128, neox
 RoPE on dims 64..127, contiguous slots into 2048 cache blocks), inputs
-resident in HBM before timing starts.  Prints one JSON line.
+resident in HBM before timing starts.  The same step as two launches
+(fp4idx_q_rope_pack + fp4idx_k_rope_pack_store) is timed too and reported
+under "two_call_step".  Prints one JSON line.
 
 Algorithmic bytes (each input read once, each output written once):
   query launch, per token: 256H (q) + 4H (weights) + 8 (position) + 256 (cos/sin
@@ -27,7 +29,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "pack_token_amd", "csrc", "fp4idx_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q_split_neox_large_prefill_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qk_kernel_large_prefill_traffic.json")
 
 
 def q_bytes_per_token(H: int) -> int:
@@ -48,9 +50,10 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(q_launch_bytes: int):
-    """HBM bytes of one query launch from committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE counts, if they were taken on the current kernel source."""
+def measured_traffic():
+    """HBM bytes of one fused launch from committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE counts (scaled by a plain copy's counts), if they were taken on
+    the current kernel source; otherwise None."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -113,11 +116,20 @@ def main():
         n = args.calibrate_copy_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
+        reps = 3
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n}),
-              flush=True)
+        c0.record()
+        for _ in range(reps):
+            dst.copy_(src)
+        c1.record()
+        torch.cuda.synchronize()
+        ms = c0.elapsed_time(c1) / reps
+        print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": n,
+                          "bytes_written_per_copy": n, "copies": reps + 1,
+                          "us_per_copy": ms * 1e3, "GBps": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
         return
 
     t_gen = time.perf_counter()
@@ -143,42 +155,48 @@ def main():
     ks = torch.zeros((wl.NB, 1, 4, 64), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    common = dict(is_neox=wl.is_neox, rope_offset=wl.rope_offset, stream=stream)
+
     def q_call():
-        fp4idx.q_rope_pack(q, pos, cs, w, q_out=q_out, q_scale_out=qs, weights_out=w_out,
-                           is_neox=wl.is_neox, rope_offset=wl.rope_offset, stream=stream)
+        fp4idx.q_rope_pack(q, pos, cs, w, q_out=q_out, q_scale_out=qs, weights_out=w_out, **common)
 
     def k_call():
-        fp4idx.k_rope_pack_store(k, pos, cs, slots, kv, ks, is_neox=wl.is_neox,
-                                 rope_offset=wl.rope_offset, stream=stream)
+        fp4idx.k_rope_pack_store(k, pos, cs, slots, kv, ks, **common)
 
-    for _ in range(args.warmup):
-        q_call()
-        k_call()
-    torch.cuda.synchronize()
+    def qk_call():
+        fp4idx.qk_rope_pack_store(q, k, pos, cs, slots, kv, ks, w, q_out=q_out, q_scale_out=qs,
+                                  weights_out=w_out, **common)
+
+    def timed(calls, K, W):
+        """Run W untimed then K timed steps of `calls` (launched back to back on
+        `stream`); returns (ms per step, [mean ms of each call's launch])."""
+        for _ in range(W):
+            for c in calls:
+                c()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+              for _ in range(K)]
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(K):
+            ev[i][0].record(stream)
+            for j, c in enumerate(calls):
+                c()
+                ev[i][j + 1].record(stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        per_call = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]))
+                    for j in range(len(calls))]
+        return t0.elapsed_time(t1) / K, per_call
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(K):
-        ev[i][0].record(stream)
-        q_call()
-        ev[i][1].record(stream)
-        k_call()
-        ev[i][2].record(stream)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    k_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    ms_per_step = total_ms / K
+    ms_per_step, (fused_ms,) = timed([qk_call], K, args.warmup)
+    two_ms, (q_ms, k_ms) = timed([q_call, k_call], K, args.warmup)
 
-    q_launch_bytes = q_bytes_per_token(H) * T
     step_bytes = step_bytes_per_token(H) * T
-    achieved = q_launch_bytes / (q_ms * 1e-3) / 1e9
-    traffic = measured_traffic(q_launch_bytes)
+    achieved = step_bytes / (fused_ms * 1e-3) / 1e9
+    traffic = measured_traffic()
     rec = {
         "metric": "tokens/s and achieved HBM GB/s (% of peak), fused q+k RoPE/FP4 pack+store",
         "value": T / (ms_per_step * 1e-3),
@@ -194,14 +212,19 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "tokens": T, "heads": H, "head_dim": 128, "rope_dim": 64,
                    "rope": "neox", "rope_offset": wl.rope_offset, "kv_blocks": wl.NB,
-                   "kv_block_size": 64, "slot_mapping": "contiguous"},
+                   "kv_block_size": 64, "slot_mapping": "contiguous",
+                   "step": "fp4idx_qk_rope_pack_store (one launch)"},
         "step_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "step_frac_of_hbm_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "q_kernel_us": q_ms * 1e3,
-        "k_kernel_us": k_ms * 1e3,
-        "roofline": {"kernel": "q_split_kernel<neox>", "bound": "hbm", "achieved": achieved,
+        "two_call_step": {"calls": "fp4idx_q_rope_pack + fp4idx_k_rope_pack_store",
+                          "ms_per_step": two_ms, "tokens_per_s": T / (two_ms * 1e-3),
+                          "GBps": step_bytes / (two_ms * 1e-3) / 1e9,
+                          "q_kernel_us": q_ms * 1e3, "k_kernel_us": k_ms * 1e3,
+                          "q_kernel_GBps": q_bytes_per_token(H) * T / (q_ms * 1e-3) / 1e9},
+        "roofline": {"kernel": "qk_kernel<neox>", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "algorithmic_bytes_per_launch": q_launch_bytes},
+                     "traffic": traffic, "algorithmic_bytes_per_launch": step_bytes,
+                     "launch_us": fused_ms * 1e3},
     }
     if not args.no_cpu_baseline:
         threads = max(1, min(16, len(os.sched_getaffinity(0))))

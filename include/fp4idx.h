@@ -148,6 +148,25 @@ int fp4idx_k_rope_pack_store(const void* k, const void* positions, int positions
                              void* stream);
 
 /*
+ * fp4idx_qk_rope_pack_store -- both sides of the producer in one launch, as
+ * the pages' producer writes all five outputs from one kernel (ROCm/aiter PR
+ * 5484 "Verification": zero mismatching bytes "across all five outputs").
+ * Arguments mean what they mean for fp4idx_q_rope_pack and
+ * fp4idx_k_rope_pack_store (q and k share T, positions, cos_sin, rope_offset,
+ * is_neox, apply_hadamard and scale_floor); every check of both calls
+ * applies.  The outputs are byte-identical to calling the two entry points
+ * one after the other; positions and cos/sin rows are read once.
+ */
+int fp4idx_qk_rope_pack_store(const void* q, const void* k, const void* positions,
+                              int positions_int64, const float* cos_sin, int64_t max_pos,
+                              const float* weights, const int64_t* slot_mapping,
+                              const void* k_norm_gamma, float k_norm_eps, int64_t T, int H, int D,
+                              int R, int rope_offset, int group_size, int is_neox,
+                              int apply_hadamard, float scale_floor, uint8_t* q_out,
+                              uint8_t* q_scale_out, float* weights_out, uint8_t* kv_cache,
+                              uint8_t* kv_cache_scale, int64_t NB, int BS, void* stream);
+
+/*
  * fp4idx_dequant_debug -- reader side, for tests and debugging: expands
  * codes back to fp32, value = E2M1(nibble) * 2^(e-127) with E2M1 magnitudes
  * {0, .5, 1, 1.5, 2, 3, 4, 6} and bit 3 the sign; e = 0 gives 2^-127 and

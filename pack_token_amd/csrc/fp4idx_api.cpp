@@ -107,14 +107,13 @@ int hip_fail(const char* fn, hipError_t err) {
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-int fp4idx_q_rope_pack(const void* q, const void* positions, int positions_int64,
-                       const float* cos_sin, int64_t max_pos, const float* weights, int64_t T,
-                       int H, int D, int R, int rope_offset, int group_size, int is_neox,
-                       int apply_hadamard, float scale_floor, uint8_t* q_out,
-                       uint8_t* q_scale_out, float* weights_out, void* stream) {
-    static const char* fn = "fp4idx_q_rope_pack";
+int prepare_q(const char* fn, const void* q, const void* positions, int positions_int64,
+              const float* cos_sin, int64_t max_pos, const float* weights, int64_t T, int H,
+              int D, int R, int rope_offset, int group_size, int is_neox, int apply_hadamard,
+              float scale_floor, uint8_t* q_out, uint8_t* q_scale_out, float* weights_out,
+              fp4idx::QArgs& a) {
     FP4IDX_TRY(check_common(fn, D, R, group_size, rope_offset, positions_int64, is_neox,
                             apply_hadamard, scale_floor, T, max_pos));
     if (H <= 0 || H % 16 != 0 || H > kMaxHeads)
@@ -126,6 +125,8 @@ int fp4idx_q_rope_pack(const void* q, const void* positions, int positions_int64
                     fn);
     if (T > INT64_MAX / ((int64_t)H * kHeadDim * 2))
         return fail(FP4IDX_EINVAL, "%s: T too large (%lld)", fn, (long long)T);
+    a = fp4idx::QArgs{};
+    a.T = T;
     if (T == 0) return FP4IDX_OK;
     FP4IDX_TRY(check_ptr(fn, "q", q, 16));
     FP4IDX_TRY(check_ptr(fn, "positions", positions, positions_int64 ? 8 : 4));
@@ -136,7 +137,6 @@ int fp4idx_q_rope_pack(const void* q, const void* positions, int positions_int64
         FP4IDX_TRY(check_ptr(fn, "weights", weights, 4));
         FP4IDX_TRY(check_ptr(fn, "weights_out", weights_out, 4));
     }
-    fp4idx::QArgs a{};
     a.q = static_cast<const uint16_t*>(q);
     a.positions = positions;
     a.cos_sin = cos_sin;
@@ -144,13 +144,75 @@ int fp4idx_q_rope_pack(const void* q, const void* positions, int positions_int64
     a.q_out = q_out;
     a.q_scale_out = q_scale_out;
     a.weights_out = weights_out;
-    a.T = T;
     a.max_pos = max_pos;
     a.H = H;
     a.J = ((H / 16) + 3) / 4 * 4;
     a.pos64 = positions_int64;
     a.rope_offset = rope_offset;
     a.e_lo = floor_exponent(scale_floor);
+    return FP4IDX_OK;
+}
+
+int prepare_k(const char* fn, const void* k, const void* positions, int positions_int64,
+              const float* cos_sin, int64_t max_pos, const int64_t* slot_mapping,
+              const void* k_norm_gamma, float k_norm_eps, int64_t T, int D, int R,
+              int rope_offset, int group_size, int is_neox, int apply_hadamard, float scale_floor,
+              uint8_t* kv_cache, uint8_t* kv_cache_scale, int64_t NB, int BS, fp4idx::KArgs& a) {
+    FP4IDX_TRY(check_common(fn, D, R, group_size, rope_offset, positions_int64, is_neox,
+                            apply_hadamard, scale_floor, T, max_pos));
+    if (BS != kKvBlock)
+        return fail(FP4IDX_EUNSUPPORTED, "%s: kv_block_size BS must be 64 (got %d)", fn, BS);
+    if (NB < 0) return fail(FP4IDX_EINVAL, "%s: NB must be >= 0 (got %lld)", fn, (long long)NB);
+    if (NB > INT64_MAX / ((int64_t)kKvBlock * kHeadDim))
+        return fail(FP4IDX_EINVAL, "%s: NB too large (%lld)", fn, (long long)NB);
+    if (k_norm_gamma != nullptr && (!std::isfinite(k_norm_eps) || k_norm_eps < 0.0f))
+        return fail(FP4IDX_EINVAL, "%s: k_norm_eps must be finite and >= 0 (got %g)", fn,
+                    (double)k_norm_eps);
+    if (T > INT64_MAX / (kHeadDim * 2))
+        return fail(FP4IDX_EINVAL, "%s: T too large (%lld)", fn, (long long)T);
+    a = fp4idx::KArgs{};
+    a.T = T;
+    if (T == 0) return FP4IDX_OK;
+    FP4IDX_TRY(check_ptr(fn, "k", k, 16));
+    FP4IDX_TRY(check_ptr(fn, "positions", positions, positions_int64 ? 8 : 4));
+    FP4IDX_TRY(check_ptr(fn, "cos_sin", cos_sin, 16));
+    FP4IDX_TRY(check_ptr(fn, "slot_mapping", slot_mapping, 8));
+    if (k_norm_gamma != nullptr) FP4IDX_TRY(check_ptr(fn, "k_norm_gamma", k_norm_gamma, 16));
+    if (NB > 0) {
+        FP4IDX_TRY(check_ptr(fn, "kv_cache", kv_cache, 16));
+        FP4IDX_TRY(check_ptr(fn, "kv_cache_scale", kv_cache_scale, 4));
+    }
+    a.k = static_cast<const uint16_t*>(k);
+    a.positions = positions;
+    a.cos_sin = cos_sin;
+    a.slot_mapping = slot_mapping;
+    a.gamma = static_cast<const uint16_t*>(k_norm_gamma);
+    a.kv_cache = kv_cache;
+    a.kv_cache_scale = kv_cache_scale;
+    a.max_pos = max_pos;
+    a.nslots = NB * kKvBlock;
+    a.eps = k_norm_eps;
+    a.pos64 = positions_int64;
+    a.rope_offset = rope_offset;
+    a.e_lo = floor_exponent(scale_floor);
+    return FP4IDX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp4idx_q_rope_pack(const void* q, const void* positions, int positions_int64,
+                       const float* cos_sin, int64_t max_pos, const float* weights, int64_t T,
+                       int H, int D, int R, int rope_offset, int group_size, int is_neox,
+                       int apply_hadamard, float scale_floor, uint8_t* q_out,
+                       uint8_t* q_scale_out, float* weights_out, void* stream) {
+    static const char* fn = "fp4idx_q_rope_pack";
+    fp4idx::QArgs a;
+    FP4IDX_TRY(prepare_q(fn, q, positions, positions_int64, cos_sin, max_pos, weights, T, H, D, R,
+                         rope_offset, group_size, is_neox, apply_hadamard, scale_floor, q_out,
+                         q_scale_out, weights_out, a));
+    if (T == 0) return FP4IDX_OK;
     hipError_t err = fp4idx::launch_q_rope_pack(a, is_neox != 0, apply_hadamard != 0,
                                                 static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return hip_fail(fn, err);
@@ -164,45 +226,37 @@ int fp4idx_k_rope_pack_store(const void* k, const void* positions, int positions
                              float scale_floor, uint8_t* kv_cache, uint8_t* kv_cache_scale,
                              int64_t NB, int BS, void* stream) {
     static const char* fn = "fp4idx_k_rope_pack_store";
-    FP4IDX_TRY(check_common(fn, D, R, group_size, rope_offset, positions_int64, is_neox,
-                            apply_hadamard, scale_floor, T, max_pos));
-    if (BS != kKvBlock)
-        return fail(FP4IDX_EUNSUPPORTED, "%s: kv_block_size BS must be 64 (got %d)", fn, BS);
-    if (NB < 0) return fail(FP4IDX_EINVAL, "%s: NB must be >= 0 (got %lld)", fn, (long long)NB);
-    if (NB > INT64_MAX / ((int64_t)kKvBlock * kHeadDim))
-        return fail(FP4IDX_EINVAL, "%s: NB too large (%lld)", fn, (long long)NB);
-    if (k_norm_gamma != nullptr && (!std::isfinite(k_norm_eps) || k_norm_eps < 0.0f))
-        return fail(FP4IDX_EINVAL, "%s: k_norm_eps must be finite and >= 0 (got %g)", fn,
-                    (double)k_norm_eps);
-    if (T > INT64_MAX / (kHeadDim * 2))
-        return fail(FP4IDX_EINVAL, "%s: T too large (%lld)", fn, (long long)T);
+    fp4idx::KArgs a;
+    FP4IDX_TRY(prepare_k(fn, k, positions, positions_int64, cos_sin, max_pos, slot_mapping,
+                         k_norm_gamma, k_norm_eps, T, D, R, rope_offset, group_size, is_neox,
+                         apply_hadamard, scale_floor, kv_cache, kv_cache_scale, NB, BS, a));
     if (T == 0) return FP4IDX_OK;
-    FP4IDX_TRY(check_ptr(fn, "k", k, 16));
-    FP4IDX_TRY(check_ptr(fn, "positions", positions, positions_int64 ? 8 : 4));
-    FP4IDX_TRY(check_ptr(fn, "cos_sin", cos_sin, 16));
-    FP4IDX_TRY(check_ptr(fn, "slot_mapping", slot_mapping, 8));
-    if (k_norm_gamma != nullptr) FP4IDX_TRY(check_ptr(fn, "k_norm_gamma", k_norm_gamma, 16));
-    if (NB > 0) {
-        FP4IDX_TRY(check_ptr(fn, "kv_cache", kv_cache, 16));
-        FP4IDX_TRY(check_ptr(fn, "kv_cache_scale", kv_cache_scale, 4));
-    }
-    fp4idx::KArgs a{};
-    a.k = static_cast<const uint16_t*>(k);
-    a.positions = positions;
-    a.cos_sin = cos_sin;
-    a.slot_mapping = slot_mapping;
-    a.gamma = static_cast<const uint16_t*>(k_norm_gamma);
-    a.kv_cache = kv_cache;
-    a.kv_cache_scale = kv_cache_scale;
-    a.T = T;
-    a.max_pos = max_pos;
-    a.nslots = NB * kKvBlock;
-    a.eps = k_norm_eps;
-    a.pos64 = positions_int64;
-    a.rope_offset = rope_offset;
-    a.e_lo = floor_exponent(scale_floor);
     hipError_t err = fp4idx::launch_k_rope_pack_store(a, is_neox != 0, apply_hadamard != 0,
                                                       static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(fn, err);
+    return FP4IDX_OK;
+}
+
+int fp4idx_qk_rope_pack_store(const void* q, const void* k, const void* positions,
+                              int positions_int64, const float* cos_sin, int64_t max_pos,
+                              const float* weights, const int64_t* slot_mapping,
+                              const void* k_norm_gamma, float k_norm_eps, int64_t T, int H, int D,
+                              int R, int rope_offset, int group_size, int is_neox,
+                              int apply_hadamard, float scale_floor, uint8_t* q_out,
+                              uint8_t* q_scale_out, float* weights_out, uint8_t* kv_cache,
+                              uint8_t* kv_cache_scale, int64_t NB, int BS, void* stream) {
+    static const char* fn = "fp4idx_qk_rope_pack_store";
+    fp4idx::QArgs qa;
+    fp4idx::KArgs ka;
+    FP4IDX_TRY(prepare_q(fn, q, positions, positions_int64, cos_sin, max_pos, weights, T, H, D, R,
+                         rope_offset, group_size, is_neox, apply_hadamard, scale_floor, q_out,
+                         q_scale_out, weights_out, qa));
+    FP4IDX_TRY(prepare_k(fn, k, positions, positions_int64, cos_sin, max_pos, slot_mapping,
+                         k_norm_gamma, k_norm_eps, T, D, R, rope_offset, group_size, is_neox,
+                         apply_hadamard, scale_floor, kv_cache, kv_cache_scale, NB, BS, ka));
+    if (T == 0) return FP4IDX_OK;
+    hipError_t err = fp4idx::launch_qk_rope_pack_store(qa, ka, is_neox != 0, apply_hadamard != 0,
+                                                       static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return hip_fail(fn, err);
     return FP4IDX_OK;
 }

@@ -58,6 +58,8 @@ struct DArgs {
 hipError_t launch_q_rope_pack(const QArgs& a, bool is_neox, bool hadamard, hipStream_t stream);
 hipError_t launch_k_rope_pack_store(const KArgs& a, bool is_neox, bool hadamard,
                                     hipStream_t stream);
+hipError_t launch_qk_rope_pack_store(const QArgs& qa, const KArgs& ka, bool is_neox, bool hadamard,
+                                     hipStream_t stream);
 hipError_t launch_dequant(const DArgs& a, hipStream_t stream);
 
 }  // namespace fp4idx

@@ -71,6 +71,22 @@ __device__ __forceinline__ uint4 load16(const void* p) {
     return *reinterpret_cast<const uint4*>(p);
 }
 
+// Streaming (non-temporal) accesses for data touched exactly once: q, k and
+// the code bytes.  They set the nt cache-policy bit so the lines do not
+// displace anything in L2; on MI355X this raises the query kernel from
+// ~5.4 to ~6.5 TB/s.  The small per-token rows (weights, scales) keep the
+// default policy, which measured faster for them.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store4_stream(void* p, uint32_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+}
+
 // ---- bf16 <-> fp32 ---------------------------------------------------------
 
 __device__ __forceinline__ void unpack8(uint4 v, float x[8]) {
@@ -297,7 +313,7 @@ __device__ __forceinline__ int64_t clamped_position(const void* positions, int p
     return p >= max_pos ? max_pos - 1 : p;
 }
 
-// ---- query kernels ------------------------------------------------------------
+// ---- query side ----------------------------------------------------------------
 // One wavefront per token.  The token's scale bytes are gathered in LDS
 // ([4][16][J] bytes, pads zero) and written out as whole dwords at the end.
 
@@ -320,139 +336,190 @@ __device__ __forceinline__ void q_token_epilogue(const QArgs& a, int64_t t, int 
 
 // Without the Hadamard, the rotated and the plain halves of a head never mix,
 // so every 16-byte load of a wave covers one half (128 bytes) of 8 heads:
-// lanes 8k..8k+7 take head hb+k.  Rotated and plain halves go through
-// separate instruction streams and no lane computes a RoPE it throws away.
+// lanes 8k..8k+7 take head hb+k, lane chunk c = chunk_of(lane & 7).  Rotated
+// and plain halves go through separate instruction streams and no lane
+// computes a RoPE it throws away.  Each step handles 16 heads (4 loads) and
+// issues the next step's loads before it computes.
 template <bool NEOX>
-__global__ __launch_bounds__(kBlock) void q_split_kernel(QArgs a) {
-    extern __shared__ uint32_t smem[];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-    if (t >= a.T) return;
+__device__ __forceinline__ void q_split_token(const QArgs& a, int64_t t, int lane, uint8_t* scb,
+                                              const float C[8], const float S[8]) {
     const int H = a.H;
     const int J = a.J;
-    uint32_t* sc = smem + wave * 16 * J;
-    uint8_t* scb = reinterpret_cast<uint8_t*>(sc);
-    q_token_prologue(a, t, lane, sc);
-
-    const int64_t pos = clamped_position(a.positions, a.pos64, t, a.max_pos);
-    const int c = chunk_of(lane & 7);  // chunk within the 64-wide half
+    const int c = chunk_of(lane & 7);
     const int hsub = lane >> 3;
-    float C[8], S[8];
-    rope_coeffs<NEOX>(a.cos_sin + pos * 64, c, C, S);
-
     const int ro = a.rope_offset;
     const int nro = 64 - ro;
     const int g_rot = ro / 32 + (c >> 2);
     const int g_pln = nro / 32 + (c >> 2);
     const bool writer = (lane & 3) == 0;
-    const uint16_t* qt = a.q + t * (int64_t)H * 128;
-    uint8_t* ot = a.q_out + t * (int64_t)H * 64;
+    const uint16_t* qt = a.q + t * (int64_t)H * 128 + hsub * 128 + 8 * c;
+    uint8_t* ot = a.q_out + t * (int64_t)H * 64 + hsub * 64 + 4 * c;
 
+    uint4 np0 = load16_stream(qt + nro), nr0 = load16_stream(qt + ro);
+    uint4 np1 = load16_stream(qt + 8 * 128 + nro), nr1 = load16_stream(qt + 8 * 128 + ro);
     for (int hb = 0; hb < H; hb += 16) {
-        const int h0 = hb + hsub;
-        const int h1 = h0 + 8;
-        const uint4 p0 = load16(qt + h0 * 128 + nro + 8 * c);
-        const uint4 r0 = load16(qt + h0 * 128 + ro + 8 * c);
-        const uint4 p1 = load16(qt + h1 * 128 + nro + 8 * c);
-        const uint4 r1 = load16(qt + h1 * 128 + ro + 8 * c);
+        const uint4 p0 = np0, r0 = nr0, p1 = np1, r1 = nr1;
+        if (hb + 16 < H) {
+            const uint16_t* nx = qt + (hb + 16) * 128;
+            np0 = load16_stream(nx + nro);
+            nr0 = load16_stream(nx + ro);
+            np1 = load16_stream(nx + 8 * 128 + nro);
+            nr1 = load16_stream(nx + 8 * 128 + ro);
+        }
         const Q8 qp0 = quant8(p0, a.e_lo);
         const Q8 qr0 = quant8(rope8<NEOX>(r0, C, S), a.e_lo);
         const Q8 qp1 = quant8(p1, a.e_lo);
         const Q8 qr1 = quant8(rope8<NEOX>(r1, C, S), a.e_lo);
-        *reinterpret_cast<uint32_t*>(ot + h0 * 64 + nro / 2 + 4 * c) = qp0.codes;
-        *reinterpret_cast<uint32_t*>(ot + h0 * 64 + ro / 2 + 4 * c) = qr0.codes;
-        *reinterpret_cast<uint32_t*>(ot + h1 * 64 + nro / 2 + 4 * c) = qp1.codes;
-        *reinterpret_cast<uint32_t*>(ot + h1 * 64 + ro / 2 + 4 * c) = qr1.codes;
+        uint8_t* o = ot + hb * 64;
+        store4_stream(o + nro / 2, qp0.codes);
+        store4_stream(o + ro / 2, qr0.codes);
+        store4_stream(o + 8 * 64 + nro / 2, qp1.codes);
+        store4_stream(o + 8 * 64 + ro / 2, qr1.codes);
         if (writer) {
+            const int h0 = hb + hsub, h1 = h0 + 8;
             scb[(g_pln * 16 + (h0 & 15)) * J + (h0 >> 4)] = (uint8_t)qp0.e;
             scb[(g_rot * 16 + (h0 & 15)) * J + (h0 >> 4)] = (uint8_t)qr0.e;
             scb[(g_pln * 16 + (h1 & 15)) * J + (h1 >> 4)] = (uint8_t)qp1.e;
             scb[(g_rot * 16 + (h1 & 15)) * J + (h1 >> 4)] = (uint8_t)qr1.e;
         }
     }
-    q_token_epilogue(a, t, lane, sc);
 }
 
 // With the Hadamard every output mixes the whole 128-row, so a wave-load is 4
-// full heads (16 lanes each); RoPE is computed on every lane and kept only on
-// the lanes of the rotated slice.
+// full heads (16 lanes each, lane chunk c = chunk_of(lane & 15)); RoPE is
+// computed on every lane and kept only on the lanes of the rotated slice.
 template <bool NEOX>
-__global__ __launch_bounds__(kBlock) void q_row_kernel(QArgs a) {
-    extern __shared__ uint32_t smem[];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-    if (t >= a.T) return;
+__device__ __forceinline__ void q_row_token(const QArgs& a, int64_t t, int lane, uint8_t* scb,
+                                            const float C[8], const float S[8]) {
     const int H = a.H;
     const int J = a.J;
-    uint32_t* sc = smem + wave * 16 * J;
-    uint8_t* scb = reinterpret_cast<uint8_t*>(sc);
-    q_token_prologue(a, t, lane, sc);
-
-    const int64_t pos = clamped_position(a.positions, a.pos64, t, a.max_pos);
     const int c = chunk_of(lane & 15);
     const int hsub = lane >> 4;
     const bool rot_lane = (c >> 3) == (a.rope_offset >> 6);
-    float C[8], S[8];
-    rope_coeffs<NEOX>(a.cos_sin + pos * 64, c & 7, C, S);
     const int g = c >> 2;
     const bool writer = (lane & 3) == 0;
-    const uint16_t* qt = a.q + t * (int64_t)H * 128;
-    uint8_t* ot = a.q_out + t * (int64_t)H * 64;
+    const uint16_t* qt = a.q + t * (int64_t)H * 128 + hsub * 128 + 8 * c;
+    uint8_t* ot = a.q_out + t * (int64_t)H * 64 + hsub * 64 + 4 * c;
 
     for (int hb = 0; hb < H; hb += 8) {
-        const int h0 = hb + hsub;
-        const int h1 = h0 + 4;
-        const uint4 v0 = load16(qt + h0 * 128 + 8 * c);
-        const uint4 v1 = load16(qt + h1 * 128 + 8 * c);
+        const uint4 v0 = load16_stream(qt + hb * 128);
+        const uint4 v1 = load16_stream(qt + (hb + 4) * 128);
         const uint4 w0 = hadamard8(select4(rot_lane, rope8<NEOX>(v0, C, S), v0), c);
         const uint4 w1 = hadamard8(select4(rot_lane, rope8<NEOX>(v1, C, S), v1), c);
         const Q8 q0 = quant8(w0, a.e_lo);
         const Q8 q1 = quant8(w1, a.e_lo);
-        *reinterpret_cast<uint32_t*>(ot + h0 * 64 + 4 * c) = q0.codes;
-        *reinterpret_cast<uint32_t*>(ot + h1 * 64 + 4 * c) = q1.codes;
+        store4_stream(ot + hb * 64, q0.codes);
+        store4_stream(ot + (hb + 4) * 64, q1.codes);
         if (writer) {
+            const int h0 = hb + hsub, h1 = h0 + 4;
             scb[(g * 16 + (h0 & 15)) * J + (h0 >> 4)] = (uint8_t)q0.e;
             scb[(g * 16 + (h1 & 15)) * J + (h1 >> 4)] = (uint8_t)q1.e;
         }
     }
-    q_token_epilogue(a, t, lane, sc);
 }
 
-// ---- key kernel ----------------------------------------------------------------
-// 16 lanes per token, 4 tokens per wavefront.  A token whose slot is outside
-// the cache leaves as a whole row of 16 lanes, so the DPP patterns (all
-// within a row) only ever read lanes of the same token.
+// ---- key side ---------------------------------------------------------------------
+// One key row on the 16 lanes of a DPP row (lane chunk c = chunk_of(lane16)).
+// v holds the row's raw bf16 chunk, already loaded.  C/S are the RoPE
+// coefficients of slice chunk c & 7.  A slot outside the cache writes nothing.
 template <bool NEOX, bool NORM, bool HAD>
-__global__ __launch_bounds__(kBlock) void k_row_kernel(KArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * (kBlock / 16) + (threadIdx.x >> 4);
-    if (t >= a.T) return;
-    const int64_t slot = a.slot_mapping[t];
-    if (slot < 0 || slot >= a.nslots) return;
-    const int64_t pos = clamped_position(a.positions, a.pos64, t, a.max_pos);
-    const int c = chunk_of(lane & 15);
-
-    uint4 v = load16(a.k + t * 128 + 8 * c);
+__device__ __forceinline__ void k_row(const KArgs& a, uint4 v, int64_t slot, int lane16,
+                                      const float C[8], const float S[8]) {
+    const int c = chunk_of(lane16);
     if (NORM) {
         float G[8];
         unpack8(load16(a.gamma + 8 * c), G);
         v = rmsnorm8(v, G, a.eps);
     }
-    float C[8], S[8];
-    rope_coeffs<NEOX>(a.cos_sin + pos * 64, c & 7, C, S);
     const bool rot_lane = (c >> 3) == (a.rope_offset >> 6);
     v = select4(rot_lane, rope8<NEOX>(v, C, S), v);
     if (HAD) v = hadamard8(v, c);
     const Q8 q = quant8(v, a.e_lo);
-
     const int64_t blk = slot >> 6;
     const int p = (int)(slot & 63);
     const int g = c >> 2;
     const int64_t row = blk * 4 + g;
-    *reinterpret_cast<uint32_t*>(a.kv_cache + (row * 64 + p) * 16 + 4 * (c & 3)) = q.codes;
+    store4_stream(a.kv_cache + (row * 64 + p) * 16 + 4 * (c & 3), q.codes);
     if ((c & 3) == 0) a.kv_cache_scale[row * 64 + (p & 15) * 4 + (p >> 4)] = (uint8_t)q.e;
+}
+
+// ---- kernels ----------------------------------------------------------------------
+
+template <bool NEOX>
+__global__ __launch_bounds__(kBlock) void q_split_kernel(QArgs a) {
+    extern __shared__ uint32_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    if (t >= a.T) return;
+    uint32_t* sc = smem + wave * 16 * a.J;
+    q_token_prologue(a, t, lane, sc);
+    const int64_t pos = clamped_position(a.positions, a.pos64, t, a.max_pos);
+    float C[8], S[8];
+    rope_coeffs<NEOX>(a.cos_sin + pos * 64, chunk_of(lane & 7), C, S);
+    q_split_token<NEOX>(a, t, lane, reinterpret_cast<uint8_t*>(sc), C, S);
+    q_token_epilogue(a, t, lane, sc);
+}
+
+template <bool NEOX>
+__global__ __launch_bounds__(kBlock) void q_row_kernel(QArgs a) {
+    extern __shared__ uint32_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    if (t >= a.T) return;
+    uint32_t* sc = smem + wave * 16 * a.J;
+    q_token_prologue(a, t, lane, sc);
+    const int64_t pos = clamped_position(a.positions, a.pos64, t, a.max_pos);
+    float C[8], S[8];
+    rope_coeffs<NEOX>(a.cos_sin + pos * 64, chunk_of(lane & 7), C, S);
+    q_row_token<NEOX>(a, t, lane, reinterpret_cast<uint8_t*>(sc), C, S);
+    q_token_epilogue(a, t, lane, sc);
+}
+
+// 16 lanes per token, 4 tokens per wavefront.  The row's loads are issued
+// before its slot is inspected; a token whose slot is outside the cache then
+// leaves as a whole row of 16 lanes, so the DPP patterns (all within a row)
+// only ever read lanes of the same token.
+template <bool NEOX, bool NORM, bool HAD>
+__global__ __launch_bounds__(kBlock) void k_row_kernel(KArgs a) {
+    const int lane16 = threadIdx.x & 15;
+    const int64_t t = (int64_t)blockIdx.x * (kBlock / 16) + (threadIdx.x >> 4);
+    if (t >= a.T) return;
+    const uint4 v = load16_stream(a.k + t * 128 + 8 * chunk_of(lane16));
+    const int64_t slot = a.slot_mapping[t];
+    const int64_t pos = clamped_position(a.positions, a.pos64, t, a.max_pos);
+    float C[8], S[8];
+    rope_coeffs<NEOX>(a.cos_sin + pos * 64, chunk_of(lane16) & 7, C, S);
+    if (slot < 0 || slot >= a.nslots) return;
+    k_row<NEOX, NORM, HAD>(a, v, slot, lane16, C, S);
+}
+
+// Both sides of a token in one launch (ROCm/aiter PR 5484: one kernel writes
+// all five outputs).  One wavefront per token: the query heads as above, then
+// the key row on lanes 0..15.  The key's loads are issued first; position and
+// RoPE coefficients are shared.  The RoPE coefficients of lane L (< 16) for
+// the key are those of slice chunk chunk_of(L) & 7 = chunk_of(L & 7), the
+// same ones the split query layout gives lane L.
+template <bool NEOX, bool HAD, bool NORM>
+__global__ __launch_bounds__(kBlock) void qk_kernel(QArgs qa, KArgs ka) {
+    extern __shared__ uint32_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    if (t >= qa.T) return;
+    uint32_t* sc = smem + wave * 16 * qa.J;
+    uint4 kv = make_uint4(0u, 0u, 0u, 0u);
+    if (lane < 16) kv = load16_stream(ka.k + t * 128 + 8 * chunk_of(lane));
+    const int64_t slot = ka.slot_mapping[t];
+    q_token_prologue(qa, t, lane, sc);
+    const int64_t pos = clamped_position(qa.positions, qa.pos64, t, qa.max_pos);
+    float C[8], S[8];
+    rope_coeffs<NEOX>(qa.cos_sin + pos * 64, chunk_of(lane & 7), C, S);
+    if (HAD) q_row_token<NEOX>(qa, t, lane, reinterpret_cast<uint8_t*>(sc), C, S);
+    else q_split_token<NEOX>(qa, t, lane, reinterpret_cast<uint8_t*>(sc), C, S);
+    q_token_epilogue(qa, t, lane, sc);
+    if (lane < 16 && slot >= 0 && slot < ka.nslots) k_row<NEOX, NORM, HAD>(ka, kv, slot, lane, C, S);
 }
 
 // ---- dequantization (debug reader) -------------------------------------------
@@ -514,6 +581,16 @@ hipError_t launch(K kernel, int64_t blocks, size_t lds, hipStream_t stream, cons
                            dim3(kBlock), args, lds, stream);
 }
 
+template <typename K>
+hipError_t launch2(K kernel, int64_t blocks, size_t lds, hipStream_t stream, const QArgs& qa,
+                   const KArgs& ka) {
+    QArgs q = qa;
+    KArgs k = ka;
+    void* args[] = {&q, &k};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)blocks),
+                           dim3(kBlock), args, lds, stream);
+}
+
 }  // namespace
 
 hipError_t launch_q_rope_pack(const QArgs& a, bool is_neox, bool hadamard, hipStream_t stream) {
@@ -542,6 +619,25 @@ hipError_t launch_k_rope_pack_store(const KArgs& a, bool is_neox, bool hadamard,
         case 5: return launch(k_row_kernel<true, false, true>, blocks, 0, stream, a);
         case 6: return launch(k_row_kernel<true, true, false>, blocks, 0, stream, a);
         default: return launch(k_row_kernel<true, true, true>, blocks, 0, stream, a);
+    }
+}
+
+hipError_t launch_qk_rope_pack_store(const QArgs& qa, const KArgs& ka, bool is_neox, bool hadamard,
+                                     hipStream_t stream) {
+    if (qa.T == 0) return hipSuccess;
+    const int64_t blocks = (qa.T + kWavesPerBlock - 1) / kWavesPerBlock;
+    const size_t lds = (size_t)kWavesPerBlock * 16 * qa.J * sizeof(uint32_t);
+    const bool norm = ka.gamma != nullptr;
+    const int sel = (is_neox ? 4 : 0) | (hadamard ? 2 : 0) | (norm ? 1 : 0);
+    switch (sel) {
+        case 0: return launch2(qk_kernel<false, false, false>, blocks, lds, stream, qa, ka);
+        case 1: return launch2(qk_kernel<false, false, true>, blocks, lds, stream, qa, ka);
+        case 2: return launch2(qk_kernel<false, true, false>, blocks, lds, stream, qa, ka);
+        case 3: return launch2(qk_kernel<false, true, true>, blocks, lds, stream, qa, ka);
+        case 4: return launch2(qk_kernel<true, false, false>, blocks, lds, stream, qa, ka);
+        case 5: return launch2(qk_kernel<true, false, true>, blocks, lds, stream, qa, ka);
+        case 6: return launch2(qk_kernel<true, true, false>, blocks, lds, stream, qa, ka);
+        default: return launch2(qk_kernel<true, true, true>, blocks, lds, stream, qa, ka);
     }
 }
 

@@ -54,6 +54,10 @@ def lib():
             L.fp4idx_k_rope_pack_store.argtypes = [_p, _p, _i, _p, _i64, _p, _p, _f, _i64, _i, _i,
                                                    _i, _i, _i, _i, _f, _p, _p, _i64, _i, _p]
             L.fp4idx_k_rope_pack_store.restype = _i
+            L.fp4idx_qk_rope_pack_store.argtypes = [_p, _p, _p, _i, _p, _i64, _p, _p, _p, _f,
+                                                    _i64, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p,
+                                                    _p, _p, _p, _i64, _i, _p]
+            L.fp4idx_qk_rope_pack_store.restype = _i
             L.fp4idx_dequant_debug.argtypes = [_i, _p, _p, _i64, _i, _p, _i64, _i, _p, _p]
             L.fp4idx_dequant_debug.restype = _i
             L.fp4idx_last_error.argtypes = []
@@ -153,6 +157,43 @@ def k_rope_pack_store(k, positions, cos_sin, slot_mapping, kv_cache, kv_cache_sc
         _ptr(kv_cache_scale), NB, KV_BLOCK, _stream_handle(stream))
     _check(rc)
     return kv_cache, kv_cache_scale
+
+
+def qk_rope_pack_store(q, k, positions, cos_sin, slot_mapping, kv_cache, kv_cache_scale,
+                       weights=None, *, q_out=None, q_scale_out=None, weights_out=None,
+                       k_norm_gamma=None, k_norm_eps=1e-6, is_neox=True, rope_offset=64,
+                       apply_hadamard=False, scale_floor=DEFAULT_SCALE_FLOOR, stream=None):
+    """fp4idx_qk_rope_pack_store: the query and key sides in one launch.
+    Returns (q_out, q_scale_out, weights_out); the cache tensors are updated in place."""
+    T, H, D = q.shape
+    dev = q.device
+    _require(q, "q", (torch.bfloat16, torch.int16, torch.uint16))
+    _require(k, "k", (torch.bfloat16, torch.int16, torch.uint16), dev)
+    _require(positions, "positions", (torch.int32, torch.int64), dev)
+    _require(cos_sin, "cos_sin", (torch.float32,), dev)
+    _require(weights, "weights", (torch.float32,), dev)
+    _require(slot_mapping, "slot_mapping", (torch.int64,), dev)
+    _require(kv_cache, "kv_cache", (torch.uint8,), dev)
+    _require(kv_cache_scale, "kv_cache_scale", (torch.uint8,), dev)
+    _require(k_norm_gamma, "k_norm_gamma", (torch.bfloat16, torch.int16, torch.uint16), dev)
+    J = q_scale_cols(H)
+    if q_out is None:
+        q_out = torch.empty((T, H, D // 2), dtype=torch.uint8, device=dev)
+    if q_scale_out is None:
+        q_scale_out = torch.empty((T, 1, 4, 16, J), dtype=torch.uint8, device=dev)
+    if weights is not None and weights_out is None:
+        weights_out = torch.empty_like(weights)
+    _require(q_out, "q_out", (torch.uint8,), dev)
+    _require(q_scale_out, "q_scale_out", (torch.uint8,), dev)
+    _require(weights_out, "weights_out", (torch.float32,), dev)
+    rc = lib().fp4idx_qk_rope_pack_store(
+        _ptr(q), _ptr(k), _ptr(positions), int(positions.dtype == torch.int64), _ptr(cos_sin),
+        cos_sin.shape[0], _ptr(weights), _ptr(slot_mapping), _ptr(k_norm_gamma), k_norm_eps, T,
+        H, D, ROPE_DIM, rope_offset, GROUP, int(is_neox), int(apply_hadamard), scale_floor,
+        _ptr(q_out), _ptr(q_scale_out), _ptr(weights_out), _ptr(kv_cache), _ptr(kv_cache_scale),
+        kv_cache.shape[0], KV_BLOCK, _stream_handle(stream))
+    _check(rc)
+    return q_out, q_scale_out, weights_out
 
 
 def dequant_q(q_out, q_scale_out, *, out=None, stream=None):

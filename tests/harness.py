@@ -39,8 +39,11 @@ def dev_tensors(wl: Workload, device):
     return d
 
 
-def gpu_run(wl: Workload, device="cuda:0", with_weights=True, positions_dtype=None, stream=None):
-    """Returns numpy (q_out, q_scale_out, weights_out, kv_cache, kv_cache_scale)."""
+def gpu_run(wl: Workload, device="cuda:0", with_weights=True, positions_dtype=None, stream=None,
+            fused=False):
+    """Returns numpy (q_out, q_scale_out, weights_out, kv_cache, kv_cache_scale).
+    fused=False: fp4idx_q_rope_pack then fp4idx_k_rope_pack_store; True: the single
+    fp4idx_qk_rope_pack_store launch."""
     import torch
 
     from pack_token_amd import fp4idx
@@ -60,10 +63,16 @@ def gpu_run(wl: Workload, device="cuda:0", with_weights=True, positions_dtype=No
     if wl.background is not None:
         fp4idx.k_rope_pack_store(d["bg_k"], d["bg_positions"], d["cos_sin"], d["bg_slots"], kv, ks,
                                  k_norm_gamma=d["gamma"], k_norm_eps=wl.k_norm_eps, **common)
-    fp4idx.q_rope_pack(d["q"], pos, d["cos_sin"], d["weights"] if with_weights else None,
-                       q_out=q_out, q_scale_out=qs, weights_out=w_out, **common)
-    fp4idx.k_rope_pack_store(d["k"], pos, d["cos_sin"], d["slot_mapping"], kv, ks,
-                             k_norm_gamma=d["gamma"], k_norm_eps=wl.k_norm_eps, **common)
+    if fused:
+        fp4idx.qk_rope_pack_store(d["q"], d["k"], pos, d["cos_sin"], d["slot_mapping"], kv, ks,
+                                  d["weights"] if with_weights else None, q_out=q_out,
+                                  q_scale_out=qs, weights_out=w_out, k_norm_gamma=d["gamma"],
+                                  k_norm_eps=wl.k_norm_eps, **common)
+    else:
+        fp4idx.q_rope_pack(d["q"], pos, d["cos_sin"], d["weights"] if with_weights else None,
+                           q_out=q_out, q_scale_out=qs, weights_out=w_out, **common)
+        fp4idx.k_rope_pack_store(d["k"], pos, d["cos_sin"], d["slot_mapping"], kv, ks,
+                                 k_norm_gamma=d["gamma"], k_norm_eps=wl.k_norm_eps, **common)
     torch.cuda.synchronize()
     return (q_out.cpu().numpy(), qs.cpu().numpy(), None if w_out is None else w_out.cpu().numpy(),
             kv.cpu().numpy(), ks.cpu().numpy())

@@ -26,7 +26,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert names == ["fp4idx_dequant_debug", "fp4idx_k_rope_pack_store", "fp4idx_last_error",
-                     "fp4idx_q_rope_pack"]
+                     "fp4idx_q_rope_pack", "fp4idx_qk_rope_pack_store"]
     lib = ctypes.CDLL(fp4idx.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -49,6 +49,16 @@ def k_call(**over):
              stream=None)
     a.update(over)
     return fp4idx.lib().fp4idx_k_rope_pack_store(*a.values())
+
+
+def qk_call(**over):
+    a = dict(q=ALIGNED, k=ALIGNED, positions=ALIGNED, positions_int64=1, cos_sin=ALIGNED,
+             max_pos=16, weights=None, slot_mapping=ALIGNED, k_norm_gamma=None, k_norm_eps=1e-6,
+             T=4, H=32, D=128, R=64, rope_offset=64, group_size=32, is_neox=1, apply_hadamard=0,
+             scale_floor=2.0 ** -126, q_out=ALIGNED, q_scale_out=ALIGNED, weights_out=None,
+             kv_cache=ALIGNED, kv_cache_scale=ALIGNED, NB=2, BS=64, stream=None)
+    a.update(over)
+    return fp4idx.lib().fp4idx_qk_rope_pack_store(*a.values())
 
 
 def d_call(**over):
@@ -135,11 +145,36 @@ def test_dequant_rejections(over, code, msg):
     assert msg in fp4idx.last_error(), fp4idx.last_error()
 
 
+QK_REJECT = [
+    (dict(D=64), fp4idx.EUNSUPPORTED, "head_dim"),
+    (dict(H=40), fp4idx.EUNSUPPORTED, "n_heads"),
+    (dict(BS=16), fp4idx.EUNSUPPORTED, "kv_block_size"),
+    (dict(q=None), fp4idx.EINVAL, "q must not be NULL"),
+    (dict(k=None), fp4idx.EINVAL, "k must not be NULL"),
+    (dict(k=MISALIGNED), fp4idx.EINVAL, "k must be 16-byte aligned"),
+    (dict(slot_mapping=None), fp4idx.EINVAL, "slot_mapping must not be NULL"),
+    (dict(weights=ALIGNED), fp4idx.EINVAL, "weights and weights_out"),
+    (dict(kv_cache=ALIGNED + 8), fp4idx.EINVAL, "kv_cache must be 16-byte"),
+    (dict(q_scale_out=ALIGNED + 2), fp4idx.EINVAL, "q_scale_out must be 4-byte"),
+    (dict(k_norm_gamma=ALIGNED, k_norm_eps=-2.0), fp4idx.EINVAL, "k_norm_eps"),
+    (dict(NB=-3), fp4idx.EINVAL, "NB must be"),
+]
+
+
+@pytest.mark.parametrize("over,code,msg", QK_REJECT)
+def test_qk_rejections(over, code, msg):
+    assert qk_call(**over) == code
+    assert msg in fp4idx.last_error(), fp4idx.last_error()
+    assert fp4idx.last_error().startswith("fp4idx_qk_rope_pack_store:")
+
+
 def test_zero_tokens_is_a_noop_even_with_null_buffers():
     assert q_call(T=0, q=None, positions=None, cos_sin=None, q_out=None, q_scale_out=None) == 0
     assert k_call(T=0, k=None, positions=None, cos_sin=None, slot_mapping=None, kv_cache=None,
                   kv_cache_scale=None) == 0
     assert d_call(rows=0, packed=None, scales=None, out=None) == 0
+    assert qk_call(T=0, q=None, k=None, positions=None, cos_sin=None, slot_mapping=None,
+                   q_out=None, q_scale_out=None, kv_cache=None, kv_cache_scale=None) == 0
     # but shapes are still checked first
     assert q_call(T=0, D=64) == fp4idx.EUNSUPPORTED
 

@@ -15,35 +15,42 @@ pytestmark = pytest.mark.gpu
 
 def check(wl, **kw):
     say(f"case {wl.name}: T={wl.T} H={wl.H} neox={wl.is_neox} ro={wl.rope_offset} "
-        f"had={wl.apply_hadamard} norm={wl.k_norm_gamma is not None}")
+        f"had={wl.apply_hadamard} norm={wl.k_norm_gamma is not None} fused={kw.get('fused')}")
     got = gpu_run(wl, **kw)
     ref = oracle_run(wl, with_weights=kw.get("with_weights", True))
     assert_all_same(got, ref)
     return got
 
 
-def test_tiny():
-    check(workloads.tiny())
+FUSED = pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused"])
 
 
+@FUSED
+def test_tiny(fused):
+    check(workloads.tiny(), fused=fused)
+
+
+@FUSED
 @pytest.mark.parametrize("pos32", [False, True])
-def test_edge_mix(pos32):
-    check(workloads.edge_mix(positions_int32=pos32))
+def test_edge_mix(pos32, fused):
+    check(workloads.edge_mix(positions_int32=pos32), fused=fused)
 
 
+@FUSED
 @pytest.mark.parametrize("T", [8, 32])
 @pytest.mark.parametrize("H", [32, 64])
 @pytest.mark.parametrize("is_neox", [True, False])
 @pytest.mark.parametrize("rope_offset", [0, 64])
-def test_sweep(T, H, is_neox, rope_offset):
-    check(workloads.sweep_case(100 + T + H, T, H, is_neox, rope_offset))
+def test_sweep(T, H, is_neox, rope_offset, fused):
+    check(workloads.sweep_case(100 + T + H, T, H, is_neox, rope_offset), fused=fused)
 
 
+@FUSED
 @pytest.mark.parametrize("is_neox", [True, False])
 @pytest.mark.parametrize("rope_offset", [0, 64])
 @pytest.mark.parametrize("norm", [False, True])
 @pytest.mark.parametrize("had", [False, True])
-def test_modes_ragged(is_neox, rope_offset, norm, had):
+def test_modes_ragged(is_neox, rope_offset, norm, had, fused):
     """Every kernel variant on a ragged token count (not a multiple of the 4
     or 16 tokens a block covers) and 16, 48 and 80 heads."""
     for T, H in [(1, 16), (37, 48), (301, 80)]:
@@ -52,31 +59,35 @@ def test_modes_ragged(is_neox, rope_offset, norm, had):
         if norm:
             rng = np.random.default_rng(T)
             wl.k_norm_gamma = workloads.to_bf16_bits((1 + 0.1 * rng.standard_normal(128)).astype(np.float32))
-        check(wl)
+        check(wl, fused=fused)
 
 
-def test_no_weights_and_scale_floor():
+@FUSED
+def test_no_weights_and_scale_floor(fused):
     wl = workloads.edge_mix(seed=21, T=64)
     wl.scale_floor = float(np.float32(1e-10))   # all-zero groups get e = 94
-    check(wl, with_weights=False)
+    check(wl, with_weights=False, fused=fused)
 
 
-def test_out_of_range_positions_and_slots():
+@FUSED
+def test_out_of_range_positions_and_slots(fused):
     wl = workloads.sweep_case(5, 40, 32, True, 64)
     wl.positions[:4] = [-3, wl.max_pos, wl.max_pos + 99, 2 ** 40]
     wl.slot_mapping[4:8] = [-1, -5, wl.NB * 64, wl.NB * 64 + 12345]
-    check(wl)
+    check(wl, fused=fused)
 
 
-def test_decode_with_background_cache():
+@FUSED
+def test_decode_with_background_cache(fused):
     wl = workloads.decode()
-    got = check(wl)
+    got = check(wl, fused=fused)
     # every slot was written by the background keys: no sentinel row is left
     assert not (got[4] == SENTINEL).all(axis=-1).any()
 
 
-def test_prefill_norm_rotate():
-    check(workloads.prefill_norm_rotate())
+@FUSED
+def test_prefill_norm_rotate(fused):
+    check(workloads.prefill_norm_rotate(), fused=fused)
 
 
 def test_non_default_stream():
@@ -171,11 +182,12 @@ def test_dequant_debug_matches_oracle():
     assert_same("dequant_k_all", kall.cpu().numpy(), oracle.dequant_kcache(kv, ks))
 
 
-def test_large_prefill_full_size_sampled():
-    """T = 131072, H = 64 in the launch configuration the benchmark times:
-    4,099 sampled tokens (including the first, the last and outlier rows)
-    against the oracle on all five outputs; at full size, every cache slot is
-    written and every exponent lies in [1, 253]."""
+@FUSED
+def test_large_prefill_full_size_sampled(fused):
+    """T = 131072, H = 64 in the launch configurations the benchmark times:
+    4,099 tokens (the first, the last and 4,096 random ones, about 1% of them
+    outlier rows) against the oracle on all five outputs; at full size, every
+    cache slot is written and every exponent lies in [1, 253]."""
     import torch
 
     from pack_token_amd import fp4idx
@@ -184,7 +196,7 @@ def test_large_prefill_full_size_sampled():
     say(f"case {wl.name}: T={wl.T} H={wl.H} (inputs generated)")
     rng = np.random.default_rng(123)
     idx = np.unique(np.concatenate([rng.choice(wl.T, 4096, replace=False), [0, 1, wl.T - 1]]))
-    got = gpu_run(wl)
+    got = gpu_run(wl, fused=fused)
     q_out, qs, w_out, kv, ks = got
     say("case large_prefill: GPU outputs copied back")
     ref_q, ref_qs, ref_w = oracle.q_rope_pack(wl.q[idx], wl.positions[idx], wl.cos_sin, wl.weights[idx],
