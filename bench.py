@@ -75,9 +75,12 @@ def cpu_baseline(wl, n_tokens: int, threads: int):
     kv, ks = wl.empty_cache()
     t0 = time.perf_counter()
     oracle.q_rope_pack(wl.q[sl], wl.positions[sl], wl.cos_sin, wl.weights[sl],
-                       is_neox=wl.is_neox, rope_offset=wl.rope_offset, threads=threads)
+                       is_neox=wl.is_neox, rope_offset=wl.rope_offset,
+                       apply_hadamard=wl.apply_hadamard, threads=threads)
     oracle.k_rope_pack_store(wl.k[sl], wl.positions[sl], wl.cos_sin, wl.slot_mapping[sl], kv, ks,
-                             is_neox=wl.is_neox, rope_offset=wl.rope_offset, threads=threads)
+                             k_norm_gamma=wl.k_norm_gamma, k_norm_eps=wl.k_norm_eps,
+                             is_neox=wl.is_neox, rope_offset=wl.rope_offset,
+                             apply_hadamard=wl.apply_hadamard, threads=threads)
     dt = time.perf_counter() - t0
     del np
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
@@ -90,8 +93,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--tokens", type=int, default=131072)
-    ap.add_argument("--heads", type=int, default=64)
+    ap.add_argument("--workload", default="large_prefill",
+                    choices=["large_prefill", "prefill_norm_rotate", "decode"],
+                    help="large_prefill is the headline configuration; the other two are timed "
+                         "for reference")
+    ap.add_argument("--tokens", type=int, default=131072, help="large_prefill only")
+    ap.add_argument("--heads", type=int, default=64, help="large_prefill only")
     ap.add_argument("--cpu-sample-tokens", type=int, default=131072)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -133,7 +140,10 @@ def main():
         return
 
     t_gen = time.perf_counter()
-    wl = workloads.large_prefill(T=args.tokens, H=args.heads)
+    if args.workload == "large_prefill":
+        wl = workloads.large_prefill(T=args.tokens, H=args.heads)
+    else:
+        wl = workloads.RECIPES[args.workload]()
     print(f"bench: generated {wl.name} T={wl.T} H={wl.H} in {time.perf_counter() - t_gen:.1f}s",
           file=sys.stderr, flush=True)
 
@@ -154,18 +164,27 @@ def main():
     kv = torch.zeros((wl.NB, 1, 4, 64, 16), dtype=torch.uint8, device=dev)
     ks = torch.zeros((wl.NB, 1, 4, 64), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    gamma = None if wl.k_norm_gamma is None else up(wl.k_norm_gamma.view(np.int16))
 
-    common = dict(is_neox=wl.is_neox, rope_offset=wl.rope_offset, stream=stream)
+    common = dict(is_neox=wl.is_neox, rope_offset=wl.rope_offset,
+                  apply_hadamard=wl.apply_hadamard, stream=stream)
+    kcommon = dict(common, k_norm_gamma=gamma, k_norm_eps=wl.k_norm_eps)
+    if wl.background is not None:
+        # fill the cache with the background keys first (not timed)
+        fp4idx.k_rope_pack_store(up(wl.background["k"].view(np.int16)),
+                                 up(wl.background["positions"]), cs, up(wl.background["slots"]),
+                                 kv, ks, **kcommon)
+        torch.cuda.synchronize()
 
     def q_call():
         fp4idx.q_rope_pack(q, pos, cs, w, q_out=q_out, q_scale_out=qs, weights_out=w_out, **common)
 
     def k_call():
-        fp4idx.k_rope_pack_store(k, pos, cs, slots, kv, ks, **common)
+        fp4idx.k_rope_pack_store(k, pos, cs, slots, kv, ks, **kcommon)
 
     def qk_call():
         fp4idx.qk_rope_pack_store(q, k, pos, cs, slots, kv, ks, w, q_out=q_out, q_scale_out=qs,
-                                  weights_out=w_out, **common)
+                                  weights_out=w_out, **kcommon)
 
     def timed(calls, K, W):
         """Run W untimed then K timed steps of `calls` (launched back to back on
@@ -196,7 +215,7 @@ def main():
 
     step_bytes = step_bytes_per_token(H) * T
     achieved = step_bytes / (fused_ms * 1e-3) / 1e9
-    traffic = measured_traffic()
+    traffic = measured_traffic() if wl.name == "large_prefill" and (T, H) == (131072, 64) else None
     rec = {
         "metric": "tokens/s and achieved HBM GB/s (% of peak), fused q+k RoPE/FP4 pack+store",
         "value": T / (ms_per_step * 1e-3),
@@ -211,8 +230,10 @@ def main():
         "dtype": "bf16->e2m1",
         "data": "synthetic",
         "config": {"workload": wl.name, "tokens": T, "heads": H, "head_dim": 128, "rope_dim": 64,
-                   "rope": "neox", "rope_offset": wl.rope_offset, "kv_blocks": wl.NB,
-                   "kv_block_size": 64, "slot_mapping": "contiguous",
+                   "rope": "neox" if wl.is_neox else "interleaved", "rope_offset": wl.rope_offset,
+                   "key_rmsnorm": wl.k_norm_gamma is not None, "hadamard": wl.apply_hadamard,
+                   "kv_blocks": wl.NB, "kv_block_size": 64,
+                   "slot_mapping": "random distinct" if wl.background is not None else "contiguous",
                    "step": "fp4idx_qk_rope_pack_store (one launch)"},
         "step_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "step_frac_of_hbm_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -221,7 +242,9 @@ def main():
                           "GBps": step_bytes / (two_ms * 1e-3) / 1e9,
                           "q_kernel_us": q_ms * 1e3, "k_kernel_us": k_ms * 1e3,
                           "q_kernel_GBps": q_bytes_per_token(H) * T / (q_ms * 1e-3) / 1e9},
-        "roofline": {"kernel": "qk_kernel<neox>", "bound": "hbm", "achieved": achieved,
+        "roofline": {"kernel": "qk_kernel<neox=%d,hadamard=%d,norm=%d>" % (
+                         wl.is_neox, wl.apply_hadamard, wl.k_norm_gamma is not None),
+                     "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": step_bytes,
                      "launch_us": fused_ms * 1e3},
