@@ -101,6 +101,10 @@ def main():
     ap.add_argument("--heads", type=int, default=64, help="large_prefill only")
     ap.add_argument("--cpu-sample-tokens", type=int, default=131072)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
+                    help="time steps replayed from captured HIP graphs (auto: on for decode, where "
+                         "host launch overhead exceeds the kernel time)")
+    ap.add_argument("--graph-steps", type=int, default=10, help="steps captured per graph")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="instead of the benchmark, time one plain device copy of this many MiB "
                          "(reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -166,8 +170,10 @@ def main():
     stream = torch.cuda.current_stream(dev)
     gamma = None if wl.k_norm_gamma is None else up(wl.k_norm_gamma.view(np.int16))
 
+    # stream=None: each call goes to torch's current stream (the capture stream
+    # while a graph is being recorded)
     common = dict(is_neox=wl.is_neox, rope_offset=wl.rope_offset,
-                  apply_hadamard=wl.apply_hadamard, stream=stream)
+                  apply_hadamard=wl.apply_hadamard, stream=None)
     kcommon = dict(common, k_norm_gamma=gamma, k_norm_eps=wl.k_norm_eps)
     if wl.background is not None:
         # fill the cache with the background keys first (not timed)
@@ -209,9 +215,39 @@ def main():
                     for j in range(len(calls))]
         return t0.elapsed_time(t1) / K, per_call
 
+    use_graph = args.graph == "on" or (args.graph == "auto" and wl.name == "decode")
+
+    G = max(1, args.graph_steps)
+
+    def graphed(fns):
+        """A HIP graph holding G steps of fns (warmed up on a side stream first)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for f in fns:
+                f()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(G):
+                for f in fns:
+                    f()
+        torch.cuda.synchronize()
+        return g.replay
+
     K = args.steps
+    # per-launch durations always come from eager launches bracketed by events
     ms_per_step, (fused_ms,) = timed([qk_call], K, args.warmup)
     two_ms, (q_ms, k_ms) = timed([q_call, k_call], K, args.warmup)
+    if use_graph:
+        # step time from graph replays: K steps = ceil(K / G) replays of G steps
+        reps = -(-K // G)
+        K = reps * G
+        g_ms, _ = timed([graphed([qk_call])], reps, max(1, args.warmup // G))
+        g2_ms, _ = timed([graphed([q_call, k_call])], reps, max(1, args.warmup // G))
+        eager_ms_per_step, eager_two_ms = ms_per_step, two_ms
+        ms_per_step, two_ms = g_ms / G, g2_ms / G
 
     step_bytes = step_bytes_per_token(H) * T
     achieved = step_bytes / (fused_ms * 1e-3) / 1e9
@@ -234,7 +270,8 @@ def main():
                    "key_rmsnorm": wl.k_norm_gamma is not None, "hadamard": wl.apply_hadamard,
                    "kv_blocks": wl.NB, "kv_block_size": 64,
                    "slot_mapping": "random distinct" if wl.background is not None else "contiguous",
-                   "step": "fp4idx_qk_rope_pack_store (one launch)"},
+                   "step": "fp4idx_qk_rope_pack_store (one launch)",
+                   "graph_replay": use_graph, "graph_steps": G if use_graph else None},
         "step_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "step_frac_of_hbm_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "two_call_step": {"calls": "fp4idx_q_rope_pack + fp4idx_k_rope_pack_store",
@@ -249,6 +286,9 @@ def main():
                      "traffic": traffic, "algorithmic_bytes_per_launch": step_bytes,
                      "launch_us": fused_ms * 1e3},
     }
+    if use_graph:
+        rec["eager_ms_per_step"] = eager_ms_per_step
+        rec["two_call_step"]["eager_ms_per_step"] = eager_two_ms
     if not args.no_cpu_baseline:
         threads = max(1, min(16, len(os.sched_getaffinity(0))))
         rec["cpu_baseline"] = cpu_baseline(wl, min(args.cpu_sample_tokens, T), threads)

@@ -217,3 +217,107 @@ def test_large_prefill_full_size_sampled(fused):
     assert ks.min() >= 1 and ks.max() <= 253
     assert qs.min() >= 1 and qs.max() <= 253
     assert np.array_equal(w_out.view(np.uint32), wl.weights.view(np.uint32))
+
+
+def _cosine_accumulate(acc, a, b):
+    acc[0] += float((a.double() * b.double()).sum())
+    acc[1] += float((a.double() ** 2).sum())
+    acc[2] += float((b.double() ** 2).sum())
+
+
+def test_decode_score_cosine():
+    """Dequantized per-head q.k scores of the 256 decode queries (x 32 heads)
+    against all 262,144 cached keys: cosine >= 0.9999 between the GPU's and the
+    oracle's dequantized values, and >= 0.97 against the unquantized rotated
+    bf16 vectors (the pages report 0.980 for an FP4 indexer pipeline against bf16
+    ground truth, ROCm/aiter PR 5484 "Verification")."""
+    import torch
+
+    from pack_token_amd import fp4idx
+    from pack_token_amd.workloads import bf16_bits_to_f32
+
+    wl = workloads.decode()
+    say(f"case decode scores: {wl.T}x{wl.H} queries vs {wl.NB * 64} keys")
+    got = gpu_run(wl, fused=True)
+    ref = oracle_run(wl)
+    assert_all_same(got, ref)
+    q_out, qs, _, kv, ks = got
+    dev = "cuda:0"
+    # GPU-side dequantization of the GPU's bytes; oracle-side of the oracle's bytes
+    qd_gpu = fp4idx.dequant_q(torch.from_numpy(q_out).to(dev), torch.from_numpy(qs).to(dev))
+    kd_gpu = fp4idx.dequant_kcache(torch.from_numpy(kv).to(dev), torch.from_numpy(ks).to(dev))
+    qd_ref = torch.from_numpy(oracle.dequant_q(ref[0], ref[1])).to(dev)
+    kd_ref = torch.from_numpy(oracle.dequant_kcache(ref[3], ref[4])).to(dev)
+    # unquantized reference: the same RoPE on the bf16 inputs, keys as the cache holds them
+    cs = wl.cos_sin[wl.positions]
+    qr = oracle.rope_rows(bf16_bits_to_f32(wl.q).reshape(-1, 128), np.repeat(cs, wl.H, 0))
+    k_all = bf16_bits_to_f32(wl.background["k"]).copy()
+    pos_all = wl.background["positions"].copy()
+    k_all[wl.slot_mapping] = bf16_bits_to_f32(wl.k)
+    pos_all[wl.slot_mapping] = wl.positions
+    kr = oracle.rope_rows(k_all, wl.cos_sin[pos_all])
+    qr = torch.from_numpy(qr).to(dev)
+    kr = torch.from_numpy(kr).to(dev)
+    Q = [qd_gpu.reshape(-1, 128), qd_ref.reshape(-1, 128), qr]
+    acc_ref, acc_bf16 = [0.0, 0.0, 0.0], [0.0, 0.0, 0.0]
+    for a in range(0, kd_gpu.shape[0], 32768):
+        kt = [x[a:a + 32768].t().contiguous() for x in (kd_gpu, kd_ref, kr)]
+        s_gpu = Q[0] @ kt[0]
+        s_ref = Q[1] @ kt[1]
+        s_bf = Q[2] @ kt[2]
+        _cosine_accumulate(acc_ref, s_gpu, s_ref)
+        _cosine_accumulate(acc_bf16, s_gpu, s_bf)
+    cos_ref = acc_ref[0] / np.sqrt(acc_ref[1] * acc_ref[2])
+    cos_bf = acc_bf16[0] / np.sqrt(acc_bf16[1] * acc_bf16[2])
+    say(f"score cosine: vs oracle {cos_ref:.7f}, vs bf16 {cos_bf:.5f}")
+    assert cos_ref >= 0.9999
+    assert cos_bf >= 0.97
+
+
+def test_graph_replay_matches_oracle():
+    """The fused call captured in a HIP graph, replayed three times with new
+    inputs copied in (eager work) between replays; every replay equals the
+    oracle on that replay's inputs."""
+    import torch
+
+    from pack_token_amd import fp4idx
+
+    dev = "cuda:0"
+    base = workloads.sweep_case(31, 48, 32, True, 64)
+    from harness import dev_tensors
+    d = dev_tensors(base, dev)
+    T, H = base.T, base.H
+    q_out = torch.empty((T, H, 64), dtype=torch.uint8, device=dev)
+    qs = torch.empty((T, 1, 4, 16, base.J), dtype=torch.uint8, device=dev)
+    w_out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    kv = torch.empty((base.NB, 1, 4, 64, 16), dtype=torch.uint8, device=dev)
+    ks = torch.empty((base.NB, 1, 4, 64), dtype=torch.uint8, device=dev)
+
+    def step():
+        fp4idx.qk_rope_pack_store(d["q"], d["k"], d["positions"], d["cos_sin"], d["slot_mapping"],
+                                  kv, ks, d["weights"], q_out=q_out, q_scale_out=qs,
+                                  weights_out=w_out)
+
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        wl = workloads.sweep_case(40 + rep, T, H, True, 64)
+        wl.slot_mapping = base.slot_mapping
+        wl.positions = base.positions
+        for name, arr in (("q", wl.q.view(np.int16)), ("k", wl.k.view(np.int16)),
+                          ("weights", wl.weights)):
+            d[name].copy_(torch.from_numpy(arr).to(dev))
+        kv.fill_(SENTINEL)
+        ks.fill_(SENTINEL)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (q_out.cpu().numpy(), qs.cpu().numpy(), w_out.cpu().numpy(), kv.cpu().numpy(),
+               ks.cpu().numpy())
+        assert_all_same(got, oracle_run(wl))
