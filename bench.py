@@ -88,13 +88,83 @@ def cpu_baseline(wl, n_tokens: int, threads: int):
                       f"path), {threads} threads, {dt:.2f} s wall"}
 
 
+FP4_MFMA_PEAK_TFLOPS = 10100.0
+
+
+def bench_scorer(args, dev):
+    """fp4idx_paged_mqa_logits over a decode batch: 64 sequences x next_n 4 query
+    tokens, H = 32, contexts U[4096, 131072] keys, every sequence on its own cache
+    blocks (random FP4 bytes, e8m0 exponents U[118, 130])."""
+    import numpy as np
+    import torch
+
+    from pack_token_amd import fp4idx, workloads
+
+    B, next_n, H = 64, 4, 32
+    sc = workloads.scorer_case(7, B, next_n, H, 4096, 131072)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    q, qs, w = up(sc.q_out), up(sc.q_scale_out), up(sc.weights)
+    kv, ks = up(sc.kv_cache), up(sc.kv_cache_scale)
+    table, ctx = up(sc.block_table), up(sc.context_lens)
+    stride = sc.max_blocks * 64
+    logits = torch.empty((B * next_n, stride), dtype=torch.float32, device=dev)
+
+    def call():
+        fp4idx.paged_mqa_logits(q, qs, w, kv, ks, table, ctx, next_n, logits=logits)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream(dev)
+    t0.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        call()
+        ev[i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / K
+    launch_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    keys = int(sc.context_lens.astype(np.int64).sum())
+    blocks = int(sum(-(-int(c) // 64) for c in sc.context_lens))
+    J = workloads.q_scale_cols(H)
+    T = B * next_n
+    bytes_ = (keys * (64 + 4) + T * (64 * H + 64 * J + 4 * H) + blocks * 4 + B * 4
+              + keys * next_n * 4)
+    flops = 2.0 * 128 * H * next_n * keys
+    gbs = bytes_ / (launch_ms * 1e-3) / 1e9
+    tfs = flops / (launch_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "FP4 paged MQA logits: keys scored per second and achieved HBM GB/s",
+        "value": keys / (ms_per_step * 1e-3), "unit": "keys/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "e2m1 x e2m1 -> fp32 (scaled MFMA)",
+        "data": "synthetic",
+        "config": {"workload": "decode_scoring", "sequences": B, "next_n": next_n, "heads": H,
+                   "head_dim": 128, "kv_block_size": 64, "keys": keys, "context": "U[4096,131072]",
+                   "relu": True},
+        "roofline": {"kernel": "mqa_logits_kernel<4,2,relu>", "bound": "hbm", "achieved": gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes_per_launch": bytes_,
+                     "launch_us": launch_ms * 1e3,
+                     "mfma": {"achieved_TFLOPs": tfs, "peak_TFLOPs": FP4_MFMA_PEAK_TFLOPS,
+                              "frac": tfs / FP4_MFMA_PEAK_TFLOPS,
+                              "algorithmic_flops_per_launch": flops}},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large_prefill",
-                    choices=["large_prefill", "prefill_norm_rotate", "decode"],
+                    choices=["large_prefill", "prefill_norm_rotate", "decode", "decode_scoring"],
                     help="large_prefill is the headline configuration; the other two are timed "
                          "for reference")
     ap.add_argument("--tokens", type=int, default=131072, help="large_prefill only")
@@ -144,6 +214,9 @@ def main():
         return
 
     t_gen = time.perf_counter()
+    if args.workload == "decode_scoring":
+        bench_scorer(args, dev)
+        return
     if args.workload == "large_prefill":
         wl = workloads.large_prefill(T=args.tokens, H=args.heads)
     else:

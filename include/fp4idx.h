@@ -184,6 +184,40 @@ int fp4idx_qk_rope_pack_store(const void* q, const void* k, const void* position
 int fp4idx_dequant_debug(int which, const uint8_t* packed, const uint8_t* scales, int64_t rows,
                          int H, const int64_t* slots, int64_t NB, int BS, float* out, void* stream);
 
+/*
+ * fp4idx_paged_mqa_logits -- the scorer that consumes the producer's bytes
+ * (ROCm/aiter PR 5484, intro: flydsl_pa_mqa_logits_fp4 scores the FP4 keys
+ * "straight out of the paged cache"; "API": the MFMA consumes the per-group
+ * e8m0 scales directly and the scorer applies its own fp32 weights_scale).
+ * Runs on the gfx950 scaled-FP4 matrix cores.
+ *
+ * For sequence b (0 <= b < B) with context length ctx_b and query token
+ * t = b*next_n + j (position ctx_b - next_n + j), and key s < ctx_b stored at
+ * slot block_table[b, s/64]*64 + s%64:
+ *     logits[t, s] = weights_scale * sum_h weights[t,h] * R(q_h . k_s)
+ * where q_h and k_s are the dequantized 128-vectors (E2M1 x 2^(e-127)) and R
+ * is ReLU (apply_relu = 1) or the identity (0).  Keys after the query's
+ * position, and keys whose block-table entry is outside [0, NB), get -inf.
+ * Entries s >= ctx_b are not written.  Products and sums are fp32 (matrix-core
+ * accumulation, then fused multiply-adds): results match an exact evaluation
+ * to within a few fp32 roundings of sum_h |w| sum_d |q_d k_d|.
+ *
+ *   q_out, q_scale_out  as written by fp4idx_q_rope_pack for T = B*next_n
+ *                       tokens (16- and 4-byte aligned).
+ *   weights      fp32 [T, H], 16-byte aligned (the plain weights_out).
+ *   kv_cache, kv_cache_scale, NB   as written by fp4idx_k_rope_pack_store.
+ *   block_table  int32 [B, max_blocks]; only entries s/64 < ctx_b are read.
+ *   context_lens int32 [B]; clamped to [0, min(max_blocks*64, stride)].
+ *   H            16, 32, 48 or 64;  next_n  1..4;  B <= 65535.
+ *   logits       fp32 [T, stride].
+ */
+int fp4idx_paged_mqa_logits(const uint8_t* q_out, const uint8_t* q_scale_out, const float* weights,
+                            float weights_scale, const uint8_t* kv_cache,
+                            const uint8_t* kv_cache_scale, int64_t NB, const int32_t* block_table,
+                            int64_t max_blocks, const int32_t* context_lens, int64_t B,
+                            int next_n, int H, int apply_relu, float* logits, int64_t stride,
+                            void* stream);
+
 /* Message describing the last non-zero return on the calling thread
  * (thread-local; "" if there was none).  Owned by the library. */
 const char* fp4idx_last_error(void);

@@ -58,6 +58,9 @@ def _lib():
             lib.oracle_fwht_rows.restype = None
             lib.oracle_rmsnorm_rows.argtypes = [_p, _p, _f, _i64]
             lib.oracle_rmsnorm_rows.restype = None
+            lib.oracle_paged_mqa_logits.argtypes = [_p, _p, _p, _f, _p, _p, _i64, _p, _i64, _p,
+                                                    _i64, _i, _i, _i, _p, _i64, _p]
+            lib.oracle_paged_mqa_logits.restype = _i
             lib.oracle_hadamard_scale.argtypes = []
             lib.oracle_hadamard_scale.restype = _f
             _LIB = lib
@@ -189,6 +192,35 @@ def dequant_kcache(kv_cache, kv_cache_scale, slots=None):
                                out.ctypes.data)
     assert rc == 0
     return out
+
+
+def paged_mqa_logits(q_out, q_scale_out, weights, kv_cache, kv_cache_scale, block_table,
+                     context_lens, next_n, *, weights_scale=1.0, apply_relu=True, stride=None,
+                     logits=None, with_bound=False):
+    """FP4 paged MQA logits.  q_out u8 [B*next_n,H,64], q_scale_out u8 [B*next_n,1,4,16,J],
+    weights fp32 [B*next_n,H], kv cache u8 [NB,1,4,64,16] / [NB,1,4,64], block_table int32
+    [B,max_blocks], context_lens int32 [B].  Returns logits fp32 [B*next_n, stride] (entries
+    at or past a sequence's context length keep their initial value, NaN by default) and,
+    with with_bound, the per-entry error scale abs_bound (float64, same shape)."""
+    q_out = _c(q_out, np.uint8)
+    T, H, _ = q_out.shape
+    block_table = _c(block_table, np.int32)
+    context_lens = _c(context_lens, np.int32)
+    B, max_blocks = block_table.shape
+    assert T == B * next_n
+    if stride is None:
+        stride = max(1, max_blocks * KV_BLOCK)
+    if logits is None:
+        logits = np.full((T, stride), np.nan, np.float32)
+    bound = np.zeros((T, stride), np.float64) if with_bound else None
+    rc = _lib().oracle_paged_mqa_logits(
+        q_out.ctypes.data, _c(q_scale_out, np.uint8).ctypes.data, _c(weights, np.float32).ctypes.data,
+        weights_scale, _c(kv_cache, np.uint8).ctypes.data, _c(kv_cache_scale, np.uint8).ctypes.data,
+        kv_cache.shape[0], block_table.ctypes.data, max_blocks, context_lens.ctypes.data, B, next_n,
+        H, int(bool(apply_relu)), logits.ctypes.data, stride, _ptr(bound))
+    if rc != 0:
+        raise ValueError(f"oracle_paged_mqa_logits rejected its arguments (rc={rc})")
+    return (logits, bound) if with_bound else logits
 
 
 # ---- step-level entry points (for the pins) ----

@@ -46,6 +46,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ORC_OK 0
@@ -378,3 +379,86 @@ void oracle_rmsnorm_rows(float* x, const uint16_t* gamma, float eps, int64_t n) 
 }
 
 float oracle_hadamard_scale(void) { return hadamard_scale(); }
+
+/* ------------------------------------------------------------------ */
+/* public: FP4 paged MQA logits (the scorer that reads the producer's  */
+/* bytes; [aiter-5484] intro and Verification: flydsl_pa_mqa_logits_fp4 */
+/* scores q_out/q_scale_out against the paged cache, with the plain     */
+/* weights and a separate fp32 scalar weights_scale).                   */
+/* Readings (not stated on the pages): the logit of key s for query     */
+/* token t is weights_scale * sum_h weights[t,h] * ReLU(q_h . k_s)      */
+/* (ReLU optional); query j of a sequence with context length ctx sits  */
+/* at position ctx - next_n + j and sees keys s <= that position, the   */
+/* others get -inf; entries s >= ctx are not written; a block-table     */
+/* entry outside [0, NB) gives -inf for its keys.                       */
+/* Values are dequantized exactly and accumulated in double; abs_bound  */
+/* (optional) receives |weights_scale| * sum_h |w| * sum_d |q_d k_d|,   */
+/* the scale of any rounding error of an fp32 evaluation.               */
+/* ------------------------------------------------------------------ */
+int oracle_paged_mqa_logits(const uint8_t* q_out, const uint8_t* q_scale_out, const float* weights,
+                            float weights_scale, const uint8_t* kv_cache,
+                            const uint8_t* kv_cache_scale, int64_t NB, const int32_t* block_table,
+                            int64_t max_blocks, const int32_t* context_lens, int64_t B, int next_n,
+                            int H, int apply_relu, float* logits, int64_t stride,
+                            double* abs_bound) {
+    if (H <= 0 || H % 16 != 0 || next_n <= 0 || B < 0 || max_blocks < 0 || stride <= 0 || NB < 0)
+        return ORC_EINVAL;
+    const int J = ((H / 16) + 3) / 4 * 4;
+    double kd[HEAD_DIM];
+    /* the dequantized query heads of one token */
+    double* qd = (double*)malloc(sizeof(double) * (size_t)H * HEAD_DIM);
+    if (!qd) return ORC_EINVAL;
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t ctx = context_lens[b];
+        if (ctx < 0) ctx = 0;
+        if (ctx > max_blocks * KV_BLOCK) ctx = max_blocks * KV_BLOCK;
+        if (ctx > stride) ctx = stride;
+        for (int j = 0; j < next_n; ++j) {
+            const int64_t t = b * next_n + j;
+            const int64_t pos = ctx - next_n + j;
+            for (int h = 0; h < H; ++h)
+                for (int d = 0; d < HEAD_DIM; ++d) {
+                    int g = d / GROUP;
+                    uint8_t byte = q_out[(t * H + h) * (HEAD_DIM / 2) + d / 2];
+                    uint8_t nib = (d & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+                    uint8_t e = q_scale_out[t * (int64_t)NGROUPS * 16 * J + (g * 16 + h % 16) * J + h / 16];
+                    qd[h * HEAD_DIM + d] = (double)e2m1_value(nib) * (double)e8m0_value(e);
+                }
+            for (int64_t s = 0; s < ctx; ++s) {
+                float* out = logits + t * stride + s;
+                double* bnd = abs_bound ? abs_bound + t * stride + s : (double*)0;
+                int32_t blk = block_table[b * max_blocks + s / KV_BLOCK];
+                if (s > pos || blk < 0 || blk >= NB) {
+                    *out = -INFINITY;
+                    if (bnd) *bnd = 0.0;
+                    continue;
+                }
+                const int64_t p = s % KV_BLOCK;
+                for (int d = 0; d < HEAD_DIM; ++d) {
+                    int g = d / GROUP;
+                    uint8_t byte = kv_cache[(((int64_t)blk * NGROUPS + g) * KV_BLOCK + p) * 16 + (d % GROUP) / 2];
+                    uint8_t nib = (d & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+                    uint8_t e = kv_cache_scale[((int64_t)blk * NGROUPS + g) * KV_BLOCK + (p % 16) * (KV_BLOCK / 16) + p / 16];
+                    kd[d] = (double)e2m1_value(nib) * (double)e8m0_value(e);
+                }
+                double acc = 0.0, abs_acc = 0.0;
+                for (int h = 0; h < H; ++h) {
+                    double dot = 0.0, abs_dot = 0.0;
+                    for (int d = 0; d < HEAD_DIM; ++d) {
+                        double pr = qd[h * HEAD_DIM + d] * kd[d];
+                        dot += pr;
+                        abs_dot += fabs(pr);
+                    }
+                    double score = (apply_relu && dot < 0.0) ? 0.0 : dot;
+                    double w = (double)weights[t * H + h];
+                    acc += w * score;
+                    abs_acc += fabs(w) * abs_dot;
+                }
+                *out = (float)((double)weights_scale * acc);
+                if (bnd) *bnd = fabs((double)weights_scale) * abs_acc;
+            }
+        }
+    }
+    free(qd);
+    return ORC_OK;
+}

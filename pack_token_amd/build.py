@@ -3,6 +3,7 @@
 Flags:
   -ffp-contract=off     every fp32 step is one rounded operation (no FMA fusion)
   -packed-fp32-ops off  no v_pk_{add,mul,fma}_f32: scalar fp32 VALU only
+  mfma-vgpr-form        matrix-core results in VGPRs (the scorer's epilogue reads them)
 Denormals stay enabled (the HIP default), which the subnormal-group and
 RMSNorm semantics rely on.
 """
@@ -14,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp4idx.so")
-SOURCES = [os.path.join(CSRC, "fp4idx_kernels.hip"), os.path.join(CSRC, "fp4idx_api.cpp")]
+SOURCES = [os.path.join(CSRC, "fp4idx_kernels.hip"), os.path.join(CSRC, "fp4idx_scorer.hip"),
+           os.path.join(CSRC, "fp4idx_api.cpp")]
 ARCH = os.environ.get("FP4IDX_OFFLOAD_ARCH", "gfx950")
 
 
@@ -29,6 +31,7 @@ def hipcc() -> str:
 def flags():
     return ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
             "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

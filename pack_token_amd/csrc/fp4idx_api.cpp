@@ -306,6 +306,64 @@ int fp4idx_dequant_debug(int which, const uint8_t* packed, const uint8_t* scales
     return FP4IDX_OK;
 }
 
+int fp4idx_paged_mqa_logits(const uint8_t* q_out, const uint8_t* q_scale_out, const float* weights,
+                            float weights_scale, const uint8_t* kv_cache,
+                            const uint8_t* kv_cache_scale, int64_t NB, const int32_t* block_table,
+                            int64_t max_blocks, const int32_t* context_lens, int64_t B,
+                            int next_n, int H, int apply_relu, float* logits, int64_t stride,
+                            void* stream) {
+    static const char* fn = "fp4idx_paged_mqa_logits";
+    if (H <= 0 || H % 16 != 0 || H > 64)
+        return fail(FP4IDX_EUNSUPPORTED,
+                    "%s: n_heads H must be 16, 32, 48 or 64 (got %d)", fn, H);
+    if (next_n < 1 || next_n > 4)
+        return fail(FP4IDX_EUNSUPPORTED, "%s: next_n must be 1..4 (got %d)", fn, next_n);
+    if (!is_flag(apply_relu))
+        return fail(FP4IDX_EINVAL, "%s: apply_relu must be 0 or 1 (got %d)", fn, apply_relu);
+    if (!std::isfinite(weights_scale))
+        return fail(FP4IDX_EINVAL, "%s: weights_scale must be finite", fn);
+    if (B < 0 || B > 65535)
+        return fail(FP4IDX_EINVAL, "%s: B must be in [0, 65535] (got %lld)", fn, (long long)B);
+    if (NB < 0 || NB > INT32_MAX)
+        return fail(FP4IDX_EINVAL, "%s: NB out of range (%lld)", fn, (long long)NB);
+    if (max_blocks < 0 || max_blocks > (int64_t)1 << 24)
+        return fail(FP4IDX_EINVAL, "%s: max_blocks out of range (%lld)", fn, (long long)max_blocks);
+    if (stride <= 0 || stride > ((int64_t)1 << 40) / (B * next_n + 1))
+        return fail(FP4IDX_EINVAL, "%s: stride out of range (%lld)", fn, (long long)stride);
+    if (B == 0 || max_blocks == 0) return FP4IDX_OK;
+    FP4IDX_TRY(check_ptr(fn, "q_out", q_out, 16));
+    FP4IDX_TRY(check_ptr(fn, "q_scale_out", q_scale_out, 4));
+    FP4IDX_TRY(check_ptr(fn, "weights", weights, 16));
+    FP4IDX_TRY(check_ptr(fn, "block_table", block_table, 4));
+    FP4IDX_TRY(check_ptr(fn, "context_lens", context_lens, 4));
+    FP4IDX_TRY(check_ptr(fn, "logits", logits, 4));
+    if (NB > 0) {
+        FP4IDX_TRY(check_ptr(fn, "kv_cache", kv_cache, 16));
+        FP4IDX_TRY(check_ptr(fn, "kv_cache_scale", kv_cache_scale, 4));
+    }
+    fp4idx::LArgs a{};
+    a.q_out = q_out;
+    a.q_scale_out = q_scale_out;
+    a.weights = weights;
+    a.kv_cache = kv_cache;
+    a.kv_cache_scale = kv_cache_scale;
+    a.block_table = block_table;
+    a.context_lens = context_lens;
+    a.logits = logits;
+    a.nblocks = NB;
+    a.max_blocks = max_blocks;
+    a.B = B;
+    a.stride = stride;
+    a.weights_scale = weights_scale;
+    a.next_n = next_n;
+    a.H = H;
+    a.J = ((H / 16) + 3) / 4 * 4;
+    a.apply_relu = apply_relu;
+    hipError_t err = fp4idx::launch_paged_mqa_logits(a, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(fn, err);
+    return FP4IDX_OK;
+}
+
 const char* fp4idx_last_error(void) { return g_last_error.c_str(); }
 
 }  // extern "C"

@@ -55,11 +55,33 @@ struct DArgs {
     int J;
 };
 
+// FP4 paged MQA logits (scorer).
+struct LArgs {
+    const uint8_t* q_out;         // u8 [B*next_n, H, 64]
+    const uint8_t* q_scale_out;   // u8 [B*next_n, 1, 4, 16, J]
+    const float* weights;         // fp32 [B*next_n, H]
+    const uint8_t* kv_cache;      // u8 [NB, 1, 4, 64, 16]
+    const uint8_t* kv_cache_scale;  // u8 [NB, 1, 4, 64]
+    const int32_t* block_table;   // int32 [B, max_blocks]
+    const int32_t* context_lens;  // int32 [B]
+    float* logits;                // fp32 [B*next_n, stride]
+    int64_t nblocks;              // NB
+    int64_t max_blocks;
+    int64_t B;
+    int64_t stride;
+    float weights_scale;
+    int next_n;
+    int H;
+    int J;
+    int apply_relu;
+};
+
 hipError_t launch_q_rope_pack(const QArgs& a, bool is_neox, bool hadamard, hipStream_t stream);
 hipError_t launch_k_rope_pack_store(const KArgs& a, bool is_neox, bool hadamard,
                                     hipStream_t stream);
 hipError_t launch_qk_rope_pack_store(const QArgs& qa, const KArgs& ka, bool is_neox, bool hadamard,
                                      hipStream_t stream);
 hipError_t launch_dequant(const DArgs& a, hipStream_t stream);
+hipError_t launch_paged_mqa_logits(const LArgs& a, hipStream_t stream);
 
 }  // namespace fp4idx

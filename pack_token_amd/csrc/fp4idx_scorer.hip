@@ -1,0 +1,235 @@
+// fp4idx_scorer.hip -- FP4 paged MQA logits on gfx950 scaled-FP4 MFMA.
+//
+// The consumer of the producer's bytes (ROCm/aiter PR 5484, intro and
+// "Verification": flydsl_pa_mqa_logits_fp4 scores q_out/q_scale_out straight
+// out of the paged cache; "API": the MFMA consumes the per-group e8m0 scales
+// directly, and the scorer applies its own fp32 weights_scale).  For query
+// token t of sequence b (t = b*next_n + j, position ctx_b - next_n + j) and
+// key s of that sequence:
+//     logits[t, s] = weights_scale * sum_h weights[t, h] * ReLU(q_h . k_s)
+// with -inf where s is past the query's position or its block-table entry is
+// outside the cache; entries s >= ctx_b are left untouched.
+//
+// Mapping onto v_mfma_scale_f32_16x16x128_f8f6f4 (E2M1 x E2M1, K = 128 in one
+// instruction, one e8m0 scale per 32 K-values per row/column):
+//   A = 16 query heads x 128 dims: lane L holds head (L % 16), dims
+//       32 (L / 16) .. +32 = 16 bytes of q_out; its scale byte is byte
+//       (head tile % 4) of the q_scale_out dword [t, 0, L / 16, L % 16, :],
+//       which is why that tensor's last axis is round_up(H/16, 4).
+//   B = 16 keys x 128 dims: lane L holds key 16 kt + (L % 16) of a 64-slot
+//       block, group L / 16 = kv_cache[blk, 0, L/16, 16 kt + L%16, :]; its scale
+//       is byte kt of the dword kv_cache_scale[blk, 0, L/16, 4 (L%16) .. +4],
+//       the interleaved (pos%16)*4 + pos/16 order of ROCm/aiter PR 4029.
+//   C = 16 heads x 16 keys: lane L holds heads 4 (L/16) + i, key L % 16.
+// Each lane folds its 4 heads (weighted ReLU) for each of the block's four
+// key tiles, then a transpose-reduce over the four 16-lane row groups leaves
+// lane L with the total of key 64 blk + L, stored as one coalesced row.
+// The library is built with the VGPR form of MFMA so results are read by the
+// epilogue without accumulator-register copies.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp4idx_internal.h"
+
+namespace fp4idx {
+namespace {
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kBlocksPerWave = 4;  // 64-slot cache blocks per wavefront
+
+__device__ __forceinline__ u32x4_t load16_stream(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// E2M1 operands occupy the low 4 dwords of the 8-dword operand; the upper 4
+// are not read, so they are left undefined (no register moves to clear them).
+__device__ __forceinline__ i32x8_t as_operand(u32x4_t v) {
+    const i32x4_t w = __builtin_bit_cast(i32x4_t, v);
+    return __builtin_shufflevector(w, w, 0, 1, 2, 3, -1, -1, -1, -1);
+}
+
+// C = A x B with scale bytes selected by the immediates SA_SEL / SB_SEL.
+template <int SA_SEL, int SB_SEL>
+__device__ __forceinline__ f32x4_t mma(i32x8_t a, i32x8_t b, int sa, int sb) {
+    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 4, 4, SA_SEL, sa, SB_SEL,
+                                                            sb);
+}
+
+// ReLU on the bit pattern: every negative float (and -0) is a negative
+// integer.  One integer max instead of a float max that the compiler would
+// precede with a NaN-quieting canonicalize of each matrix-core result.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// acc += sum_i w_i * ReLU(c_i) for the lane's 4 heads
+__device__ __forceinline__ float fold4(f32x4_t c, float4 w, float acc) {
+    acc = __builtin_fmaf(w.x, relu(c[0]), acc);
+    acc = __builtin_fmaf(w.y, relu(c[1]), acc);
+    acc = __builtin_fmaf(w.z, relu(c[2]), acc);
+    acc = __builtin_fmaf(w.w, relu(c[3]), acc);
+    return acc;
+}
+
+__device__ __forceinline__ float fold4_linear(f32x4_t c, float4 w, float acc) {
+    acc = __builtin_fmaf(w.x, c[0], acc);
+    acc = __builtin_fmaf(w.y, c[1], acc);
+    acc = __builtin_fmaf(w.z, c[2], acc);
+    acc = __builtin_fmaf(w.w, c[3], acc);
+    return acc;
+}
+
+// Static loop over the head tiles and key tiles of one query token.
+template <int HT, int I, bool RELU>
+struct HeadLoop {
+    __device__ __forceinline__ static void run(const i32x8_t* A, const int* SA, const float4* W,
+                                               const i32x8_t* Bk, int sb, float* acc) {
+        const i32x8_t a = A[I];
+        const int sa = SA[I / 4];
+        const float4 w = W[I];
+        const f32x4_t c0 = mma<I % 4, 0>(a, Bk[0], sa, sb);
+        const f32x4_t c1 = mma<I % 4, 1>(a, Bk[1], sa, sb);
+        const f32x4_t c2 = mma<I % 4, 2>(a, Bk[2], sa, sb);
+        const f32x4_t c3 = mma<I % 4, 3>(a, Bk[3], sa, sb);
+        if (RELU) {
+            acc[0] = fold4(c0, w, acc[0]);
+            acc[1] = fold4(c1, w, acc[1]);
+            acc[2] = fold4(c2, w, acc[2]);
+            acc[3] = fold4(c3, w, acc[3]);
+        } else {
+            acc[0] = fold4_linear(c0, w, acc[0]);
+            acc[1] = fold4_linear(c1, w, acc[1]);
+            acc[2] = fold4_linear(c2, w, acc[2]);
+            acc[3] = fold4_linear(c3, w, acc[3]);
+        }
+        HeadLoop<HT, I + 1, RELU>::run(A, SA, W, Bk, sb, acc);
+    }
+};
+template <int HT, bool RELU>
+struct HeadLoop<HT, HT, RELU> {
+    __device__ __forceinline__ static void run(const i32x8_t*, const int*, const float4*,
+                                               const i32x8_t*, int, float*) {}
+};
+
+// acc[kt] (this lane's partial sums of key 16 kt + L%16) -> the total of key
+// tile L/16 summed over the four 16-lane row groups, with the gfx950 lane
+// swaps: permlane32_swap(a, b) returns ([a.lo, b.lo], [a.hi, b.hi]) and
+// permlane16_swap(a, b) returns ([a.r0, b.r0, a.r2, b.r2], [a.r1, b.r1, a.r3,
+// b.r3]) in 32-lane halves / 16-lane rows, so the sum of the two outputs is,
+// per lane, exactly the partner total it needs (no selects, no LDS).
+__device__ __forceinline__ float transpose_reduce(const float acc[4]) {
+    const auto p02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[0]),
+                                                      __float_as_uint(acc[2]), false, false);
+    const auto p13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[1]),
+                                                      __float_as_uint(acc[3]), false, false);
+    const float n0 = __uint_as_float(p02[0]) + __uint_as_float(p02[1]);
+    const float n1 = __uint_as_float(p13[0]) + __uint_as_float(p13[1]);
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(n0), __float_as_uint(n1),
+                                                    false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+template <int NQ, int HT, bool RELU>
+__global__ __launch_bounds__(64 * kWaves) void mqa_logits_kernel(LArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t b = blockIdx.y;
+    int64_t ctx = a.context_lens[b];
+    ctx = ctx < 0 ? 0 : ctx;
+    ctx = ctx > a.max_blocks * 64 ? a.max_blocks * 64 : ctx;
+    ctx = ctx > a.stride ? a.stride : ctx;
+    const int64_t nblk = (ctx + 63) >> 6;
+    const int64_t kb0 = ((int64_t)blockIdx.x * kWaves + wave) * kBlocksPerWave;
+    if (kb0 >= nblk) return;
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    const int H = HT * 16;
+    const int J = a.J;
+
+    // query operands of the sequence's next_n tokens, kept in registers
+    i32x8_t A[NQ][HT];
+    int SA[NQ][(HT + 3) / 4];
+    float4 W[NQ][HT];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        const int64_t t = b * NQ + j;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            A[j][ht] = as_operand(*reinterpret_cast<const u32x4_t*>(
+                a.q_out + ((t * H + 16 * ht + n) * 64 + 16 * g)));
+            W[j][ht] = *reinterpret_cast<const float4*>(a.weights + t * H + 16 * ht + 4 * g);
+        }
+#pragma unroll
+        for (int d = 0; d < (HT + 3) / 4; ++d)
+            SA[j][d] = *reinterpret_cast<const int*>(a.q_scale_out + t * 64 * (int64_t)J +
+                                                     (g * 16 + n) * J + 4 * d);
+    }
+
+    const int64_t kb_end = kb0 + kBlocksPerWave < nblk ? kb0 + kBlocksPerWave : nblk;
+    for (int64_t kb = kb0; kb < kb_end; ++kb) {
+        const int32_t blk = a.block_table[b * a.max_blocks + kb];
+        const bool valid = blk >= 0 && (int64_t)blk < a.nblocks;
+        i32x8_t Bk[4];
+        int sb = 0;
+        if (valid) {
+            const uint8_t* base = a.kv_cache + (((int64_t)blk * 4 + g) * 64 + n) * 16;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) Bk[kt] = as_operand(load16_stream(base + kt * 16 * 16));
+            sb = *reinterpret_cast<const int*>(a.kv_cache_scale + ((int64_t)blk * 4 + g) * 64 + 4 * n);
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) Bk[kt] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+        const int64_t s = kb * 64 + lane;
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            HeadLoop<HT, 0, RELU>::run(A[j], SA[j], W[j], Bk, sb, acc);
+            const float v = transpose_reduce(acc);
+            const int64_t t = b * NQ + j;
+            const int64_t pos = ctx - NQ + j;
+            const float out = (!valid || s > pos) ? -__builtin_huge_valf() : a.weights_scale * v;
+            if (s < ctx) __builtin_nontemporal_store(out, a.logits + t * a.stride + s);
+        }
+    }
+}
+
+template <int NQ, int HT>
+hipError_t launch_nq_ht(const LArgs& a, hipStream_t stream) {
+    const int64_t per_wg = (int64_t)kWaves * kBlocksPerWave;
+    dim3 grid((unsigned)((a.max_blocks + per_wg - 1) / per_wg), (unsigned)a.B);
+    LArgs copy = a;
+    void* args[] = {&copy};
+    const void* fn = a.apply_relu ? reinterpret_cast<const void*>(mqa_logits_kernel<NQ, HT, true>)
+                                  : reinterpret_cast<const void*>(mqa_logits_kernel<NQ, HT, false>);
+    return hipLaunchKernel(fn, grid, dim3(64 * kWaves), args, 0, stream);
+}
+
+template <int NQ>
+hipError_t launch_nq(const LArgs& a, hipStream_t stream) {
+    switch (a.H / 16) {
+        case 1: return launch_nq_ht<NQ, 1>(a, stream);
+        case 2: return launch_nq_ht<NQ, 2>(a, stream);
+        case 3: return launch_nq_ht<NQ, 3>(a, stream);
+        default: return launch_nq_ht<NQ, 4>(a, stream);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_paged_mqa_logits(const LArgs& a, hipStream_t stream) {
+    if (a.B == 0 || a.max_blocks == 0) return hipSuccess;
+    switch (a.next_n) {
+        case 1: return launch_nq<1>(a, stream);
+        case 2: return launch_nq<2>(a, stream);
+        case 3: return launch_nq<3>(a, stream);
+        default: return launch_nq<4>(a, stream);
+    }
+}
+
+}  // namespace fp4idx

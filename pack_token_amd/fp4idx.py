@@ -58,6 +58,9 @@ def lib():
                                                     _i64, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p,
                                                     _p, _p, _p, _i64, _i, _p]
             L.fp4idx_qk_rope_pack_store.restype = _i
+            L.fp4idx_paged_mqa_logits.argtypes = [_p, _p, _p, _f, _p, _p, _i64, _p, _i64, _p,
+                                                  _i64, _i, _i, _i, _p, _i64, _p]
+            L.fp4idx_paged_mqa_logits.restype = _i
             L.fp4idx_dequant_debug.argtypes = [_i, _p, _p, _i64, _i, _p, _i64, _i, _p, _p]
             L.fp4idx_dequant_debug.restype = _i
             L.fp4idx_last_error.argtypes = []
@@ -194,6 +197,37 @@ def qk_rope_pack_store(q, k, positions, cos_sin, slot_mapping, kv_cache, kv_cach
         kv_cache.shape[0], KV_BLOCK, _stream_handle(stream))
     _check(rc)
     return q_out, q_scale_out, weights_out
+
+
+def paged_mqa_logits(q_out, q_scale_out, weights, kv_cache, kv_cache_scale, block_table,
+                     context_lens, next_n, *, weights_scale=1.0, apply_relu=True, logits=None,
+                     stride=None, stream=None):
+    """fp4idx_paged_mqa_logits.  Returns logits fp32 [B*next_n, stride]; entries at or past
+    a sequence's context length keep their previous contents (uninitialised if allocated
+    here)."""
+    T, H, _ = q_out.shape
+    dev = q_out.device
+    B, max_blocks = block_table.shape
+    if T != B * next_n:
+        raise ValueError(f"q_out has {T} tokens, expected B*next_n = {B * next_n}")
+    _require(q_out, "q_out", (torch.uint8,))
+    _require(q_scale_out, "q_scale_out", (torch.uint8,), dev)
+    _require(weights, "weights", (torch.float32,), dev)
+    _require(kv_cache, "kv_cache", (torch.uint8,), dev)
+    _require(kv_cache_scale, "kv_cache_scale", (torch.uint8,), dev)
+    _require(block_table, "block_table", (torch.int32,), dev)
+    _require(context_lens, "context_lens", (torch.int32,), dev)
+    if stride is None:
+        stride = logits.shape[1] if logits is not None else max(1, max_blocks * KV_BLOCK)
+    if logits is None:
+        logits = torch.empty((T, stride), dtype=torch.float32, device=dev)
+    _require(logits, "logits", (torch.float32,), dev)
+    _check(lib().fp4idx_paged_mqa_logits(
+        _ptr(q_out), _ptr(q_scale_out), _ptr(weights), weights_scale, _ptr(kv_cache),
+        _ptr(kv_cache_scale), kv_cache.shape[0], _ptr(block_table), max_blocks,
+        _ptr(context_lens), B, next_n, H, int(bool(apply_relu)), _ptr(logits), stride,
+        _stream_handle(stream)))
+    return logits
 
 
 def dequant_q(q_out, q_scale_out, *, out=None, stream=None):

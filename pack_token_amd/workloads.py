@@ -275,3 +275,62 @@ RECIPES = {
     "prefill_norm_rotate": prefill_norm_rotate,
     "large_prefill": large_prefill,
 }
+
+
+@dataclass
+class ScorerCase:
+    """Inputs of the paged MQA-logits scorer: FP4 query rows with their q-scale rows,
+    head weights, a paged FP4 key cache, block tables and context lengths."""
+    name: str
+    B: int
+    next_n: int
+    H: int
+    q_out: np.ndarray           # u8 [B*next_n, H, 64]
+    q_scale_out: np.ndarray     # u8 [B*next_n, 1, 4, 16, J]
+    weights: np.ndarray         # fp32 [B*next_n, H]
+    kv_cache: np.ndarray        # u8 [NB, 1, 4, 64, 16]
+    kv_cache_scale: np.ndarray  # u8 [NB, 1, 4, 64]
+    block_table: np.ndarray     # int32 [B, max_blocks]
+    context_lens: np.ndarray    # int32 [B]
+
+    @property
+    def NB(self) -> int:
+        return int(self.kv_cache.shape[0])
+
+    @property
+    def max_blocks(self) -> int:
+        return int(self.block_table.shape[1])
+
+
+def scorer_case(seed: int, B: int, next_n: int, H: int, ctx_lo: int, ctx_hi: int,
+                max_context: Optional[int] = None, exp_lo: int = 118, exp_hi: int = 130,
+                signed_weights: bool = False, spare_blocks: int = 0) -> ScorerCase:
+    """Random FP4 bytes: uniform nibbles, e8m0 exponents U[exp_lo, exp_hi]; context
+    lengths U[ctx_lo, ctx_hi]; every sequence owns distinct cache blocks, assigned in
+    a random order; unused block-table entries are -1."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    T = B * next_n
+    J = q_scale_cols(H)
+    ctx = rng.integers(ctx_lo, ctx_hi + 1, B).astype(np.int32)
+    if max_context is None:
+        max_context = int(ctx.max()) if B else 1
+    max_blocks = max(1, -(-max_context // KV_BLOCK))
+    need = [-(-int(c) // KV_BLOCK) for c in ctx]
+    NB = sum(need) + spare_blocks
+    perm = rng.permutation(NB).astype(np.int32)
+    table = np.full((B, max_blocks), -1, np.int32)
+    at = 0
+    for b, nb in enumerate(need):
+        table[b, :nb] = perm[at:at + nb]
+        at += nb
+    q_out = rng.integers(0, 256, (T, H, 64), dtype=np.uint8)
+    qs = np.zeros((T, 1, 4, 16, J), np.uint8)
+    qs[..., : H // 16] = rng.integers(exp_lo, exp_hi + 1, (T, 1, 4, 16, H // 16), dtype=np.uint8)
+    if signed_weights:
+        weights = rng.uniform(-1.0, 1.0, (T, H)).astype(np.float32)
+    else:
+        weights = rng.random((T, H), dtype=np.float32)
+    kv = rng.integers(0, 256, (NB, 1, 4, KV_BLOCK, 16), dtype=np.uint8)
+    ks = rng.integers(exp_lo, exp_hi + 1, (NB, 1, 4, KV_BLOCK), dtype=np.uint8)
+    return ScorerCase(f"scorer_B{B}_n{next_n}_H{H}", B, next_n, H, q_out, qs, weights, kv, ks,
+                      table, ctx)

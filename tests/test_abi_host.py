@@ -26,7 +26,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert names == ["fp4idx_dequant_debug", "fp4idx_k_rope_pack_store", "fp4idx_last_error",
-                     "fp4idx_q_rope_pack", "fp4idx_qk_rope_pack_store"]
+                     "fp4idx_paged_mqa_logits", "fp4idx_q_rope_pack", "fp4idx_qk_rope_pack_store"]
     lib = ctypes.CDLL(fp4idx.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -168,6 +168,39 @@ def test_qk_rejections(over, code, msg):
     assert fp4idx.last_error().startswith("fp4idx_qk_rope_pack_store:")
 
 
+def s_call(**over):
+    a = dict(q_out=ALIGNED, q_scale_out=ALIGNED, weights=ALIGNED, weights_scale=1.0,
+             kv_cache=ALIGNED, kv_cache_scale=ALIGNED, NB=4, block_table=ALIGNED, max_blocks=8,
+             context_lens=ALIGNED, B=2, next_n=4, H=32, apply_relu=1, logits=ALIGNED,
+             stride=512, stream=None)
+    a.update(over)
+    return fp4idx.lib().fp4idx_paged_mqa_logits(*a.values())
+
+
+S_REJECT = [
+    (dict(H=128), fp4idx.EUNSUPPORTED, "n_heads"),
+    (dict(H=24), fp4idx.EUNSUPPORTED, "n_heads"),
+    (dict(next_n=5), fp4idx.EUNSUPPORTED, "next_n"),
+    (dict(next_n=0), fp4idx.EUNSUPPORTED, "next_n"),
+    (dict(apply_relu=2), fp4idx.EINVAL, "apply_relu"),
+    (dict(weights_scale=float("inf")), fp4idx.EINVAL, "weights_scale"),
+    (dict(B=70000), fp4idx.EINVAL, "B must be"),
+    (dict(NB=-1), fp4idx.EINVAL, "NB"),
+    (dict(stride=0), fp4idx.EINVAL, "stride"),
+    (dict(weights=ALIGNED + 4), fp4idx.EINVAL, "weights must be 16-byte"),
+    (dict(q_out=None), fp4idx.EINVAL, "q_out must not be NULL"),
+    (dict(block_table=ALIGNED + 2), fp4idx.EINVAL, "block_table must be 4-byte"),
+    (dict(kv_cache=ALIGNED + 4), fp4idx.EINVAL, "kv_cache must be 16-byte"),
+    (dict(logits=None), fp4idx.EINVAL, "logits must not be NULL"),
+]
+
+
+@pytest.mark.parametrize("over,code,msg", S_REJECT)
+def test_scorer_rejections(over, code, msg):
+    assert s_call(**over) == code
+    assert msg in fp4idx.last_error(), fp4idx.last_error()
+
+
 def test_zero_tokens_is_a_noop_even_with_null_buffers():
     assert q_call(T=0, q=None, positions=None, cos_sin=None, q_out=None, q_scale_out=None) == 0
     assert k_call(T=0, k=None, positions=None, cos_sin=None, slot_mapping=None, kv_cache=None,
@@ -175,6 +208,7 @@ def test_zero_tokens_is_a_noop_even_with_null_buffers():
     assert d_call(rows=0, packed=None, scales=None, out=None) == 0
     assert qk_call(T=0, q=None, k=None, positions=None, cos_sin=None, slot_mapping=None,
                    q_out=None, q_scale_out=None, kv_cache=None, kv_cache_scale=None) == 0
+    assert s_call(B=0, q_out=None, logits=None, block_table=None) == 0
     # but shapes are still checked first
     assert q_call(T=0, D=64) == fp4idx.EUNSUPPORTED
 

@@ -1,0 +1,137 @@
+"""GPU parity of the FP4 paged MQA-logits scorer (scaled-FP4 MFMA) against
+the oracle.  The scorer accumulates in fp32 on the matrix cores, so parity is
+a tolerance: every finite logit within (K + H + 8) * 2^-24 of the oracle's
+error scale |weights_scale| * sum_h |w| * sum_d |q_d k_d| (a forward error
+bound of fp32 summation over the 128 products and the H heads), cosine >=
+0.9999 over all finite logits, and -inf / untouched entries identical."""
+import numpy as np
+import pytest
+
+import oracle
+from pack_token_amd import workloads
+from harness import say
+
+pytestmark = pytest.mark.gpu
+
+SENT = np.float32(-12345.0)
+
+
+def run_gpu_scorer(sc, weights_scale=1.0, relu=True, stride=None):
+    import torch
+
+    from pack_token_amd import fp4idx
+
+    dev = "cuda:0"
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    stride = stride or sc.max_blocks * 64
+    logits = torch.full((sc.B * sc.next_n, stride), float(SENT), dtype=torch.float32, device=dev)
+    fp4idx.paged_mqa_logits(t(sc.q_out), t(sc.q_scale_out), t(sc.weights), t(sc.kv_cache),
+                            t(sc.kv_cache_scale), t(sc.block_table), t(sc.context_lens),
+                            sc.next_n, weights_scale=weights_scale, apply_relu=relu, logits=logits)
+    torch.cuda.synchronize()
+    return logits.cpu().numpy()
+
+
+def check_scorer(got, ref, bound, H):
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref))
+    assert np.array_equal(got == SENT, np.isnan(ref))            # untouched past the context
+    g, r = got[fin].astype(np.float64), ref[fin].astype(np.float64)
+    tol = (128 + H + 8) * 2.0 ** -24 * bound[fin] + 1e-37
+    bad = np.abs(g - r) > tol
+    assert not bad.any(), (int(bad.sum()), float(np.max(np.abs(g - r) / np.maximum(tol, 1e-300))))
+    if g.size:
+        cos = float(g @ r / (np.linalg.norm(g) * np.linalg.norm(r) + 1e-300))
+        assert cos >= 0.9999, cos
+    return fin
+
+
+@pytest.mark.parametrize("next_n", [1, 2, 3, 4])
+@pytest.mark.parametrize("H", [16, 32, 48, 64])
+@pytest.mark.parametrize("relu", [True, False])
+def test_scorer_random_bytes(next_n, H, relu):
+    sc = workloads.scorer_case(100 * next_n + H, 5, next_n, H, 1, 700, signed_weights=not relu)
+    say(f"case scorer next_n={next_n} H={H} relu={relu} ctx={list(sc.context_lens)}")
+    got = run_gpu_scorer(sc, 0.5, relu)
+    ref, bound = oracle.paged_mqa_logits(sc.q_out, sc.q_scale_out, sc.weights, sc.kv_cache,
+                                         sc.kv_cache_scale, sc.block_table, sc.context_lens,
+                                         next_n, weights_scale=0.5, apply_relu=relu,
+                                         with_bound=True)
+    check_scorer(got, ref, bound, H)
+
+
+def test_scorer_edge_cases():
+    """Contexts shorter than next_n, exactly one block, ragged tails, longer than
+    the table (clamped), invalid block entries, and a stride wider than the table."""
+    sc = workloads.scorer_case(7, 6, 4, 32, 1, 200, spare_blocks=3)
+    sc.context_lens[:] = [0, 2, 64, 65, 191, 10_000]   # last one is clamped to max_blocks*64
+    sc.block_table[4, 1] = -7
+    sc.block_table[3, 1] = sc.NB
+    stride = sc.max_blocks * 64 + 37
+    got = run_gpu_scorer(sc, 1.0, True, stride)
+    ref, bound = oracle.paged_mqa_logits(sc.q_out, sc.q_scale_out, sc.weights, sc.kv_cache,
+                                         sc.kv_cache_scale, sc.block_table, sc.context_lens, 4,
+                                         stride=stride, with_bound=True)
+    check_scorer(got, ref, bound, 32)
+
+
+@pytest.mark.parametrize("next_n", [1, 4])
+def test_producer_to_scorer_end_to_end(next_n):
+    """The producer's own bytes fed to the scorer at H=32, D=128, kv_block=64 with
+    next_n 1 and 4 (the shapes of ROCm/aiter PR 5484 "Verification", which reports
+    cosine 1.000000 and top-64 overlap 1.00 against its reference): GPU producer +
+    GPU scorer against oracle producer + oracle scorer."""
+    import torch
+
+    from pack_token_amd import fp4idx
+    from harness import gpu_run, oracle_run, assert_all_same
+
+    B, H = 16, 32
+    ctx = np.random.default_rng(3).integers(300, 1500, B).astype(np.int32)
+    n_keys = int(ctx.sum())
+    rng = np.random.Generator(np.random.PCG64(77 + next_n))
+    # one producer call writes the keys of all sequences (contiguous slots) and the
+    # queries of the last next_n positions of every sequence
+    T = B * next_n
+    wl = workloads.sweep_case(55 + next_n, T, H, True, 64)
+    keys = workloads.sweep_case(66 + next_n, n_keys, 16, True, 64)
+    starts = np.concatenate([[0], np.cumsum(ctx)[:-1]])
+    NB = -(-n_keys // 64) + B
+    # each sequence starts on a fresh block
+    blk_starts = np.concatenate([[0], np.cumsum(-(-ctx // 64))[:-1]])
+    slots = np.concatenate([blk_starts[b] * 64 + np.arange(ctx[b]) for b in range(B)])
+    keys.slot_mapping = slots.astype(np.int64)
+    keys.positions = np.concatenate([np.arange(c) for c in ctx]).astype(np.int64)
+    keys.cos_sin = workloads.cos_sin_table(int(ctx.max()))
+    keys.NB = NB
+    wl.positions = np.concatenate([np.arange(c - next_n, c) for c in ctx]).astype(np.int64)
+    wl.cos_sin = keys.cos_sin
+    wl.NB = NB
+    max_blocks = int(-(-ctx.max() // 64))
+    table = np.full((B, max_blocks), -1, np.int32)
+    for b in range(B):
+        nb = -(-int(ctx[b]) // 64)
+        table[b, :nb] = blk_starts[b] + np.arange(nb)
+    say(f"case e2e next_n={next_n}: {B} sequences, {n_keys} keys")
+    gq = gpu_run(wl)                         # queries (the cache part is ignored)
+    gk = gpu_run(keys)                       # keys into the cache
+    rq = oracle_run(wl)
+    rk = oracle_run(keys)
+    assert_all_same(gq[:3] + (None, None), rq[:3] + (None, None))
+    assert_all_same((None, None, None) + gk[3:], (None, None, None) + rk[3:])
+    sc = workloads.ScorerCase("e2e", B, next_n, H, gq[0], gq[1], wl.weights, gk[3], gk[4], table, ctx)
+    got = run_gpu_scorer(sc)
+    ref, bound = oracle.paged_mqa_logits(rq[0], rq[1], wl.weights, rk[3], rk[4], table, ctx,
+                                         next_n, with_bound=True)
+    fin = check_scorer(got, ref, bound, H)
+    # top-64 overlap per query row
+    overlaps = []
+    for t in range(T):
+        f = np.isfinite(ref[t])
+        if f.sum() < 64:
+            continue
+        a = set(np.argsort(-np.where(f, got[t], -np.inf))[:64])
+        b = set(np.argsort(-np.where(f, ref[t], -np.inf))[:64])
+        overlaps.append(len(a & b) / 64)
+    say(f"top-64 overlap mean {np.mean(overlaps):.4f} min {np.min(overlaps):.4f}")
+    assert np.mean(overlaps) >= 0.99
