@@ -72,10 +72,10 @@ __device__ __forceinline__ uint4 load16(const void* p) {
 }
 
 // Streaming (non-temporal) accesses for data touched exactly once: q, k and
-// the code bytes.  They set the nt cache-policy bit so the lines do not
+// the query code bytes.  They set the nt cache-policy bit so the lines do not
 // displace anything in L2; on MI355X this raises the query kernel from
-// ~5.4 to ~6.5 TB/s.  The small per-token rows (weights, scales) keep the
-// default policy, which measured faster for them.
+// ~5.4 to ~6.5 TB/s.  The small per-token rows (weights, scales) and the key
+// cache writes keep the default policy, which measured faster for them.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint4 load16_stream(const void* p) {
@@ -439,7 +439,9 @@ __device__ __forceinline__ void k_row(const KArgs& a, uint4 v, int64_t slot, int
     const int p = (int)(slot & 63);
     const int g = c >> 2;
     const int64_t row = blk * 4 + g;
-    store4_stream(a.kv_cache + (row * 64 + p) * 16 + 4 * (c & 3), q.codes);
+    // default cache policy: a block's 64 B pieces of a 64-slot row are written by
+    // several workgroups, and L2 merges them before the line goes to HBM
+    *reinterpret_cast<uint32_t*>(a.kv_cache + (row * 64 + p) * 16 + 4 * (c & 3)) = q.codes;
     if ((c & 3) == 0) a.kv_cache_scale[row * 64 + (p & 15) * 4 + (p >> 4)] = (uint8_t)q.e;
 }
 
@@ -496,11 +498,12 @@ __global__ __launch_bounds__(kBlock) void k_row_kernel(KArgs a) {
 }
 
 // Both sides of a token in one launch (ROCm/aiter PR 5484: one kernel writes
-// all five outputs).  One wavefront per token: the query heads as above, then
-// the key row on lanes 0..15.  The key's loads are issued first; position and
-// RoPE coefficients are shared.  The RoPE coefficients of lane L (< 16) for
-// the key are those of slice chunk chunk_of(L) & 7 = chunk_of(L & 7), the
-// same ones the split query layout gives lane L.
+// all five outputs).  One wavefront per token for the query heads as above;
+// wavefront 0 of each block also does the key rows of the block's 4 tokens,
+// one per 16-lane row (rather than every wavefront doing its own key on a
+// quarter of its lanes).  The key loads are issued before the query work.
+// The RoPE coefficients of lane L for a key row are those of slice chunk
+// chunk_of(L & 15) & 7 = chunk_of(L & 7).
 template <bool NEOX, bool HAD, bool NORM>
 __global__ __launch_bounds__(kBlock) void qk_kernel(QArgs qa, KArgs ka) {
     extern __shared__ uint32_t smem[];
@@ -509,9 +512,19 @@ __global__ __launch_bounds__(kBlock) void qk_kernel(QArgs qa, KArgs ka) {
     const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
     if (t >= qa.T) return;
     uint32_t* sc = smem + wave * 16 * qa.J;
+    // key row of token tk on the 16-lane row lane / 16 of wavefront 0; rows past
+    // T and rows whose slot is outside the cache leave as a whole row
+    const int64_t tk = (int64_t)blockIdx.x * kWavesPerBlock + (lane >> 4);
+    const bool krow = wave == 0 && tk < ka.T;
     uint4 kv = make_uint4(0u, 0u, 0u, 0u);
-    if (lane < 16) kv = load16_stream(ka.k + t * 128 + 8 * chunk_of(lane));
-    const int64_t slot = ka.slot_mapping[t];
+    int64_t kslot = -1;
+    float KC[8], KS[8];
+    if (krow) {
+        kv = load16_stream(ka.k + tk * 128 + 8 * chunk_of(lane & 15));
+        kslot = ka.slot_mapping[tk];
+        const int64_t kpos = clamped_position(ka.positions, ka.pos64, tk, ka.max_pos);
+        rope_coeffs<NEOX>(ka.cos_sin + kpos * 64, chunk_of(lane & 7), KC, KS);
+    }
     q_token_prologue(qa, t, lane, sc);
     const int64_t pos = clamped_position(qa.positions, qa.pos64, t, qa.max_pos);
     float C[8], S[8];
@@ -519,7 +532,8 @@ __global__ __launch_bounds__(kBlock) void qk_kernel(QArgs qa, KArgs ka) {
     if (HAD) q_row_token<NEOX>(qa, t, lane, reinterpret_cast<uint8_t*>(sc), C, S);
     else q_split_token<NEOX>(qa, t, lane, reinterpret_cast<uint8_t*>(sc), C, S);
     q_token_epilogue(qa, t, lane, sc);
-    if (lane < 16 && slot >= 0 && slot < ka.nslots) k_row<NEOX, NORM, HAD>(ka, kv, slot, lane, C, S);
+    if (krow && kslot >= 0 && kslot < ka.nslots)
+        k_row<NEOX, NORM, HAD>(ka, kv, kslot, lane & 15, KC, KS);
 }
 
 // ---- dequantization (debug reader) -------------------------------------------
