@@ -82,10 +82,24 @@ def cpu_baseline(wl, n_tokens: int, threads: int):
                              is_neox=wl.is_neox, rope_offset=wl.rope_offset,
                              apply_hadamard=wl.apply_hadamard, threads=threads)
     dt = time.perf_counter() - t0
+    # single-threaded on a smaller slice of the same workload
+    n1 = min(n_tokens, 8192)
+    kv, ks = wl.empty_cache()
+    t1 = time.perf_counter()
+    oracle.q_rope_pack(wl.q[:n1], wl.positions[:n1], wl.cos_sin, wl.weights[:n1],
+                       is_neox=wl.is_neox, rope_offset=wl.rope_offset,
+                       apply_hadamard=wl.apply_hadamard, threads=1)
+    oracle.k_rope_pack_store(wl.k[:n1], wl.positions[:n1], wl.cos_sin, wl.slot_mapping[:n1], kv,
+                             ks, k_norm_gamma=wl.k_norm_gamma, k_norm_eps=wl.k_norm_eps,
+                             is_neox=wl.is_neox, rope_offset=wl.rope_offset,
+                             apply_hadamard=wl.apply_hadamard, threads=1)
+    dt1 = time.perf_counter() - t1
     del np
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n_tokens} of {wl.T} tokens of the same workload (query + key "
-                      f"path), {threads} threads, {dt:.2f} s wall"}
+                      f"path), {threads} threads, {dt:.2f} s wall",
+            "single_thread_value": n1 / dt1,
+            "single_thread_sample": f"first {n1} tokens, 1 thread, {dt1:.2f} s wall"}
 
 
 FP4_MFMA_PEAK_TFLOPS = 10100.0

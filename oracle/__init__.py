@@ -33,9 +33,12 @@ def _lib():
     global _LIB
     with _LOCK:
         if _LIB is None:
-            if not os.path.exists(_build.LIB):
+            # FP4IDX_ORACLE_LIB: an alternative build of this oracle (used by the
+            # mutation check, which loads deliberately broken copies)
+            path = os.environ.get("FP4IDX_ORACLE_LIB") or _build.LIB
+            if path == _build.LIB and not os.path.exists(path):
                 _build.build()
-            lib = ctypes.CDLL(_build.LIB)
+            lib = ctypes.CDLL(path)
             lib.oracle_q_rope_pack.argtypes = [_p, _p, _i, _p, _i64, _p, _i64, _i, _i, _i, _i, _i,
                                                _i, _i, _f, _p, _p, _p]
             lib.oracle_q_rope_pack.restype = _i

@@ -14,14 +14,14 @@ CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-s
           "-Wall", "-Wextra"]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = ["gcc", *CFLAGS, "-o", tmp, SRC, "-lm"]
+def build(verbose: bool = False, src: str = SRC, out: str = LIB, extra=()) -> str:
+    tmp = out + ".tmp"
+    cmd = ["gcc", *CFLAGS, *extra, "-o", tmp, src, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

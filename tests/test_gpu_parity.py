@@ -321,3 +321,13 @@ def test_graph_replay_matches_oracle():
         got = (q_out.cpu().numpy(), qs.cpu().numpy(), w_out.cpu().numpy(), kv.cpu().numpy(),
                ks.cpu().numpy())
         assert_all_same(got, oracle_run(wl))
+
+
+@FUSED
+@pytest.mark.parametrize("T", [1, 5, 64, 300])
+@pytest.mark.parametrize("pos32", [False, True])
+def test_sglang_row_matrix(T, pos32, fused):
+    """Rows {1, 5, 64, 300} x scales {1, 40, 1e-3} plus zero, subnormal and
+    half-way groups x int32/int64 positions, the matrix of sgl-project/sglang
+    PR 39656 "Verification" (compress ratios are a different producer)."""
+    check(workloads.edge_mix(seed=200 + T, T=T, positions_int32=pos32), fused=fused)

@@ -1,0 +1,95 @@
+"""The pins catch plausible mistakes: each case plants one mistake in a copy
+of the oracle source (on the CPU, in a temporary directory), builds it, and
+requires the pin suite to fail against that copy.  The committed oracle is
+never modified."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+from oracle import build as obuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PINS = ["tests/test_oracle_quant.py", "tests/test_oracle_transforms.py",
+        "tests/test_oracle_layout.py", "tests/test_oracle_scorer.py"]
+
+MUTATIONS = {
+    "tie_at_0.75_goes_down": ("else if (m < 0.75f) code = 1;", "else if (m <= 0.75f) code = 1;"),
+    "tie_at_5_goes_down": ("else if (m <= 5.0f) code = 6;", "else if (m < 5.0f) code = 6;"),
+    "zero_code_drops_sign": ("return (uint8_t)((sign << 3) | code);",
+                             "return (uint8_t)(((code ? sign : 0) << 3) | code);"),
+    "floor_exponent_rule": ("int e = (int)(b >> 23) + ((b & 0x7FFFFFu) != 0u ? 1 : 0);",
+                            "int e = (int)(b >> 23);"),
+    "neox_interleaved_swapped": ("int ia = is_neox ? i : 2 * i;", "int ia = is_neox ? 2 * i : i;"),
+    "rope_sign": ("S[ia] = round_bf16(ac - bs);", "S[ia] = round_bf16(ac + bs);"),
+    "cos_sin_swapped": ("float c = cs_row[i], s = cs_row[ROPE_DIM / 2 + i];",
+                        "float s = cs_row[i], c = cs_row[ROPE_DIM / 2 + i];"),
+    "no_bf16_after_rope": ("S[ib] = round_bf16(bc + as);", "S[ib] = (bc + as);"),
+    "linear_key_scales": ("kv_cache_scale[((blk * 1 + 0) * NGROUPS + g) * BS + (p % 16) * (BS / 16) + p / 16] = e[g];",
+                          "kv_cache_scale[((blk * 1 + 0) * NGROUPS + g) * BS + p] = e[g];"),
+    "nibbles_swapped": ("bytes[g * (GROUP / 2) + b] = (uint8_t)(lo | (hi << 4));",
+                        "bytes[g * (GROUP / 2) + b] = (uint8_t)(hi | (lo << 4));"),
+    "q_scales_transposed": ("qs[(g * 16 + h % 16) * J + h / 16] = e[g];",
+                            "qs[(g * 16 + h / 16) * J + h % 16] = e[g];"),
+    "fwht_sign": ("x[j + h] = u - w;", "x[j + h] = w - u;"),
+    "rmsnorm_without_eps": ("float den = sqrtf(mean + eps);", "float den = sqrtf(mean);"),
+    "rmsnorm_mean_over_64": ("float mean = p[0] / (float)HEAD_DIM;", "float mean = p[0] / 64.0f;"),
+    "bf16_truncates": ("u += 0x7FFFu + lsb;", "u += 0u * lsb;"),
+    "bf16_ties_away": ("u += 0x7FFFu + lsb;", "u += 0x8000u + 0u * lsb;"),
+    "wrong_rope_slice": ("rope_slice(x + rope_offset, cs_row, is_neox);",
+                         "rope_slice(x + 64 - rope_offset, cs_row, is_neox);"),
+    "q_scale_pads_unwritten": ("memset(qs, 0, (size_t)NGROUPS * 16 * J);", ";"),
+    "signed_amax": ("float a = fabsf(v[i]);", "float a = v[i];"),
+    "amax_over_4": ("float q = amax / 6.0f;", "float q = amax / 4.0f;"),
+    "position_clamp_to_0": ("if (p >= max_pos) p = max_pos - 1;", "if (p >= max_pos) p = 0;"),
+    "slot_0_skipped": ("if (slot < 0 || slot >= nslots) continue;",
+                       "if (slot <= 0 || slot >= nslots) continue;"),
+    "hadamard_scale_1_over_8": ("return (float)(1.0 / sqrt((double)HEAD_DIM));",
+                                "return (float)(1.0 / sqrt((double)64));"),
+    "weights_head_0_skipped": ("for (int h = 0; h < H; ++h) weights_out[t * H + h] = weights[t * H + h];",
+                               "for (int h = 1; h < H; ++h) weights_out[t * H + h] = weights[t * H + h];"),
+    "no_saturation": ("else code = 7;", "else code = 6;"),
+    "scorer_without_relu": ("double score = (apply_relu && dot < 0.0) ? 0.0 : dot;",
+                            "double score = dot;"),
+    "scorer_mask_off_by_one": ("if (s > pos || blk < 0 || blk >= NB) {",
+                               "if (s >= pos || blk < 0 || blk >= NB) {"),
+    "scorer_ignores_weights": ("acc += w * score;", "acc += score;"),
+}
+
+
+def _run_mutant(name, workdir):
+    old, new = MUTATIONS[name]
+    src = open(obuild.SRC).read()
+    if src.count(old) != 1:
+        return f"mutation site not unique or missing: {name}"
+    d = os.path.join(workdir, name)
+    os.makedirs(d, exist_ok=True)
+    mutant = os.path.join(d, "fp4idx_oracle_mutant.c")
+    with open(mutant, "w") as f:
+        f.write(src.replace(old, new))
+    lib = obuild.build(src=mutant, out=os.path.join(d, "libmutant.so"))
+    env = dict(os.environ, FP4IDX_ORACLE_LIB=lib, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        "-m", "not gpu", *PINS], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=900)
+    return r.returncode
+
+
+@pytest.fixture(scope="module")
+def mutant_results(tmp_path_factory):
+    from concurrent.futures import ThreadPoolExecutor
+
+    workdir = str(tmp_path_factory.mktemp("mutants"))
+    workers = max(1, min(6, (os.cpu_count() or 2) - 1))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        futs = {n: ex.submit(_run_mutant, n, workdir) for n in sorted(MUTATIONS)}
+        return {n: f.result() for n, f in futs.items()}
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, mutant_results):
+    rc = mutant_results[name]
+    assert not isinstance(rc, str), rc
+    assert rc != 0, f"no pin caught the planted mistake {name}"
