@@ -64,6 +64,14 @@ def _lib():
             lib.oracle_paged_mqa_logits.argtypes = [_p, _p, _p, _f, _p, _p, _i64, _p, _i64, _p,
                                                     _i64, _i, _i, _i, _p, _i64, _p]
             lib.oracle_paged_mqa_logits.restype = _i
+            lib.oracle_q_rope_pack_sglang.argtypes = [_p, _p, _i, _p, _i64, _i64, _i, _i, _i, _i,
+                                                      _i, _i, _f, _f, _p]
+            lib.oracle_q_rope_pack_sglang.restype = _i
+            lib.oracle_k_rope_pack_store_sglang.argtypes = [_p, _p, _i, _p, _i64, _p, _p, _f, _i64,
+                                                            _i, _i, _i, _i, _i, _f, _f, _p, _i64]
+            lib.oracle_k_rope_pack_store_sglang.restype = _i
+            lib.oracle_quantize_rows_two_stage.argtypes = [_p, _i64, _f, _f, _p]
+            lib.oracle_quantize_rows_two_stage.restype = None
             lib.oracle_hadamard_scale.argtypes = []
             lib.oracle_hadamard_scale.restype = _f
             _LIB = lib
@@ -224,6 +232,61 @@ def paged_mqa_logits(q_out, q_scale_out, weights, kv_cache, kv_cache_scale, bloc
     if rc != 0:
         raise ValueError(f"oracle_paged_mqa_logits rejected its arguments (rc={rc})")
     return (logits, bound) if with_bound else logits
+
+
+SLOT68 = 68
+
+
+def q_rope_pack_sglang(q_bits, positions, cos_sin, *, is_neox=True, rope_offset=64,
+                       fake_quant_floor=DEFAULT_SCALE_FLOOR, pack_floor=DEFAULT_SCALE_FLOOR):
+    """sglang-compatible query side: records u8 [T,H,68] (64 code bytes, 4 exponents)."""
+    q_bits = _c(q_bits, np.uint16)
+    T, H, D = q_bits.shape
+    positions = np.ascontiguousarray(positions)
+    pos64 = 1 if positions.dtype == np.int64 else 0
+    if not pos64:
+        positions = _c(positions, np.int32)
+    cos_sin = _c(cos_sin, np.float32)
+    out = np.full((T, H, SLOT68), 0xA5, np.uint8)
+    rc = _lib().oracle_q_rope_pack_sglang(q_bits.ctypes.data, positions.ctypes.data, pos64,
+                                          cos_sin.ctypes.data, cos_sin.shape[0], T, H, D, ROPE_DIM,
+                                          rope_offset, 32, int(bool(is_neox)), fake_quant_floor,
+                                          pack_floor, out.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_q_rope_pack_sglang rejected its arguments (rc={rc})")
+    return out
+
+
+def k_rope_pack_store_sglang(k_bits, positions, cos_sin, slot_mapping, index_k_cache, *,
+                             k_norm_gamma=None, k_norm_eps=1e-6, is_neox=True, rope_offset=64,
+                             fake_quant_floor=DEFAULT_SCALE_FLOOR, pack_floor=DEFAULT_SCALE_FLOOR):
+    """sglang-compatible key side: writes 68-byte records into index_k_cache u8 [num_slots,68]."""
+    k_bits = _c(k_bits, np.uint16)
+    T, D = k_bits.shape
+    positions = np.ascontiguousarray(positions)
+    pos64 = 1 if positions.dtype == np.int64 else 0
+    if not pos64:
+        positions = _c(positions, np.int32)
+    cos_sin = _c(cos_sin, np.float32)
+    slot_mapping = _c(slot_mapping, np.int64)
+    assert index_k_cache.dtype == np.uint8 and index_k_cache.flags.c_contiguous
+    gamma = None if k_norm_gamma is None else _c(k_norm_gamma, np.uint16)
+    rc = _lib().oracle_k_rope_pack_store_sglang(
+        k_bits.ctypes.data, positions.ctypes.data, pos64, cos_sin.ctypes.data, cos_sin.shape[0],
+        slot_mapping.ctypes.data, _ptr(gamma), k_norm_eps, T, D, ROPE_DIM, rope_offset, 32,
+        int(bool(is_neox)), fake_quant_floor, pack_floor, index_k_cache.ctypes.data,
+        index_k_cache.shape[0])
+    if rc != 0:
+        raise ValueError(f"oracle_k_rope_pack_store_sglang rejected its arguments (rc={rc})")
+    return index_k_cache
+
+
+def quantize_rows_two_stage(x, floor1=DEFAULT_SCALE_FLOOR, floor2=DEFAULT_SCALE_FLOOR):
+    x = _c(x, np.float32)
+    n = x.shape[0]
+    out = np.empty((n, SLOT68), np.uint8)
+    _lib().oracle_quantize_rows_two_stage(x.ctypes.data, n, floor1, floor2, out.ctypes.data)
+    return out
 
 
 # ---- step-level entry points (for the pins) ----

@@ -462,3 +462,84 @@ int oracle_paged_mqa_logits(const uint8_t* q_out, const uint8_t* q_scale_out, co
     free(qd);
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* sglang-compatible mode ([sglang-39656] Summary and review).          */
+/* Two quantization stages with their own floors: stage 1 fake-quantizes */
+/* each 32-group to the UE8M0 E2M1 grid (values, not codes); stage 2     */
+/* ("the indexer packer") recomputes the exponent from the fake-quant    */
+/* values with its own floor and packs codes whose sign bit is set only  */
+/* when the magnitude code is nonzero (sign = (x < 0) & (idx != 0)).     */
+/* Record: 64 code bytes then the 4 stage-2 exponents = 68 bytes.        */
+/* ------------------------------------------------------------------ */
+#define SLOT68 68
+
+static void quantize_row_two_stage(const float* x, float floor1, float floor2, uint8_t* record) {
+    for (int g = 0; g < NGROUPS; ++g) {
+        const float* v = x + g * GROUP;
+        int e1 = group_exponent(v, GROUP, floor1);
+        float y[GROUP];
+        for (int i = 0; i < GROUP; ++i) y[i] = e2m1_value(e2m1_nibble(v[i], e1)) * e8m0_value((uint8_t)e1);
+        int e2 = group_exponent(y, GROUP, floor2);
+        for (int b = 0; b < GROUP / 2; ++b) {
+            uint8_t n[2];
+            for (int q = 0; q < 2; ++q) {
+                float yv = y[2 * b + q];
+                uint8_t code = (uint8_t)(e2m1_nibble(yv, e2) & 7);
+                uint8_t sign = (yv < 0.0f && code != 0) ? 1 : 0;
+                n[q] = (uint8_t)((sign << 3) | code);
+            }
+            record[g * 16 + b] = (uint8_t)(n[0] | (n[1] << 4));
+        }
+        record[64 + g] = (uint8_t)e2;
+    }
+}
+
+/* query side: record [t, h, 0:68] = two-stage codes of head h, then its 4 exponents */
+int oracle_q_rope_pack_sglang(const uint16_t* q, const void* positions, int positions_int64,
+                              const float* cos_sin, int64_t max_pos, int64_t T, int H, int D,
+                              int R, int rope_offset, int group_size, int is_neox,
+                              float fake_quant_floor, float pack_floor, uint8_t* q_packed) {
+    if (check_shape(D, R, rope_offset, group_size) != ORC_OK) return ORC_EINVAL;
+    if (H <= 0 || H % 16 != 0 || T < 0 || max_pos <= 0) return ORC_EINVAL;
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t pos = read_position(positions, positions_int64, t, max_pos);
+        const float* cs_row = cos_sin + pos * ROPE_DIM;
+        for (int h = 0; h < H; ++h) {
+            float x[HEAD_DIM];
+            for (int i = 0; i < HEAD_DIM; ++i) x[i] = bf16_to_f32(q[(t * H + h) * HEAD_DIM + i]);
+            rope_slice(x + rope_offset, cs_row, is_neox);
+            quantize_row_two_stage(x, fake_quant_floor, pack_floor, q_packed + (t * H + h) * SLOT68);
+        }
+    }
+    return ORC_OK;
+}
+
+/* key side: optional RMSNorm, RoPE, two stages, 68-byte record at slot; slot 0
+   (and any slot outside [1, num_slots)) publishes nothing */
+int oracle_k_rope_pack_store_sglang(const uint16_t* k, const void* positions, int positions_int64,
+                                    const float* cos_sin, int64_t max_pos,
+                                    const int64_t* slot_mapping, const uint16_t* k_norm_gamma,
+                                    float k_norm_eps, int64_t T, int D, int R, int rope_offset,
+                                    int group_size, int is_neox, float fake_quant_floor,
+                                    float pack_floor, uint8_t* index_k_cache, int64_t num_slots) {
+    if (check_shape(D, R, rope_offset, group_size) != ORC_OK) return ORC_EINVAL;
+    if (num_slots < 0 || T < 0 || max_pos <= 0) return ORC_EINVAL;
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t slot = slot_mapping[t];
+        if (slot <= 0 || slot >= num_slots) continue;
+        int64_t pos = read_position(positions, positions_int64, t, max_pos);
+        float x[HEAD_DIM];
+        for (int i = 0; i < HEAD_DIM; ++i) x[i] = bf16_to_f32(k[t * HEAD_DIM + i]);
+        if (k_norm_gamma) rmsnorm128(x, k_norm_gamma, k_norm_eps);
+        rope_slice(x + rope_offset, cos_sin + pos * ROPE_DIM, is_neox);
+        quantize_row_two_stage(x, fake_quant_floor, pack_floor, index_k_cache + slot * SLOT68);
+    }
+    return ORC_OK;
+}
+
+/* step-level: two-stage records of n rows of 128 (for the pins) */
+void oracle_quantize_rows_two_stage(const float* x, int64_t n, float floor1, float floor2,
+                                    uint8_t* records) {
+    for (int64_t r = 0; r < n; ++r) quantize_row_two_stage(x + r * HEAD_DIM, floor1, floor2, records + r * SLOT68);
+}

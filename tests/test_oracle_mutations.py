@@ -12,7 +12,8 @@ from oracle import build as obuild
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PINS = ["tests/test_oracle_quant.py", "tests/test_oracle_transforms.py",
-        "tests/test_oracle_layout.py", "tests/test_oracle_scorer.py"]
+        "tests/test_oracle_layout.py", "tests/test_oracle_scorer.py",
+        "tests/test_oracle_sglang.py"]
 
 MUTATIONS = {
     "tie_at_0.75_goes_down": ("else if (m < 0.75f) code = 1;", "else if (m <= 0.75f) code = 1;"),
@@ -37,8 +38,8 @@ MUTATIONS = {
     "rmsnorm_mean_over_64": ("float mean = p[0] / (float)HEAD_DIM;", "float mean = p[0] / 64.0f;"),
     "bf16_truncates": ("u += 0x7FFFu + lsb;", "u += 0u * lsb;"),
     "bf16_ties_away": ("u += 0x7FFFu + lsb;", "u += 0x8000u + 0u * lsb;"),
-    "wrong_rope_slice": ("rope_slice(x + rope_offset, cs_row, is_neox);",
-                         "rope_slice(x + 64 - rope_offset, cs_row, is_neox);"),
+    "wrong_rope_slice": ("rope_slice(x + rope_offset, cs_row, is_neox);\n    if (apply_hadamard)",
+                         "rope_slice(x + 64 - rope_offset, cs_row, is_neox);\n    if (apply_hadamard)"),
     "q_scale_pads_unwritten": ("memset(qs, 0, (size_t)NGROUPS * 16 * J);", ";"),
     "signed_amax": ("float a = fabsf(v[i]);", "float a = v[i];"),
     "amax_over_4": ("float q = amax / 6.0f;", "float q = amax / 4.0f;"),
@@ -55,6 +56,22 @@ MUTATIONS = {
     "scorer_mask_off_by_one": ("if (s > pos || blk < 0 || blk >= NB) {",
                                "if (s >= pos || blk < 0 || blk >= NB) {"),
     "scorer_ignores_weights": ("acc += w * score;", "acc += score;"),
+    "two_stage_sign_on_zero": ("uint8_t sign = (yv < 0.0f && code != 0) ? 1 : 0;",
+                               "uint8_t sign = signbit(yv) ? 1 : 0;"),
+    "two_stage_reuses_stage_1_exponent": ("int e2 = group_exponent(y, GROUP, floor2);",
+                                          "int e2 = e1 + 0 * group_exponent(y, GROUP, floor2);"),
+    "two_stage_skips_fake_quant": ("y[i] = e2m1_value(e2m1_nibble(v[i], e1)) * e8m0_value((uint8_t)e1);",
+                                   "y[i] = v[i] + 0.0f * e1;"),
+    "two_stage_floors_swapped": ("int e1 = group_exponent(v, GROUP, floor1);",
+                                 "int e1 = group_exponent(v, GROUP, floor2);"),
+    "two_stage_exponents_reversed": ("record[64 + g] = (uint8_t)e2;", "record[64 + 3 - g] = (uint8_t)e2;"),
+    "sglang_slot_0_published": ("if (slot <= 0 || slot >= num_slots) continue;",
+                                "if (slot < 0 || slot >= num_slots) continue;"),
+    "sglang_key_without_norm": ("if (k_norm_gamma) rmsnorm128(x, k_norm_gamma, k_norm_eps);\n        rope_slice(",
+                                "if (0) rmsnorm128(x, k_norm_gamma, k_norm_eps);\n        rope_slice("),
+    "sglang_query_wrong_rope_slice": ("rope_slice(x + rope_offset, cs_row, is_neox);\n            quantize_row_two_stage",
+                                      "rope_slice(x + 64 - rope_offset, cs_row, is_neox);\n            quantize_row_two_stage"),
+    "sglang_query_heads_shifted": ("q_packed + (t * H + h) * SLOT68", "q_packed + (t * H + (h ^ 1)) * SLOT68"),
 }
 
 
