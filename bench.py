@@ -105,6 +105,98 @@ def cpu_baseline(wl, n_tokens: int, threads: int):
 FP4_MFMA_PEAK_TFLOPS = 10100.0
 
 
+def sglang_q_bytes_per_token(H: int) -> int:
+    return 256 * H + 8 + 256 + 68 * H
+
+
+def sglang_k_bytes_per_token() -> int:
+    return 256 + 8 + 68
+
+
+def bench_sglang(args, dev):
+    """sglang-compatible mode over the large-prefill input (T = 131072, H = 64,
+    neox, dims 64..127 rotated): one step = fp4idx_q_rope_pack_sglang +
+    fp4idx_k_rope_pack_store_sglang (two launches), keys to slots 1..T.
+    Algorithmic bytes per token: query launch 256H + 8 + 256 + 68H, key launch
+    256 + 8 + 68 (its position and cos/sin reads repeat the query launch's)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from pack_token_amd import fp4idx, workloads
+
+    wl = workloads.large_prefill(T=args.tokens, H=args.heads)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    q, k = up(wl.q.view(np.int16)), up(wl.k.view(np.int16))
+    pos, cs = up(wl.positions), up(wl.cos_sin)
+    slots_np = wl.slot_mapping + 1
+    slots = up(slots_np)
+    T, H = wl.T, wl.H
+    q_packed = torch.empty((T, H, 68), dtype=torch.uint8, device=dev)
+    cache = torch.zeros((T + 1, 68), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def q_call():
+        fp4idx.q_rope_pack_sglang(q, pos, cs, q_packed=q_packed, stream=stream)
+
+    def k_call():
+        fp4idx.k_rope_pack_store_sglang(k, pos, cs, slots, cache, stream=stream)
+
+    for _ in range(args.warmup):
+        q_call()
+        k_call()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        q_call()
+        ev[i][1].record(stream)
+        k_call()
+        ev[i][2].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / K
+    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    k_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    qb = sglang_q_bytes_per_token(H) * T
+    kb = sglang_k_bytes_per_token() * T
+    q_gbs = qb / (q_ms * 1e-3) / 1e9
+    rec = {
+        "metric": "tokens/s and achieved HBM GB/s, sglang-compatible q+k RoPE/FP4 68-byte records",
+        "value": T / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16->e2m1 (two stages)",
+        "data": "synthetic",
+        "config": {"workload": "sglang_prefill", "tokens": T, "heads": H, "head_dim": 128,
+                   "rope_dim": 64, "rope": "neox", "rope_offset": 64, "record_bytes": 68,
+                   "slots": "1..T (slot 0 unpublished)",
+                   "step": "fp4idx_q_rope_pack_sglang + fp4idx_k_rope_pack_store_sglang"},
+        "step_GBps": (qb + kb) / (ms_per_step * 1e-3) / 1e9,
+        "q_kernel_us": q_ms * 1e3, "k_kernel_us": k_ms * 1e3,
+        "k_kernel_GBps": kb / (k_ms * 1e-3) / 1e9,
+        "roofline": {"kernel": "q_sglang_kernel<neox>", "bound": "hbm", "achieved": q_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": q_gbs / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes_per_launch": qb,
+                     "launch_us": q_ms * 1e3},
+    }
+    if not args.no_cpu_baseline:
+        n = min(args.cpu_sample_tokens, T, 16384)
+        c0 = time.perf_counter()
+        oracle.q_rope_pack_sglang(wl.q[:n], wl.positions[:n], wl.cos_sin)
+        ref = np.zeros((n + 1, 68), np.uint8)
+        oracle.k_rope_pack_store_sglang(wl.k[:n], wl.positions[:n], wl.cos_sin,
+                                        np.arange(1, n + 1, dtype=np.int64), ref)
+        dt = time.perf_counter() - c0
+        rec["cpu_baseline"] = {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"first {n} of {T} tokens (query + key records), "
+                                         f"1 thread, {dt:.2f} s wall"}
+    print(json.dumps(rec), flush=True)
+
+
 def bench_scorer(args, dev):
     """fp4idx_paged_mqa_logits over a decode batch: 64 sequences x next_n 4 query
     tokens, H = 32, contexts U[4096, 131072] keys, every sequence on its own cache
@@ -178,11 +270,12 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large_prefill",
-                    choices=["large_prefill", "prefill_norm_rotate", "decode", "decode_scoring"],
+                    choices=["large_prefill", "prefill_norm_rotate", "decode", "decode_scoring",
+                             "sglang_prefill"],
                     help="large_prefill is the headline configuration; the other two are timed "
                          "for reference")
-    ap.add_argument("--tokens", type=int, default=131072, help="large_prefill only")
-    ap.add_argument("--heads", type=int, default=64, help="large_prefill only")
+    ap.add_argument("--tokens", type=int, default=131072, help="large_prefill and sglang_prefill")
+    ap.add_argument("--heads", type=int, default=64, help="large_prefill and sglang_prefill")
     ap.add_argument("--cpu-sample-tokens", type=int, default=131072)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
@@ -230,6 +323,9 @@ def main():
     t_gen = time.perf_counter()
     if args.workload == "decode_scoring":
         bench_scorer(args, dev)
+        return
+    if args.workload == "sglang_prefill":
+        bench_sglang(args, dev)
         return
     if args.workload == "large_prefill":
         wl = workloads.large_prefill(T=args.tokens, H=args.heads)

@@ -167,6 +167,51 @@ int fp4idx_qk_rope_pack_store(const void* q, const void* k, const void* position
                               uint8_t* kv_cache_scale, int64_t NB, int BS, void* stream);
 
 /*
+ * fp4idx_q_rope_pack_sglang / fp4idx_k_rope_pack_store_sglang -- the
+ * sglang-compatible mode (sgl-project/sglang PR 39656 "Summary": RoPE and
+ * FP4 packing into the 68-byte index-K format, 64 E2M1 bytes plus four block
+ * exponents; review: the packer's sign rule and separate stage floors).
+ * Per 128-row, after the optional key RMSNorm and the RoPE (as for the calls
+ * above; there is no Hadamard in this mode), each 32-group is quantized twice:
+ *   stage 1 (fake quant): e1 from fake_quant_floor by the block-exponent
+ *     rule above, y_i = E2M1(v_i * 2^(127-e1)) * 2^(e1-127) in fp32 (a y of
+ *     magnitude >= 2^128 is +-inf);
+ *   stage 2 (packer): e2 from the y's with pack_floor by the same rule, codes
+ *     of y_i * 2^(127-e2) rounded to nearest even, and the sign bit set only
+ *     when the magnitude code is nonzero (no -0 codes).
+ * Record (68 bytes): byte g*16+b holds the codes of elements 32g+2b (low
+ * nibble) and 32g+2b+1 (high nibble); bytes 64..67 hold e2 of groups 0..3.
+ * Both floors: finite and >= 0.  No weights are passed through.
+ *
+ * fp4idx_q_rope_pack_sglang
+ *   q, positions, positions_int64, cos_sin, max_pos, T, H, D, R, rope_offset,
+ *   group_size, is_neox: as for fp4idx_q_rope_pack.
+ *   q_packed     u8 [T, H, 68], 4-byte aligned: record of head h of token t.
+ *
+ * fp4idx_k_rope_pack_store_sglang
+ *   k, positions, positions_int64, cos_sin, max_pos, slot_mapping,
+ *   k_norm_gamma, k_norm_eps, T, D, R, rope_offset, group_size, is_neox: as
+ *   for fp4idx_k_rope_pack_store.
+ *   index_k_cache u8 [num_slots, 68], 4-byte aligned: token t's record goes
+ *                to row slot_mapping[t] when 1 <= slot < num_slots; slot 0
+ *                (and any slot outside that range) publishes nothing.
+ *   num_slots    >= 0.  Rows that no token maps to are left untouched.
+ */
+int fp4idx_q_rope_pack_sglang(const void* q, const void* positions, int positions_int64,
+                              const float* cos_sin, int64_t max_pos, int64_t T, int H, int D,
+                              int R, int rope_offset, int group_size, int is_neox,
+                              float fake_quant_floor, float pack_floor, uint8_t* q_packed,
+                              void* stream);
+
+int fp4idx_k_rope_pack_store_sglang(const void* k, const void* positions, int positions_int64,
+                                    const float* cos_sin, int64_t max_pos,
+                                    const int64_t* slot_mapping, const void* k_norm_gamma,
+                                    float k_norm_eps, int64_t T, int D, int R, int rope_offset,
+                                    int group_size, int is_neox, float fake_quant_floor,
+                                    float pack_floor, uint8_t* index_k_cache, int64_t num_slots,
+                                    void* stream);
+
+/*
  * fp4idx_dequant_debug -- reader side, for tests and debugging: expands
  * codes back to fp32, value = E2M1(nibble) * 2^(e-127) with E2M1 magnitudes
  * {0, .5, 1, 1.5, 2, 3, 4, 6} and bit 3 the sign; e = 0 gives 2^-127 and

@@ -86,6 +86,12 @@ int check_common(const char* fn, int D, int R, int group_size, int rope_offset, 
     return FP4IDX_OK;
 }
 
+int check_floor(const char* fn, const char* name, float v) {
+    if (!std::isfinite(v) || v < 0.0f)
+        return fail(FP4IDX_EINVAL, "%s: %s must be finite and >= 0 (got %g)", fn, name, (double)v);
+    return FP4IDX_OK;
+}
+
 int check_ptr(const char* fn, const char* name, const void* p, uintptr_t align) {
     if (p == nullptr) return fail(FP4IDX_EINVAL, "%s: %s must not be NULL", fn, name);
     if (!aligned(p, align))
@@ -257,6 +263,92 @@ int fp4idx_qk_rope_pack_store(const void* q, const void* k, const void* position
     if (T == 0) return FP4IDX_OK;
     hipError_t err = fp4idx::launch_qk_rope_pack_store(qa, ka, is_neox != 0, apply_hadamard != 0,
                                                        static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(fn, err);
+    return FP4IDX_OK;
+}
+
+int fp4idx_q_rope_pack_sglang(const void* q, const void* positions, int positions_int64,
+                              const float* cos_sin, int64_t max_pos, int64_t T, int H, int D,
+                              int R, int rope_offset, int group_size, int is_neox,
+                              float fake_quant_floor, float pack_floor, uint8_t* q_packed,
+                              void* stream) {
+    static const char* fn = "fp4idx_q_rope_pack_sglang";
+    FP4IDX_TRY(check_floor(fn, "fake_quant_floor", fake_quant_floor));
+    FP4IDX_TRY(check_floor(fn, "pack_floor", pack_floor));
+    FP4IDX_TRY(check_common(fn, D, R, group_size, rope_offset, positions_int64, is_neox, 0,
+                            fake_quant_floor, T, max_pos));
+    if (H <= 0 || H % 16 != 0 || H > kMaxHeads)
+        return fail(FP4IDX_EUNSUPPORTED,
+                    "%s: n_heads H must be a positive multiple of 16 and <= %d (got %d)", fn,
+                    kMaxHeads, H);
+    if (T > INT64_MAX / ((int64_t)H * kHeadDim * 2))
+        return fail(FP4IDX_EINVAL, "%s: T too large (%lld)", fn, (long long)T);
+    if (T == 0) return FP4IDX_OK;
+    FP4IDX_TRY(check_ptr(fn, "q", q, 16));
+    FP4IDX_TRY(check_ptr(fn, "positions", positions, positions_int64 ? 8 : 4));
+    FP4IDX_TRY(check_ptr(fn, "cos_sin", cos_sin, 16));
+    FP4IDX_TRY(check_ptr(fn, "q_packed", q_packed, 4));
+    fp4idx::SQArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.positions = positions;
+    a.cos_sin = cos_sin;
+    a.q_packed = q_packed;
+    a.T = T;
+    a.max_pos = max_pos;
+    a.H = H;
+    a.pos64 = positions_int64;
+    a.rope_offset = rope_offset;
+    a.e_lo1 = floor_exponent(fake_quant_floor);
+    a.e_lo2 = floor_exponent(pack_floor);
+    hipError_t err = fp4idx::launch_q_rope_pack_sglang(a, is_neox != 0,
+                                                       static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(fn, err);
+    return FP4IDX_OK;
+}
+
+int fp4idx_k_rope_pack_store_sglang(const void* k, const void* positions, int positions_int64,
+                                    const float* cos_sin, int64_t max_pos,
+                                    const int64_t* slot_mapping, const void* k_norm_gamma,
+                                    float k_norm_eps, int64_t T, int D, int R, int rope_offset,
+                                    int group_size, int is_neox, float fake_quant_floor,
+                                    float pack_floor, uint8_t* index_k_cache, int64_t num_slots,
+                                    void* stream) {
+    static const char* fn = "fp4idx_k_rope_pack_store_sglang";
+    FP4IDX_TRY(check_floor(fn, "fake_quant_floor", fake_quant_floor));
+    FP4IDX_TRY(check_floor(fn, "pack_floor", pack_floor));
+    FP4IDX_TRY(check_common(fn, D, R, group_size, rope_offset, positions_int64, is_neox, 0,
+                            fake_quant_floor, T, max_pos));
+    if (num_slots < 0 || num_slots > INT64_MAX / fp4idx::kSglangRecord)
+        return fail(FP4IDX_EINVAL, "%s: num_slots out of range (%lld)", fn, (long long)num_slots);
+    if (k_norm_gamma != nullptr && (!std::isfinite(k_norm_eps) || k_norm_eps < 0.0f))
+        return fail(FP4IDX_EINVAL, "%s: k_norm_eps must be finite and >= 0 (got %g)", fn,
+                    (double)k_norm_eps);
+    if (T > INT64_MAX / (kHeadDim * 2))
+        return fail(FP4IDX_EINVAL, "%s: T too large (%lld)", fn, (long long)T);
+    if (T == 0) return FP4IDX_OK;
+    FP4IDX_TRY(check_ptr(fn, "k", k, 16));
+    FP4IDX_TRY(check_ptr(fn, "positions", positions, positions_int64 ? 8 : 4));
+    FP4IDX_TRY(check_ptr(fn, "cos_sin", cos_sin, 16));
+    FP4IDX_TRY(check_ptr(fn, "slot_mapping", slot_mapping, 8));
+    if (k_norm_gamma != nullptr) FP4IDX_TRY(check_ptr(fn, "k_norm_gamma", k_norm_gamma, 16));
+    if (num_slots > 0) FP4IDX_TRY(check_ptr(fn, "index_k_cache", index_k_cache, 4));
+    fp4idx::SKArgs a{};
+    a.k = static_cast<const uint16_t*>(k);
+    a.positions = positions;
+    a.cos_sin = cos_sin;
+    a.slot_mapping = slot_mapping;
+    a.gamma = static_cast<const uint16_t*>(k_norm_gamma);
+    a.index_k_cache = index_k_cache;
+    a.T = T;
+    a.max_pos = max_pos;
+    a.nslots = num_slots;
+    a.eps = k_norm_eps;
+    a.pos64 = positions_int64;
+    a.rope_offset = rope_offset;
+    a.e_lo1 = floor_exponent(fake_quant_floor);
+    a.e_lo2 = floor_exponent(pack_floor);
+    hipError_t err = fp4idx::launch_k_rope_pack_store_sglang(a, is_neox != 0,
+                                                             static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return hip_fail(fn, err);
     return FP4IDX_OK;
 }

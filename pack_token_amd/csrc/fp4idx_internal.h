@@ -55,6 +55,40 @@ struct DArgs {
     int J;
 };
 
+// sglang-compatible mode: two quantization stages, 68-byte records.
+constexpr int kSglangRecord = 68;   // 64 code bytes + 4 exponent bytes
+
+struct SQArgs {
+    const uint16_t* q;          // bf16 [T, H, 128]
+    const void* positions;
+    const float* cos_sin;
+    uint8_t* q_packed;          // u8 [T, H, 68]
+    int64_t T;
+    int64_t max_pos;
+    int H;
+    int pos64;
+    int rope_offset;
+    int e_lo1;                  // clamp(E(fake_quant_floor), 1, 254)
+    int e_lo2;                  // clamp(E(pack_floor), 1, 254)
+};
+
+struct SKArgs {
+    const uint16_t* k;          // bf16 [T, 128]
+    const void* positions;
+    const float* cos_sin;
+    const int64_t* slot_mapping;  // [T]
+    const uint16_t* gamma;      // bf16 [128] or nullptr
+    uint8_t* index_k_cache;     // u8 [num_slots, 68]
+    int64_t T;
+    int64_t max_pos;
+    int64_t nslots;             // num_slots
+    float eps;
+    int pos64;
+    int rope_offset;
+    int e_lo1;
+    int e_lo2;
+};
+
 // FP4 paged MQA logits (scorer).
 struct LArgs {
     const uint8_t* q_out;         // u8 [B*next_n, H, 64]
@@ -81,6 +115,8 @@ hipError_t launch_k_rope_pack_store(const KArgs& a, bool is_neox, bool hadamard,
                                     hipStream_t stream);
 hipError_t launch_qk_rope_pack_store(const QArgs& qa, const KArgs& ka, bool is_neox, bool hadamard,
                                      hipStream_t stream);
+hipError_t launch_q_rope_pack_sglang(const SQArgs& a, bool is_neox, hipStream_t stream);
+hipError_t launch_k_rope_pack_store_sglang(const SKArgs& a, bool is_neox, hipStream_t stream);
 hipError_t launch_dequant(const DArgs& a, hipStream_t stream);
 hipError_t launch_paged_mqa_logits(const LArgs& a, hipStream_t stream);
 

@@ -536,6 +536,157 @@ __global__ __launch_bounds__(kBlock) void qk_kernel(QArgs qa, KArgs ka) {
         k_row<NEOX, NORM, HAD>(ka, kv, kslot, lane & 15, KC, KS);
 }
 
+// ---- sglang-compatible mode --------------------------------------------------
+// (sgl-project/sglang PR 39656 "Summary" and review.)  Each 32-group is
+// quantized twice.  Stage 1 fake-quantizes to the UE8M0 E2M1 grid with its own
+// floor: codes c1 under exponent e1, standing for the values
+// y = val(c1) * 2^(e1-127).  Stage 2 (the packer) takes the exponent of the
+// y's with the packer floor and packs their codes with the sign bit kept
+// only on a nonzero magnitude (+0 codes).
+//
+// Stage 2 works on the codes, not on the y's.  The largest |y| is
+// val(cmax) * 2^(e1-127) where cmax is the code of the stage-1 amax, and
+// ceil_pow2(val/6) is 2^((cmax >> 1) - 3) for every nonzero code, so
+//     e2 = max(e1 + (cmax >> 1) - 3, e_lo2)     (cmax > 0),   e_lo2 otherwise,
+// and the stage-2 code of y is RNE(val(c1) / 2^(e2-e1)) on the E2M1 grid:
+// the scaled converter applied to val(c1) (exact in bf16) with the
+// power-of-two scale 2^(e2-e1).  One corner differs: for e1 >= 253 a y of
+// magnitude >= 2^128 is +-inf in fp32, which makes the packer's amax infinite
+// (e2 = 254) and its code 7.
+__device__ __forceinline__ Q8 quant8_two_stage(uint4 v, int e_lo1, int e_lo2) {
+    const u16x2_t a0 = __builtin_bit_cast(u16x2_t, v.x & 0x7FFF7FFFu);
+    const u16x2_t a1 = __builtin_bit_cast(u16x2_t, v.y & 0x7FFF7FFFu);
+    const u16x2_t a2 = __builtin_bit_cast(u16x2_t, v.z & 0x7FFF7FFFu);
+    const u16x2_t a3 = __builtin_bit_cast(u16x2_t, v.w & 0x7FFF7FFFu);
+    const u16x2_t m2 = __builtin_elementwise_max(__builtin_elementwise_max(a0, a1),
+                                                 __builtin_elementwise_max(a2, a3));
+    uint32_t m = max((uint32_t)m2.x, (uint32_t)m2.y);
+    m = max(m, dpp<kDppXor1>(m));
+    m = max(m, dpp<kDppXor2>(m));
+    const int e1 = max((int)((m + 0x3Fu) >> 7) - 2, e_lo1);
+    const float scale1 = __uint_as_float((uint32_t)e1 << 23);
+    uint32_t c1 = 0;
+    c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c1, __builtin_bit_cast(bf16x2_t, v.x), scale1, 0);
+    c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c1, __builtin_bit_cast(bf16x2_t, v.y), scale1, 1);
+    c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c1, __builtin_bit_cast(bf16x2_t, v.z), scale1, 2);
+    c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c1, __builtin_bit_cast(bf16x2_t, v.w), scale1, 3);
+    const int cmax = (int)(__builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
+                               0u, __builtin_bit_cast(bf16x2_t, m), scale1, 0) & 7u);
+    // y of code c overflows iff (c >> 1) >= 256 - e1
+    const bool ovf = (cmax >> 1) >= 256 - e1;
+    int e2 = cmax ? max(e1 + (cmax >> 1) - 3, e_lo2) : e_lo2;
+    if (ovf) e2 = 254;
+    const int d = min(max(e2 - e1, -3), 8);  // beyond 8 every code is 0 either way
+    const float scale2 = __uint_as_float((uint32_t)(127 + d) << 23);
+    uint32_t p = 0;
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(p, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c1, 1.0f, 0), scale2, 0);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(p, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c1, 1.0f, 1), scale2, 1);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(p, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c1, 1.0f, 2), scale2, 2);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(p, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c1, 1.0f, 3), scale2, 3);
+    if (ovf) {
+        // nibbles whose y is infinite: (c >> 1) >= 3 for e1 = 253, >= 2 for e1 = 254
+        const uint32_t hi = (c1 >> 2) & 0x11111111u;
+        const uint32_t inf = (e1 >= 254) ? hi : (hi & (c1 >> 1));
+        p = (p & ~(inf * 0xFu)) | (inf * 7u) | (c1 & (inf << 3));
+    }
+    // +0 codes: bit 4k of nz is set iff nibble k has a nonzero magnitude
+    const uint32_t nz = (p | (p >> 1) | (p >> 2)) & 0x11111111u;
+    p &= 0x77777777u | (nz << 3);
+    return {p, e2};
+}
+
+// Query records [T, H, 68]: head h of token t is 64 code bytes, then its four
+// stage-2 exponents as one dword.  Lane and load layout as q_split_token; the
+// exponents of a head's four groups sit on the two quads of its 8 lanes and
+// are merged into lane 0 of the 8 with one half-row mirror.
+template <bool NEOX>
+__device__ __forceinline__ void q_sglang_token(const SQArgs& a, int64_t t, int lane,
+                                               const float C[8], const float S[8]) {
+    const int H = a.H;
+    const int c = chunk_of(lane & 7);
+    const int hsub = lane >> 3;
+    const int ro = a.rope_offset;
+    const int nro = 64 - ro;
+    const int sh_rot = 8 * (ro / 32 + (c >> 2));
+    const int sh_pln = 8 * (nro / 32 + (c >> 2));
+    const bool writer = (lane & 7) == 0;
+    const uint16_t* qt = a.q + t * (int64_t)H * 128 + hsub * 128 + 8 * c;
+    uint8_t* ot = a.q_packed + t * (int64_t)H * kSglangRecord + hsub * kSglangRecord + 4 * c;
+
+    uint4 np0 = load16_stream(qt + nro), nr0 = load16_stream(qt + ro);
+    uint4 np1 = load16_stream(qt + 8 * 128 + nro), nr1 = load16_stream(qt + 8 * 128 + ro);
+    for (int hb = 0; hb < H; hb += 16) {
+        const uint4 p0 = np0, r0 = nr0, p1 = np1, r1 = nr1;
+        if (hb + 16 < H) {
+            const uint16_t* nx = qt + (hb + 16) * 128;
+            np0 = load16_stream(nx + nro);
+            nr0 = load16_stream(nx + ro);
+            np1 = load16_stream(nx + 8 * 128 + nro);
+            nr1 = load16_stream(nx + 8 * 128 + ro);
+        }
+        const Q8 qp0 = quant8_two_stage(p0, a.e_lo1, a.e_lo2);
+        const Q8 qr0 = quant8_two_stage(rope8<NEOX>(r0, C, S), a.e_lo1, a.e_lo2);
+        const Q8 qp1 = quant8_two_stage(p1, a.e_lo1, a.e_lo2);
+        const Q8 qr1 = quant8_two_stage(rope8<NEOX>(r1, C, S), a.e_lo1, a.e_lo2);
+        uint8_t* o = ot + hb * kSglangRecord;
+        store4_stream(o + nro / 2, qp0.codes);
+        store4_stream(o + ro / 2, qr0.codes);
+        store4_stream(o + 8 * kSglangRecord + nro / 2, qp1.codes);
+        store4_stream(o + 8 * kSglangRecord + ro / 2, qr1.codes);
+        uint32_t x0 = ((uint32_t)qp0.e << sh_pln) | ((uint32_t)qr0.e << sh_rot);
+        uint32_t x1 = ((uint32_t)qp1.e << sh_pln) | ((uint32_t)qr1.e << sh_rot);
+        x0 |= dpp<kDppHalfMirror>(x0);
+        x1 |= dpp<kDppHalfMirror>(x1);
+        if (writer) {  // c == 0 here, so o is the start of the head's record
+            store4_stream(o + 64, x0);
+            store4_stream(o + 8 * kSglangRecord + 64, x1);
+        }
+    }
+}
+
+template <bool NEOX>
+__global__ __launch_bounds__(kBlock) void q_sglang_kernel(SQArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    if (t >= a.T) return;
+    const int64_t pos = clamped_position(a.positions, a.pos64, t, a.max_pos);
+    float C[8], S[8];
+    rope_coeffs<NEOX>(a.cos_sin + pos * 64, chunk_of(lane & 7), C, S);
+    q_sglang_token<NEOX>(a, t, lane, C, S);
+}
+
+// Key records [num_slots, 68]: 16 lanes per token as k_row_kernel.  Slot 0,
+// like any slot outside [1, num_slots), publishes nothing.  The four group
+// exponents are merged into lane 0 of the row (half-row mirror, then ror 8).
+template <bool NEOX, bool NORM>
+__global__ __launch_bounds__(kBlock) void k_sglang_kernel(SKArgs a) {
+    const int lane16 = threadIdx.x & 15;
+    const int64_t t = (int64_t)blockIdx.x * (kBlock / 16) + (threadIdx.x >> 4);
+    if (t >= a.T) return;
+    const int c = chunk_of(lane16);
+    uint4 v = load16_stream(a.k + t * 128 + 8 * c);
+    const int64_t slot = a.slot_mapping[t];
+    const int64_t pos = clamped_position(a.positions, a.pos64, t, a.max_pos);
+    float C[8], S[8];
+    rope_coeffs<NEOX>(a.cos_sin + pos * 64, c & 7, C, S);
+    if (slot <= 0 || slot >= a.nslots) return;
+    if (NORM) {
+        float G[8];
+        unpack8(load16(a.gamma + 8 * c), G);
+        v = rmsnorm8(v, G, a.eps);
+    }
+    const bool rot_lane = (c >> 3) == (a.rope_offset >> 6);
+    v = select4(rot_lane, rope8<NEOX>(v, C, S), v);
+    const Q8 q = quant8_two_stage(v, a.e_lo1, a.e_lo2);
+    uint8_t* rec = a.index_k_cache + slot * kSglangRecord;
+    *reinterpret_cast<uint32_t*>(rec + 4 * c) = q.codes;
+    uint32_t x = (uint32_t)q.e << (8 * (c >> 2));
+    x |= dpp<kDppHalfMirror>(x);
+    x |= dpp<kDppRor8>(x);
+    if (lane16 == 0) *reinterpret_cast<uint32_t*>(rec + 64) = x;
+}
+
 // ---- dequantization (debug reader) -------------------------------------------
 // One thread per 8 consecutive values (4 code bytes).
 __device__ __forceinline__ float e2m1_value(uint32_t nib) {
@@ -653,6 +804,24 @@ hipError_t launch_qk_rope_pack_store(const QArgs& qa, const KArgs& ka, bool is_n
         case 6: return launch2(qk_kernel<true, true, false>, blocks, lds, stream, qa, ka);
         default: return launch2(qk_kernel<true, true, true>, blocks, lds, stream, qa, ka);
     }
+}
+
+hipError_t launch_q_rope_pack_sglang(const SQArgs& a, bool is_neox, hipStream_t stream) {
+    if (a.T == 0) return hipSuccess;
+    const int64_t blocks = (a.T + kWavesPerBlock - 1) / kWavesPerBlock;
+    return is_neox ? launch(q_sglang_kernel<true>, blocks, 0, stream, a)
+                   : launch(q_sglang_kernel<false>, blocks, 0, stream, a);
+}
+
+hipError_t launch_k_rope_pack_store_sglang(const SKArgs& a, bool is_neox, hipStream_t stream) {
+    if (a.T == 0) return hipSuccess;
+    const int64_t blocks = (a.T + kBlock / 16 - 1) / (kBlock / 16);
+    const bool norm = a.gamma != nullptr;
+    if (is_neox)
+        return norm ? launch(k_sglang_kernel<true, true>, blocks, 0, stream, a)
+                    : launch(k_sglang_kernel<true, false>, blocks, 0, stream, a);
+    return norm ? launch(k_sglang_kernel<false, true>, blocks, 0, stream, a)
+                : launch(k_sglang_kernel<false, false>, blocks, 0, stream, a);
 }
 
 hipError_t launch_dequant(const DArgs& a, hipStream_t stream) {

@@ -58,6 +58,13 @@ def lib():
                                                     _i64, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p,
                                                     _p, _p, _p, _i64, _i, _p]
             L.fp4idx_qk_rope_pack_store.restype = _i
+            L.fp4idx_q_rope_pack_sglang.argtypes = [_p, _p, _i, _p, _i64, _i64, _i, _i, _i, _i,
+                                                    _i, _i, _f, _f, _p, _p]
+            L.fp4idx_q_rope_pack_sglang.restype = _i
+            L.fp4idx_k_rope_pack_store_sglang.argtypes = [_p, _p, _i, _p, _i64, _p, _p, _f, _i64,
+                                                          _i, _i, _i, _i, _i, _f, _f, _p, _i64,
+                                                          _p]
+            L.fp4idx_k_rope_pack_store_sglang.restype = _i
             L.fp4idx_paged_mqa_logits.argtypes = [_p, _p, _p, _f, _p, _p, _i64, _p, _i64, _p,
                                                   _i64, _i, _i, _i, _p, _i64, _p]
             L.fp4idx_paged_mqa_logits.restype = _i
@@ -160,6 +167,56 @@ def k_rope_pack_store(k, positions, cos_sin, slot_mapping, kv_cache, kv_cache_sc
         _ptr(kv_cache_scale), NB, KV_BLOCK, _stream_handle(stream))
     _check(rc)
     return kv_cache, kv_cache_scale
+
+
+SGLANG_RECORD = 68
+
+
+def q_rope_pack_sglang(q, positions, cos_sin, *, q_packed=None, is_neox=True, rope_offset=64,
+                       fake_quant_floor=DEFAULT_SCALE_FLOOR, pack_floor=DEFAULT_SCALE_FLOOR,
+                       stream=None):
+    """fp4idx_q_rope_pack_sglang.  q bf16 [T,H,128]; returns q_packed u8 [T,H,68]."""
+    T, H, D = q.shape
+    dev = q.device
+    _require(q, "q", (torch.bfloat16, torch.int16, torch.uint16))
+    _require(positions, "positions", (torch.int32, torch.int64), dev)
+    _require(cos_sin, "cos_sin", (torch.float32,), dev)
+    if q_packed is None:
+        q_packed = torch.empty((T, H, SGLANG_RECORD), dtype=torch.uint8, device=dev)
+    _require(q_packed, "q_packed", (torch.uint8,), dev)
+    if q_packed.numel() != T * H * SGLANG_RECORD:
+        raise ValueError(f"q_packed must hold [T, H, 68] = {T * H * SGLANG_RECORD} bytes")
+    rc = lib().fp4idx_q_rope_pack_sglang(
+        _ptr(q), _ptr(positions), int(positions.dtype == torch.int64), _ptr(cos_sin),
+        cos_sin.shape[0], T, H, D, ROPE_DIM, rope_offset, GROUP, int(is_neox), fake_quant_floor,
+        pack_floor, _ptr(q_packed), _stream_handle(stream))
+    _check(rc)
+    return q_packed
+
+
+def k_rope_pack_store_sglang(k, positions, cos_sin, slot_mapping, index_k_cache, *,
+                             k_norm_gamma=None, k_norm_eps=1e-6, is_neox=True, rope_offset=64,
+                             fake_quant_floor=DEFAULT_SCALE_FLOOR, pack_floor=DEFAULT_SCALE_FLOOR,
+                             stream=None):
+    """fp4idx_k_rope_pack_store_sglang.  k bf16 [T,128]; index_k_cache u8 [num_slots,68] is
+    updated in place (slot 0 publishes nothing)."""
+    T, D = k.shape
+    dev = k.device
+    _require(k, "k", (torch.bfloat16, torch.int16, torch.uint16))
+    _require(positions, "positions", (torch.int32, torch.int64), dev)
+    _require(cos_sin, "cos_sin", (torch.float32,), dev)
+    _require(slot_mapping, "slot_mapping", (torch.int64,), dev)
+    _require(index_k_cache, "index_k_cache", (torch.uint8,), dev)
+    _require(k_norm_gamma, "k_norm_gamma", (torch.bfloat16, torch.int16, torch.uint16), dev)
+    if index_k_cache.dim() != 2 or index_k_cache.shape[1] != SGLANG_RECORD:
+        raise ValueError("index_k_cache must be [num_slots, 68]")
+    rc = lib().fp4idx_k_rope_pack_store_sglang(
+        _ptr(k), _ptr(positions), int(positions.dtype == torch.int64), _ptr(cos_sin),
+        cos_sin.shape[0], _ptr(slot_mapping), _ptr(k_norm_gamma), k_norm_eps, T, D, ROPE_DIM,
+        rope_offset, GROUP, int(is_neox), fake_quant_floor, pack_floor, _ptr(index_k_cache),
+        index_k_cache.shape[0], _stream_handle(stream))
+    _check(rc)
+    return index_k_cache
 
 
 def qk_rope_pack_store(q, k, positions, cos_sin, slot_mapping, kv_cache, kv_cache_scale,

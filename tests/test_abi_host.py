@@ -25,8 +25,10 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert names == ["fp4idx_dequant_debug", "fp4idx_k_rope_pack_store", "fp4idx_last_error",
-                     "fp4idx_paged_mqa_logits", "fp4idx_q_rope_pack", "fp4idx_qk_rope_pack_store"]
+    assert names == ["fp4idx_dequant_debug", "fp4idx_k_rope_pack_store",
+                     "fp4idx_k_rope_pack_store_sglang", "fp4idx_last_error",
+                     "fp4idx_paged_mqa_logits", "fp4idx_q_rope_pack", "fp4idx_q_rope_pack_sglang",
+                     "fp4idx_qk_rope_pack_store"]
     lib = ctypes.CDLL(fp4idx.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -201,6 +203,67 @@ def test_scorer_rejections(over, code, msg):
     assert msg in fp4idx.last_error(), fp4idx.last_error()
 
 
+def sq_call(**over):
+    a = dict(q=ALIGNED, positions=ALIGNED, positions_int64=1, cos_sin=ALIGNED, max_pos=16, T=4,
+             H=32, D=128, R=64, rope_offset=64, group_size=32, is_neox=1,
+             fake_quant_floor=2.0 ** -126, pack_floor=1e-10, q_packed=ALIGNED, stream=None)
+    a.update(over)
+    return fp4idx.lib().fp4idx_q_rope_pack_sglang(*a.values())
+
+
+def sk_call(**over):
+    a = dict(k=ALIGNED, positions=ALIGNED, positions_int64=1, cos_sin=ALIGNED, max_pos=16,
+             slot_mapping=ALIGNED, k_norm_gamma=None, k_norm_eps=1e-6, T=4, D=128, R=64,
+             rope_offset=64, group_size=32, is_neox=1, fake_quant_floor=2.0 ** -126,
+             pack_floor=1e-10, index_k_cache=ALIGNED, num_slots=128, stream=None)
+    a.update(over)
+    return fp4idx.lib().fp4idx_k_rope_pack_store_sglang(*a.values())
+
+
+SQ_REJECT = [
+    (dict(D=64), fp4idx.EUNSUPPORTED, "head_dim"),
+    (dict(H=8), fp4idx.EUNSUPPORTED, "n_heads"),
+    (dict(rope_offset=16), fp4idx.EUNSUPPORTED, "rope_offset"),
+    (dict(fake_quant_floor=-1.0), fp4idx.EINVAL, "fake_quant_floor"),
+    (dict(pack_floor=float("nan")), fp4idx.EINVAL, "pack_floor"),
+    (dict(pack_floor=float("inf")), fp4idx.EINVAL, "pack_floor"),
+    (dict(is_neox=5), fp4idx.EINVAL, "is_neox"),
+    (dict(q_packed=None), fp4idx.EINVAL, "q_packed must not be NULL"),
+    (dict(q_packed=ALIGNED + 2), fp4idx.EINVAL, "q_packed must be 4-byte"),
+    (dict(q=ALIGNED + 4), fp4idx.EINVAL, "q must be 16-byte"),
+    (dict(T=1 << 58), fp4idx.EINVAL, "T too large"),
+]
+
+
+@pytest.mark.parametrize("over,code,msg", SQ_REJECT)
+def test_sglang_q_rejections(over, code, msg):
+    assert sq_call(**over) == code
+    assert msg in fp4idx.last_error(), fp4idx.last_error()
+    assert fp4idx.last_error().startswith("fp4idx_q_rope_pack_sglang:")
+
+
+SK_REJECT = [
+    (dict(group_size=64), fp4idx.EUNSUPPORTED, "group_size"),
+    (dict(num_slots=-1), fp4idx.EINVAL, "num_slots"),
+    (dict(num_slots=1 << 62), fp4idx.EINVAL, "num_slots"),
+    (dict(fake_quant_floor=float("-inf")), fp4idx.EINVAL, "fake_quant_floor"),
+    (dict(pack_floor=-0.5), fp4idx.EINVAL, "pack_floor"),
+    (dict(k_norm_gamma=ALIGNED, k_norm_eps=-1.0), fp4idx.EINVAL, "k_norm_eps"),
+    (dict(k_norm_gamma=ALIGNED + 8), fp4idx.EINVAL, "k_norm_gamma must be 16-byte"),
+    (dict(index_k_cache=ALIGNED + 1), fp4idx.EINVAL, "index_k_cache must be 4-byte"),
+    (dict(index_k_cache=None), fp4idx.EINVAL, "index_k_cache must not be NULL"),
+    (dict(slot_mapping=ALIGNED + 4), fp4idx.EINVAL, "slot_mapping must be 8-byte"),
+    (dict(positions_int64=0, positions=ALIGNED + 2), fp4idx.EINVAL, "positions must be 4-byte"),
+]
+
+
+@pytest.mark.parametrize("over,code,msg", SK_REJECT)
+def test_sglang_k_rejections(over, code, msg):
+    assert sk_call(**over) == code
+    assert msg in fp4idx.last_error(), fp4idx.last_error()
+    assert fp4idx.last_error().startswith("fp4idx_k_rope_pack_store_sglang:")
+
+
 def test_zero_tokens_is_a_noop_even_with_null_buffers():
     assert q_call(T=0, q=None, positions=None, cos_sin=None, q_out=None, q_scale_out=None) == 0
     assert k_call(T=0, k=None, positions=None, cos_sin=None, slot_mapping=None, kv_cache=None,
@@ -209,6 +272,9 @@ def test_zero_tokens_is_a_noop_even_with_null_buffers():
     assert qk_call(T=0, q=None, k=None, positions=None, cos_sin=None, slot_mapping=None,
                    q_out=None, q_scale_out=None, kv_cache=None, kv_cache_scale=None) == 0
     assert s_call(B=0, q_out=None, logits=None, block_table=None) == 0
+    assert sq_call(T=0, q=None, positions=None, cos_sin=None, q_packed=None) == 0
+    assert sk_call(T=0, k=None, positions=None, cos_sin=None, slot_mapping=None,
+                   index_k_cache=None) == 0
     # but shapes are still checked first
     assert q_call(T=0, D=64) == fp4idx.EUNSUPPORTED
 
