@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "pack_token_amd", "csrc", "fp4idx_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qk_kernel_large_prefill_traffic.json")
+SGLANG_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q_sglang_kernel_sglang_prefill_traffic.json")
 
 
 def q_bytes_per_token(H: int) -> int:
@@ -50,12 +51,12 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes of one fused launch from committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE counts (scaled by a plain copy's counts), if they were taken on
-    the current kernel source; otherwise None."""
+def measured_traffic(path=TRAFFIC_FILE):
+    """HBM bytes of one launch of the profiled kernel from committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE counts (scaled by a plain copy's counts), if they
+    were taken on the current kernel source; otherwise None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -180,7 +181,9 @@ def bench_sglang(args, dev):
         "k_kernel_GBps": kb / (k_ms * 1e-3) / 1e9,
         "roofline": {"kernel": "q_sglang_kernel<neox>", "bound": "hbm", "achieved": q_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": q_gbs / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes_per_launch": qb,
+                     "traffic": measured_traffic(SGLANG_TRAFFIC_FILE) if (T, H) == (131072, 64)
+                     else None,
+                     "algorithmic_bytes_per_launch": qb,
                      "launch_us": q_ms * 1e3},
     }
     if not args.no_cpu_baseline:
