@@ -72,6 +72,19 @@ def _lib():
             lib.oracle_k_rope_pack_store_sglang.restype = _i
             lib.oracle_quantize_rows_two_stage.argtypes = [_p, _i64, _f, _f, _p]
             lib.oracle_quantize_rows_two_stage.restype = None
+            lib.oracle_q_rope_pack_fp8.argtypes = [_p, _p, _i, _p, _i64, _p, _f, _i64, _i, _i, _i,
+                                                   _i, _i, _i, _i, _f, _p, _p]
+            lib.oracle_q_rope_pack_fp8.restype = _i
+            lib.oracle_k_rope_pack_store_fp8.argtypes = [_p, _p, _i, _p, _i64, _p, _p, _f, _i64,
+                                                         _i, _i, _i, _i, _i, _i, _f, _p, _p, _i64,
+                                                         _i]
+            lib.oracle_k_rope_pack_store_fp8.restype = _i
+            lib.oracle_e4m3_codes.argtypes = [_p, _i64, _p]
+            lib.oracle_e4m3_codes.restype = None
+            lib.oracle_fp8_scales.argtypes = [_p, _i64, _f, _i, _p]
+            lib.oracle_fp8_scales.restype = None
+            lib.oracle_quantize_rows_fp8.argtypes = [_p, _i64, _f, _i, _p, _p]
+            lib.oracle_quantize_rows_fp8.restype = None
             lib.oracle_hadamard_scale.argtypes = []
             lib.oracle_hadamard_scale.restype = _f
             _LIB = lib
@@ -287,6 +300,86 @@ def quantize_rows_two_stage(x, floor1=DEFAULT_SCALE_FLOOR, floor2=DEFAULT_SCALE_
     out = np.empty((n, SLOT68), np.uint8)
     _lib().oracle_quantize_rows_two_stage(x.ctypes.data, n, floor1, floor2, out.ctypes.data)
     return out
+
+
+FP8_UE8M0, FP8_FP32 = 0, 1
+
+
+def _positions(positions):
+    positions = np.ascontiguousarray(positions)
+    pos64 = 1 if positions.dtype == np.int64 else 0
+    if not pos64:
+        positions = _c(positions, np.int32)
+    return positions, pos64
+
+
+def q_rope_pack_fp8(q_bits, positions, cos_sin, weights, *, weights_scale=1.0, is_neox=True,
+                    rope_offset=64, apply_hadamard=False, scale_fmt=FP8_UE8M0,
+                    scale_floor=DEFAULT_SCALE_FLOOR):
+    """FP8 output mode, query side: (q_out u8 [T,H,128], weights_out bf16 bits u16 [T,H])."""
+    q_bits = _c(q_bits, np.uint16)
+    T, H, D = q_bits.shape
+    positions, pos64 = _positions(positions)
+    cos_sin = _c(cos_sin, np.float32)
+    weights = _c(weights, np.float32)
+    q_out = np.full((T, H, D), 0xA5, np.uint8)
+    w_out = np.full((T, H), 0xFFFF, np.uint16)
+    rc = _lib().oracle_q_rope_pack_fp8(q_bits.ctypes.data, positions.ctypes.data, pos64,
+                                       cos_sin.ctypes.data, cos_sin.shape[0], weights.ctypes.data,
+                                       weights_scale, T, H, D, ROPE_DIM, rope_offset,
+                                       int(bool(is_neox)), int(bool(apply_hadamard)), scale_fmt,
+                                       scale_floor, q_out.ctypes.data, w_out.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_q_rope_pack_fp8 rejected its arguments (rc={rc})")
+    return q_out, w_out
+
+
+def k_rope_pack_store_fp8(k_bits, positions, cos_sin, slot_mapping, kv_cache, kv_cache_scale, *,
+                          k_norm_gamma=None, k_norm_eps=1e-6, is_neox=True, rope_offset=64,
+                          apply_hadamard=False, scale_fmt=FP8_UE8M0,
+                          scale_floor=DEFAULT_SCALE_FLOOR):
+    """FP8 output mode, key side: kv_cache u8 [NB,64,128], kv_cache_scale fp32 [NB,64]."""
+    k_bits = _c(k_bits, np.uint16)
+    T, D = k_bits.shape
+    positions, pos64 = _positions(positions)
+    cos_sin = _c(cos_sin, np.float32)
+    slot_mapping = _c(slot_mapping, np.int64)
+    assert kv_cache.dtype == np.uint8 and kv_cache.flags.c_contiguous
+    assert kv_cache_scale.dtype == np.float32 and kv_cache_scale.flags.c_contiguous
+    gamma = None if k_norm_gamma is None else _c(k_norm_gamma, np.uint16)
+    rc = _lib().oracle_k_rope_pack_store_fp8(
+        k_bits.ctypes.data, positions.ctypes.data, pos64, cos_sin.ctypes.data, cos_sin.shape[0],
+        slot_mapping.ctypes.data, _ptr(gamma), k_norm_eps, T, D, ROPE_DIM, rope_offset,
+        int(bool(is_neox)), int(bool(apply_hadamard)), scale_fmt, scale_floor,
+        kv_cache.ctypes.data, kv_cache_scale.ctypes.data, kv_cache.shape[0], 64)
+    if rc != 0:
+        raise ValueError(f"oracle_k_rope_pack_store_fp8 rejected its arguments (rc={rc})")
+    return kv_cache, kv_cache_scale
+
+
+def e4m3_codes(y):
+    y = _c(y, np.float32)
+    out = np.empty(y.shape, np.uint8)
+    _lib().oracle_e4m3_codes(y.ctypes.data, y.size, out.ctypes.data)
+    return out
+
+
+def fp8_scales(amax, scale_floor=DEFAULT_SCALE_FLOOR, ue8m0=True):
+    amax = _c(amax, np.float32)
+    out = np.empty(amax.shape, np.float32)
+    _lib().oracle_fp8_scales(amax.ctypes.data, amax.size, scale_floor, int(bool(ue8m0)),
+                             out.ctypes.data)
+    return out
+
+
+def quantize_rows_fp8(x, scale_floor=DEFAULT_SCALE_FLOOR, ue8m0=True):
+    x = _c(x, np.float32)
+    n = x.shape[0]
+    codes = np.empty((n, 128), np.uint8)
+    scales = np.empty(n, np.float32)
+    _lib().oracle_quantize_rows_fp8(x.ctypes.data, n, scale_floor, int(bool(ue8m0)),
+                                    codes.ctypes.data, scales.ctypes.data)
+    return codes, scales
 
 
 # ---- step-level entry points (for the pins) ----

@@ -543,3 +543,149 @@ void oracle_quantize_rows_two_stage(const float* x, int64_t n, float floor1, flo
                                     uint8_t* records) {
     for (int64_t r = 0; r < n; ++r) quantize_row_two_stage(x + r * HEAD_DIM, floor1, floor2, records + r * SLOT68);
 }
+
+/* ------------------------------------------------------------------ */
+/* FP8 output mode ([aiter-5484] API: the FP8 contract of the same op   */
+/* folds its per-(token, head) q scale into weights_out, together with  */
+/* weights_scale, which then rounds through q.dtype = bf16; scale_fmt   */
+/* is ue8m0 or fp32.  [aiter-4029] review: the gfx950 FP8 format is     */
+/* e4m3fn with a largest value of 448).                                 */
+/* Readings: one scale per 128-row (a query head, a key token); scale   */
+/* s = max(amax / 448, floor), under ue8m0 raised to a power of two by  */
+/* the same (bits >> 23) + (mantissa != 0) rule as the FP4 exponent;    */
+/* codes are the e4m3fn values nearest to x / s (ties to even, sign     */
+/* kept on zero); keys go to kv_cache[slot, 0:128] with the fp32 scale  */
+/* at kv_cache_scale[slot].                                             */
+/* ------------------------------------------------------------------ */
+#define FP8_MAX 448.0f
+
+/* e4m3fn code of a finite y.  Magnitudes: k * 2^-9 for codes k < 8
+   (subnormals), (8 + m) * 2^(E - 10) for code (E << 3) | m, E = 1..15,
+   except code 0x7F (NaN).  Nearest value, ties to the even code; anything
+   at or beyond 448 saturates to 448 (0x7E). */
+static uint8_t e4m3_code(float y) {
+    const uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    const double a = fabs((double)y);
+    if (a >= 448.0) return (uint8_t)(sign | 0x7E);
+    int code;
+    if (a < ldexp(1.0, -6)) {
+        const double k = a * 512.0;              /* exact */
+        const double fk = floor(k);
+        int ki = (int)fk;
+        const double r = k - fk;
+        if (r > 0.5 || (r == 0.5 && (ki & 1))) ki += 1;
+        code = ki;                               /* 8 is the smallest normal */
+    } else {
+        int e;
+        const double m = frexp(a, &e);           /* a = m * 2^e, m in [0.5, 1) */
+        const double s = m * 16.0;               /* exact, in [8, 16) */
+        const double fs = floor(s);
+        int si = (int)fs;
+        const double r = s - fs;
+        if (r > 0.5 || (r == 0.5 && (si & 1))) si += 1;
+        int E = e - 1 + 7;
+        if (si == 16) { si = 8; E += 1; }
+        code = (E << 3) | (si - 8);
+    }
+    return (uint8_t)(sign | code);
+}
+
+static float fp8_scale(float amax, float scale_floor, int ue8m0) {
+    float s = amax / FP8_MAX;
+    if (s < scale_floor) s = scale_floor;
+    if (ue8m0) {
+        uint32_t b = f2u(s);
+        int e = (int)(b >> 23) + ((b & 0x7FFFFFu) != 0u ? 1 : 0);
+        if (e < 1) e = 1;
+        if (e > 254) e = 254;
+        s = u2f((uint32_t)e << 23);
+    }
+    return s;
+}
+
+/* one 128-row: scale and the 128 codes */
+static float quantize_row_fp8(const float* x, float scale_floor, int ue8m0, uint8_t* codes) {
+    float amax = 0.0f;
+    for (int i = 0; i < HEAD_DIM; ++i) {
+        float a = fabsf(x[i]);
+        if (a > amax) amax = a;
+    }
+    const float s = fp8_scale(amax, scale_floor, ue8m0);
+    for (int i = 0; i < HEAD_DIM; ++i) codes[i] = e4m3_code(x[i] / s);
+    return s;
+}
+
+static int check_fp8_args(int scale_fmt, float scale_floor) {
+    if (scale_fmt != 0 && scale_fmt != 1) return ORC_EINVAL;
+    if (!(scale_floor >= 0.0f)) return ORC_EINVAL;
+    if (scale_fmt == 1 && !(scale_floor > 0.0f)) return ORC_EINVAL;  /* s must be > 0 */
+    return ORC_OK;
+}
+
+/* scale_fmt: 0 = ue8m0, 1 = fp32.  q_out u8 [T, H, 128]; weights_out bf16
+   [T, H] = bf16((weights * s_q) * weights_scale). */
+int oracle_q_rope_pack_fp8(const uint16_t* q, const void* positions, int positions_int64,
+                           const float* cos_sin, int64_t max_pos, const float* weights,
+                           float weights_scale, int64_t T, int H, int D, int R, int rope_offset,
+                           int is_neox, int apply_hadamard, int scale_fmt, float scale_floor,
+                           uint8_t* q_out, uint16_t* weights_out) {
+    if (check_shape(D, R, rope_offset, GROUP) != ORC_OK) return ORC_EINVAL;
+    if (check_fp8_args(scale_fmt, scale_floor) != ORC_OK) return ORC_EINVAL;
+    if (H <= 0 || H % 16 != 0 || T < 0 || max_pos <= 0) return ORC_EINVAL;
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t pos = read_position(positions, positions_int64, t, max_pos);
+        const float* cs_row = cos_sin + pos * ROPE_DIM;
+        for (int h = 0; h < H; ++h) {
+            float x[HEAD_DIM];
+            for (int i = 0; i < HEAD_DIM; ++i) x[i] = bf16_to_f32(q[(t * H + h) * HEAD_DIM + i]);
+            rope_hadamard_row(x, cs_row, rope_offset, is_neox, apply_hadamard);
+            const float s = quantize_row_fp8(x, scale_floor, scale_fmt == 0,
+                                             q_out + (t * H + h) * HEAD_DIM);
+            const float w = weights[t * H + h] * s;
+            weights_out[t * H + h] = f32_to_bf16_bits(w * weights_scale);
+        }
+    }
+    return ORC_OK;
+}
+
+/* kv_cache u8 [NB, BS, 128]: token -> kv_cache[slot, :]; kv_cache_scale fp32
+   [NB, BS]: its scale at [slot].  Slots outside [0, NB*BS) write nothing. */
+int oracle_k_rope_pack_store_fp8(const uint16_t* k, const void* positions, int positions_int64,
+                                 const float* cos_sin, int64_t max_pos,
+                                 const int64_t* slot_mapping, const uint16_t* k_norm_gamma,
+                                 float k_norm_eps, int64_t T, int D, int R, int rope_offset,
+                                 int is_neox, int apply_hadamard, int scale_fmt,
+                                 float scale_floor, uint8_t* kv_cache, float* kv_cache_scale,
+                                 int64_t NB, int BS) {
+    if (check_shape(D, R, rope_offset, GROUP) != ORC_OK) return ORC_EINVAL;
+    if (check_fp8_args(scale_fmt, scale_floor) != ORC_OK) return ORC_EINVAL;
+    if (BS != KV_BLOCK || NB < 0 || T < 0 || max_pos <= 0) return ORC_EINVAL;
+    const int64_t nslots = NB * BS;
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t slot = slot_mapping[t];
+        if (slot < 0 || slot >= nslots) continue;
+        int64_t pos = read_position(positions, positions_int64, t, max_pos);
+        float x[HEAD_DIM];
+        for (int i = 0; i < HEAD_DIM; ++i) x[i] = bf16_to_f32(k[t * HEAD_DIM + i]);
+        if (k_norm_gamma) rmsnorm128(x, k_norm_gamma, k_norm_eps);
+        rope_hadamard_row(x, cos_sin + pos * ROPE_DIM, rope_offset, is_neox, apply_hadamard);
+        kv_cache_scale[slot] = quantize_row_fp8(x, scale_floor, scale_fmt == 0,
+                                                kv_cache + slot * HEAD_DIM);
+    }
+    return ORC_OK;
+}
+
+/* step-level, for the pins */
+void oracle_e4m3_codes(const float* y, int64_t n, uint8_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = e4m3_code(y[i]);
+}
+
+void oracle_fp8_scales(const float* amax, int64_t n, float scale_floor, int ue8m0, float* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = fp8_scale(amax[i], scale_floor, ue8m0);
+}
+
+void oracle_quantize_rows_fp8(const float* x, int64_t n, float scale_floor, int ue8m0,
+                              uint8_t* codes, float* scales) {
+    for (int64_t r = 0; r < n; ++r)
+        scales[r] = quantize_row_fp8(x + r * HEAD_DIM, scale_floor, ue8m0, codes + r * HEAD_DIM);
+}

@@ -1,0 +1,157 @@
+"""Pins for the oracle's FP8 output mode (ROCm/aiter PR 5484 "API": the FP8
+contract folds the per-(token, head) q scale, and weights_scale, into
+weights_out in q.dtype; scale_fmt ue8m0 or fp32.  ROCm/aiter PR 4029 review:
+e4m3fn, largest value 448, on gfx950).  The e4m3fn encoder is pinned to
+torch's float8_e4m3fn cast and to a nearest-value search; the whole quantizer
+to torch's division followed by that cast."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from pack_token_amd import workloads
+from pack_token_amd.workloads import bf16_bits_to_f32, to_bf16_bits
+
+
+def torch_e4m3(y):
+    return torch.from_numpy(np.ascontiguousarray(y, np.float32)).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+
+
+def e4m3_values():
+    """Magnitudes of codes 0..126 from the format's definition."""
+    c = np.arange(127)
+    E, m = c >> 3, c & 7
+    return np.where(E == 0, m * 2.0 ** -9, (8 + m) * 2.0 ** (E - 10.0))
+
+
+def test_values_table_against_torch_decode():
+    v = e4m3_values()
+    dec = torch.from_numpy(np.arange(127, dtype=np.uint8)).view(torch.float8_e4m3fn).float().numpy()
+    assert np.array_equal(v, dec.astype(np.float64))
+    assert v[126] == 448.0 and v[8] == 2.0 ** -6 and v[1] == 2.0 ** -9
+
+
+def test_every_finite_bf16_in_range_matches_torch():
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    x = bf16_bits_to_f32(b)
+    x = x[np.isfinite(x) & (np.abs(x) < 464.0)]
+    assert np.array_equal(oracle.e4m3_codes(x), torch_e4m3(x))
+
+
+def test_random_fp32_and_midpoints_match_torch_and_search():
+    rng = np.random.default_rng(0)
+    y = np.concatenate([
+        (rng.uniform(-1, 1, 200000) * 2.0 ** rng.integers(-14, 9, 200000)).astype(np.float32),
+        rng.uniform(-463.9, 463.9, 20000).astype(np.float32)])
+    v = e4m3_values()
+    mids = ((v[1:] + v[:-1]) / 2).astype(np.float32)          # every midpoint, exact in fp32
+    y = np.concatenate([y, mids, -mids, np.nextafter(mids, 0), np.nextafter(mids, 1000)])
+    got = oracle.e4m3_codes(y)
+    assert np.array_equal(got, torch_e4m3(y))
+    # nearest-value search with ties to the even code
+    a = np.abs(y.astype(np.float64))[:, None]
+    d = np.abs(a - v[None, :])
+    best = d.min(axis=1, keepdims=True)
+    cand = np.where(d == best, np.arange(127)[None, :], 1 << 20)
+    even = np.where(cand % 2 == 0, cand, 1 << 20).min(axis=1)
+    code = np.where(even < (1 << 20), even, cand.min(axis=1))
+    code = code | np.where(np.signbit(y), 0x80, 0)
+    assert np.array_equal(got, code.astype(np.uint8))
+
+
+def test_zero_sign_and_saturation():
+    y = np.array([0.0, -0.0, -1e-30, 448.0, 463.9, -455.0, 2.0 ** -10, -2.0 ** -10], np.float32)
+    assert oracle.e4m3_codes(y).tolist() == [0x00, 0x80, 0x80, 0x7E, 0x7E, 0xFE, 0x00, 0x80]
+
+
+def test_scales():
+    rng = np.random.default_rng(1)
+    amax = (rng.uniform(0.5, 1, 5000) * 2.0 ** rng.integers(-130, 120, 5000)).astype(np.float32)
+    amax[:3] = [0.0, 448.0, 896.0]
+    fl = np.float32(2.0 ** -126)
+    s32 = oracle.fp8_scales(amax, fl, ue8m0=False)
+    want32 = np.maximum(amax / np.float32(448.0), fl)
+    assert np.array_equal(s32, want32)
+    s8 = oracle.fp8_scales(amax, fl, ue8m0=True)
+    # least power of two >= max(amax / 448, floor) (fp32 division), within [2^-126, 2^127]
+    m, e = np.frexp(want32.astype(np.float64))
+    p2 = np.where(m == 0.5, want32, np.ldexp(1.0, e))
+    assert np.array_equal(s8.astype(np.float64), np.clip(p2, 2.0 ** -126, 2.0 ** 127))
+    assert s8[1] == 1.0 and s8[2] == 2.0 and s8[0] == fl
+
+
+@pytest.mark.parametrize("ue8m0", [True, False])
+def test_quantizer_equals_torch_division_and_cast(ue8m0):
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((400, 128)).astype(np.float32) * np.float32(3.0)
+    x[:, 0] *= np.float32(50.0)
+    x[5] = 0.0
+    x[6, :64] = -0.0
+    x = bf16_bits_to_f32(to_bf16_bits(x))
+    codes, s = oracle.quantize_rows_fp8(x, ue8m0=ue8m0)
+    amax = torch.from_numpy(np.abs(x)).amax(dim=1)
+    st = torch.clamp(amax / 448.0, min=float(np.float32(2.0 ** -126)))
+    if ue8m0:
+        st = torch.exp2(torch.ceil(torch.log2(st)))
+    assert np.array_equal(s, st.numpy())
+    y = torch.from_numpy(x) / st[:, None]
+    assert np.array_equal(codes, y.to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    # dequantized values within half an e4m3 step of x
+    deq = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy() * s[:, None]
+    step = np.maximum(np.abs(x) * 2.0 ** -3, 2.0 ** -9 * s[:, None])
+    assert (np.abs(deq - x) <= step / 2 * (1 + 1e-6)).all()
+
+
+def test_query_records_and_weight_fold():
+    wl = workloads.sweep_case(8, 24, 32, True, 64)
+    for fmt, ws in [(0, 1.0), (0, 0.125), (1, 0.7)]:
+        q_out, w_out = oracle.q_rope_pack_fp8(wl.q, wl.positions, wl.cos_sin, wl.weights,
+                                              weights_scale=ws, scale_fmt=fmt)
+        cs = np.repeat(wl.cos_sin[wl.positions], 32, axis=0)
+        x = oracle.rope_rows(bf16_bits_to_f32(wl.q).reshape(-1, 128), cs)
+        codes, s = oracle.quantize_rows_fp8(x, ue8m0=fmt == 0)
+        assert np.array_equal(q_out.reshape(-1, 128), codes)
+        w = wl.weights.reshape(-1).astype(np.float32)
+        want = to_bf16_bits((w * s) * np.float32(ws))
+        assert np.array_equal(w_out.reshape(-1), want)
+        if fmt == 0 and ws == 1.0:
+            # a power-of-two scale commutes with the bf16 rounding
+            assert np.array_equal(bf16_bits_to_f32(w_out.reshape(-1)),
+                                  bf16_bits_to_f32(to_bf16_bits(w)) * s)
+
+
+def test_key_cache_layout_rmsnorm_and_skips():
+    rng = np.random.default_rng(3)
+    wl = workloads.sweep_case(9, 30, 16, False, 0)
+    gamma = to_bf16_bits(rng.uniform(0.5, 1.5, 128).astype(np.float32))
+    NB = 2
+    slots = rng.permutation(NB * 64)[:30].astype(np.int64)
+    slots[[3, 7]] = [-1, NB * 64]
+    slots[np.nonzero(slots == 0)[0]] = NB * 64 + 1
+    slots[11] = 0                                       # slot 0 is an ordinary slot here
+    kv = np.full((NB, 64, 128), 0xA5, np.uint8)
+    ks = np.full((NB, 64), np.nan, np.float32)
+    for fmt in (0, 1):
+        oracle.k_rope_pack_store_fp8(wl.k, wl.positions, wl.cos_sin, slots, kv, ks,
+                                     k_norm_gamma=gamma, is_neox=False, rope_offset=0,
+                                     apply_hadamard=True, scale_fmt=fmt)
+        x = oracle.rmsnorm_rows(bf16_bits_to_f32(wl.k), gamma, 1e-6)
+        x = oracle.fwht_rows(oracle.rope_rows(x, wl.cos_sin[wl.positions], rope_offset=0,
+                                              is_neox=False))      # scaled, bf16-rounded
+        codes, s = oracle.quantize_rows_fp8(x, ue8m0=fmt == 0)
+        flat, fs = kv.reshape(-1, 128), ks.reshape(-1)
+        for t, sl in enumerate(slots):
+            if 0 <= sl < NB * 64:
+                assert np.array_equal(flat[sl], codes[t]) and fs[sl] == s[t]
+        untouched = np.setdiff1d(np.arange(NB * 64), slots)
+        assert (flat[untouched] == 0xA5).all() and np.isnan(fs[untouched]).all()
+
+
+def test_rejects_zero_floor_with_fp32_scales():
+    wl = workloads.tiny(T=2, H=16)
+    with pytest.raises(ValueError):
+        oracle.q_rope_pack_fp8(wl.q, wl.positions, wl.cos_sin, wl.weights, scale_fmt=1,
+                               scale_floor=0.0)
+    oracle.q_rope_pack_fp8(wl.q, wl.positions, wl.cos_sin, wl.weights, scale_fmt=0,
+                           scale_floor=0.0)

@@ -13,15 +13,15 @@ from oracle import build as obuild
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PINS = ["tests/test_oracle_quant.py", "tests/test_oracle_transforms.py",
         "tests/test_oracle_layout.py", "tests/test_oracle_scorer.py",
-        "tests/test_oracle_sglang.py"]
+        "tests/test_oracle_sglang.py", "tests/test_oracle_fp8.py"]
 
 MUTATIONS = {
     "tie_at_0.75_goes_down": ("else if (m < 0.75f) code = 1;", "else if (m <= 0.75f) code = 1;"),
     "tie_at_5_goes_down": ("else if (m <= 5.0f) code = 6;", "else if (m < 5.0f) code = 6;"),
     "zero_code_drops_sign": ("return (uint8_t)((sign << 3) | code);",
                              "return (uint8_t)(((code ? sign : 0) << 3) | code);"),
-    "floor_exponent_rule": ("int e = (int)(b >> 23) + ((b & 0x7FFFFFu) != 0u ? 1 : 0);",
-                            "int e = (int)(b >> 23);"),
+    "floor_exponent_rule": ("uint32_t b = f2u(q);\n    int e = (int)(b >> 23) + ((b & 0x7FFFFFu) != 0u ? 1 : 0);",
+                            "uint32_t b = f2u(q);\n    int e = (int)(b >> 23);"),
     "neox_interleaved_swapped": ("int ia = is_neox ? i : 2 * i;", "int ia = is_neox ? 2 * i : i;"),
     "rope_sign": ("S[ia] = round_bf16(ac - bs);", "S[ia] = round_bf16(ac + bs);"),
     "cos_sin_swapped": ("float c = cs_row[i], s = cs_row[ROPE_DIM / 2 + i];",
@@ -44,8 +44,10 @@ MUTATIONS = {
     "signed_amax": ("float a = fabsf(v[i]);", "float a = v[i];"),
     "amax_over_4": ("float q = amax / 6.0f;", "float q = amax / 4.0f;"),
     "position_clamp_to_0": ("if (p >= max_pos) p = max_pos - 1;", "if (p >= max_pos) p = 0;"),
-    "slot_0_skipped": ("if (slot < 0 || slot >= nslots) continue;",
-                       "if (slot <= 0 || slot >= nslots) continue;"),
+    "slot_0_skipped": ("\n        int64_t slot = slot_mapping[t];\n        if (slot < 0 || slot >= nslots) continue;",
+                       "\n        int64_t slot = slot_mapping[t];\n        if (slot <= 0 || slot >= nslots) continue;"),
+    "fp8_slot_0_skipped": ("const int64_t slot = slot_mapping[t];\n        if (slot < 0 || slot >= nslots) continue;",
+                           "const int64_t slot = slot_mapping[t];\n        if (slot <= 0 || slot >= nslots) continue;"),
     "hadamard_scale_1_over_8": ("return (float)(1.0 / sqrt((double)HEAD_DIM));",
                                 "return (float)(1.0 / sqrt((double)64));"),
     "weights_head_0_skipped": ("for (int h = 0; h < H; ++h) weights_out[t * H + h] = weights[t * H + h];",
@@ -71,6 +73,22 @@ MUTATIONS = {
                                 "if (0) rmsnorm128(x, k_norm_gamma, k_norm_eps);\n        rope_slice("),
     "sglang_query_wrong_rope_slice": ("rope_slice(x + rope_offset, cs_row, is_neox);\n            quantize_row_two_stage",
                                       "rope_slice(x + 64 - rope_offset, cs_row, is_neox);\n            quantize_row_two_stage"),
+    "fp8_max_240": ("#define FP8_MAX 448.0f", "#define FP8_MAX 240.0f"),
+    "e4m3_ties_up": ("if (r > 0.5 || (r == 0.5 && (si & 1))) si += 1;", "if (r >= 0.5) si += 1;"),
+    "e4m3_subnormal_ties_up": ("if (r > 0.5 || (r == 0.5 && (ki & 1))) ki += 1;",
+                               "if (r >= 0.5) ki += 1;"),
+    "e4m3_zero_sign_dropped": ("const uint8_t sign = signbit(y) ? 0x80 : 0x00;",
+                               "const uint8_t sign = (y < 0.0f) ? 0x80 : 0x00;"),
+    "fp8_ue8m0_floor_rule": ("uint32_t b = f2u(s);\n        int e = (int)(b >> 23) + ((b & 0x7FFFFFu) != 0u ? 1 : 0);",
+                             "uint32_t b = f2u(s);\n        int e = (int)(b >> 23);"),
+    "fp8_fold_without_weights_scale": ("f32_to_bf16_bits(w * weights_scale);",
+                                       "f32_to_bf16_bits(w + 0.0f * weights_scale);"),
+    "fp8_fold_truncates": ("f32_to_bf16_bits(w * weights_scale);",
+                           "(uint16_t)(f2u(w * weights_scale) >> 16);"),
+    "fp8_multiplies_by_scale": ("codes[i] = e4m3_code(x[i] / s);", "codes[i] = e4m3_code(x[i] * s);"),
+    "fp8_key_scale_misplaced": ("kv_cache_scale[slot] = quantize_row_fp8(",
+                                "kv_cache_scale[slot ^ 1] = quantize_row_fp8("),
+    "fp8_floor_ignored": ("if (s < scale_floor) s = scale_floor;", "if (0) s = scale_floor;"),
     "sglang_query_heads_shifted": ("q_packed + (t * H + h) * SLOT68", "q_packed + (t * H + (h ^ 1)) * SLOT68"),
 }
 
