@@ -31,6 +31,7 @@ HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "pack_token_amd", "csrc", "fp4idx_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qk_kernel_large_prefill_traffic.json")
 SGLANG_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q_sglang_kernel_sglang_prefill_traffic.json")
+FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q_fp8_kernel_fp8_prefill_traffic.json")
 
 
 def q_bytes_per_token(H: int) -> int:
@@ -104,6 +105,108 @@ def cpu_baseline(wl, n_tokens: int, threads: int):
 
 
 FP4_MFMA_PEAK_TFLOPS = 10100.0
+
+
+def fp8_q_bytes_per_token(H: int) -> int:
+    return 256 * H + 4 * H + 8 + 256 + 128 * H + 2 * H
+
+
+def fp8_k_bytes_per_token() -> int:
+    return 256 + 8 + 128 + 4
+
+
+def bench_fp8(args, dev):
+    """FP8 output mode over the large-prefill input (T = 131072, H = 64, neox,
+    dims 64..127 rotated, contiguous slots): one step = fp4idx_q_rope_pack_fp8 +
+    fp4idx_k_rope_pack_store_fp8 with ue8m0 scales; the same step with fp32
+    scales is timed beside it.  Algorithmic bytes per token: query launch
+    256H + 4H + 8 + 256 + 128H + 2H, key launch 256 + 8 + 128 + 4 (its position
+    and cos/sin reads repeat the query launch's)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from pack_token_amd import fp4idx, workloads
+
+    wl = workloads.large_prefill(T=args.tokens, H=args.heads)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    q, k = up(wl.q.view(np.int16)), up(wl.k.view(np.int16))
+    pos, cs, w = up(wl.positions), up(wl.cos_sin), up(wl.weights)
+    slots = up(wl.slot_mapping)
+    T, H = wl.T, wl.H
+    q_out = torch.empty((T, H, 128), dtype=torch.uint8, device=dev)
+    w_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    kv = torch.zeros((wl.NB, 64, 128), dtype=torch.uint8, device=dev)
+    ks = torch.zeros((wl.NB, 64), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run(fmt):
+        def q_call():
+            fp4idx.q_rope_pack_fp8(q, pos, cs, w, q_out=q_out, weights_out=w_out, scale_fmt=fmt,
+                                   stream=stream)
+
+        def k_call():
+            fp4idx.k_rope_pack_store_fp8(k, pos, cs, slots, kv, ks, scale_fmt=fmt, stream=stream)
+
+        for _ in range(args.warmup):
+            q_call()
+            k_call()
+        torch.cuda.synchronize()
+        K = args.steps
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(K):
+            ev[i][0].record(stream)
+            q_call()
+            ev[i][1].record(stream)
+            k_call()
+            ev[i][2].record(stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return (t0.elapsed_time(t1) / K,
+                float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
+                float(np.mean([e[1].elapsed_time(e[2]) for e in ev])))
+
+    ms, q_ms, k_ms = run("ue8m0")
+    ms32, q_ms32, k_ms32 = run("fp32")
+    qb = fp8_q_bytes_per_token(H) * T
+    kb = fp8_k_bytes_per_token() * T
+    q_gbs = qb / (q_ms * 1e-3) / 1e9
+    rec = {
+        "metric": "tokens/s and achieved HBM GB/s, FP8 (e4m3fn) q+k RoPE/quant + paged store",
+        "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16->e4m3fn", "data": "synthetic",
+        "config": {"workload": "fp8_prefill", "tokens": T, "heads": H, "head_dim": 128,
+                   "rope_dim": 64, "rope": "neox", "rope_offset": 64, "scale_fmt": "ue8m0",
+                   "kv_blocks": wl.NB, "kv_block_size": 64, "slot_mapping": "contiguous",
+                   "step": "fp4idx_q_rope_pack_fp8 + fp4idx_k_rope_pack_store_fp8"},
+        "step_GBps": (qb + kb) / (ms * 1e-3) / 1e9,
+        "q_kernel_us": q_ms * 1e3, "k_kernel_us": k_ms * 1e3,
+        "fp32_scales": {"ms_per_step": ms32, "tokens_per_s": T / (ms32 * 1e-3),
+                        "q_kernel_us": q_ms32 * 1e3, "k_kernel_us": k_ms32 * 1e3,
+                        "q_kernel_GBps": qb / (q_ms32 * 1e-3) / 1e9},
+        "roofline": {"kernel": "q_fp8_kernel<neox,ue8m0>", "bound": "hbm", "achieved": q_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": q_gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(FP8_TRAFFIC_FILE) if (T, H) == (131072, 64)
+                     else None,
+                     "algorithmic_bytes_per_launch": qb, "launch_us": q_ms * 1e3},
+    }
+    if not args.no_cpu_baseline:
+        n = min(args.cpu_sample_tokens, T, 16384)
+        c0 = time.perf_counter()
+        oracle.q_rope_pack_fp8(wl.q[:n], wl.positions[:n], wl.cos_sin, wl.weights[:n])
+        rkv = np.zeros((wl.NB, 64, 128), np.uint8)
+        rks = np.zeros((wl.NB, 64), np.float32)
+        oracle.k_rope_pack_store_fp8(wl.k[:n], wl.positions[:n], wl.cos_sin, wl.slot_mapping[:n],
+                                     rkv, rks)
+        dt = time.perf_counter() - c0
+        rec["cpu_baseline"] = {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"first {n} of {T} tokens (query + key, ue8m0), "
+                                         f"1 thread, {dt:.2f} s wall"}
+    print(json.dumps(rec), flush=True)
 
 
 def sglang_q_bytes_per_token(H: int) -> int:
@@ -274,11 +377,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large_prefill",
                     choices=["large_prefill", "prefill_norm_rotate", "decode", "decode_scoring",
-                             "sglang_prefill"],
+                             "sglang_prefill", "fp8_prefill"],
                     help="large_prefill is the headline configuration; the other two are timed "
                          "for reference")
-    ap.add_argument("--tokens", type=int, default=131072, help="large_prefill and sglang_prefill")
-    ap.add_argument("--heads", type=int, default=64, help="large_prefill and sglang_prefill")
+    ap.add_argument("--tokens", type=int, default=131072,
+                    help="large_prefill, sglang_prefill and fp8_prefill")
+    ap.add_argument("--heads", type=int, default=64,
+                    help="large_prefill, sglang_prefill and fp8_prefill")
     ap.add_argument("--cpu-sample-tokens", type=int, default=131072)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
@@ -329,6 +434,9 @@ def main():
         return
     if args.workload == "sglang_prefill":
         bench_sglang(args, dev)
+        return
+    if args.workload == "fp8_prefill":
+        bench_fp8(args, dev)
         return
     if args.workload == "large_prefill":
         wl = workloads.large_prefill(T=args.tokens, H=args.heads)

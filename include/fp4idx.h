@@ -76,6 +76,10 @@ extern "C" {
 #define FP4IDX_EUNSUPPORTED 2
 #define FP4IDX_EHIP 3
 
+/* FP8 scale formats */
+#define FP4IDX_SCALE_UE8M0 0
+#define FP4IDX_SCALE_FP32 1
+
 /*
  * fp4idx_q_rope_pack -- query side of the producer (ROCm/aiter PR 5484 "API":
  * q_out u8 [num_tokens, n_heads, head_dim/2], q_scale_out u8
@@ -210,6 +214,57 @@ int fp4idx_k_rope_pack_store_sglang(const void* k, const void* positions, int po
                                     int group_size, int is_neox, float fake_quant_floor,
                                     float pack_floor, uint8_t* index_k_cache, int64_t num_slots,
                                     void* stream);
+
+/*
+ * fp4idx_q_rope_pack_fp8 / fp4idx_k_rope_pack_store_fp8 -- the FP8 output
+ * mode of the same producer (ROCm/aiter PR 5484 "API": the FP8 contract folds
+ * its per-(token, head) q scale, and weights_scale, into weights_out of
+ * dtype q.dtype; scale_fmt ue8m0 or fp32.  ROCm/aiter PR 4029 review: the
+ * gfx950 FP8 format is e4m3fn, largest value 448).  The rotation, key
+ * RMSNorm and optional Hadamard are those of the FP4 calls above; then each
+ * 128-row (a query head, a key token) gets one scale
+ *     s = max(amax / 448, scale_floor)                  (fp32, scale_fmt = 1)
+ *     s = 2^(E - 127), E = clamp(E(amax / 448 floored), 1, 254)   (ue8m0 = 0)
+ * with E() the block-exponent rule above, and every element the e4m3fn code
+ * nearest to x / s (x / s rounded to fp32 first; ties to even; the sign kept
+ * on zero; codes 0x7F/0xFF never produced).  The preshuffled cache layout
+ * is not provided.
+ *
+ * fp4idx_q_rope_pack_fp8
+ *   q, positions, positions_int64, cos_sin, max_pos, T, H, D, R,
+ *   rope_offset, is_neox, apply_hadamard: as for fp4idx_q_rope_pack.
+ *   weights      fp32 [T, H], 4-byte aligned (required: it carries the scale).
+ *   weights_scale finite fp32 scalar.
+ *   scale_fmt    FP4IDX_SCALE_UE8M0 or FP4IDX_SCALE_FP32.
+ *   scale_floor  >= 0; >= 2^-126 with fp32 scales.
+ *   q_out        e4m3fn [T, H, 128] (bytes), 16-byte aligned.
+ *   weights_out  bf16 [T, H], 2-byte aligned:
+ *                bf16((weights[t,h] * s_{t,h}) * weights_scale), round to
+ *                nearest even, products rounded separately.
+ *
+ * fp4idx_k_rope_pack_store_fp8
+ *   k, positions, positions_int64, cos_sin, max_pos, slot_mapping,
+ *   k_norm_gamma, k_norm_eps, T, D, R, rope_offset, is_neox,
+ *   apply_hadamard, NB, BS: as for fp4idx_k_rope_pack_store; scale_fmt and
+ *   scale_floor as above.
+ *   kv_cache       e4m3fn [NB, 64, 128], 16-byte aligned: row slot = the
+ *                  token's 128 codes.
+ *   kv_cache_scale fp32 [NB, 64], 4-byte aligned: [slot] = the token's s.
+ *   A slot outside [0, NB*64) writes nothing.
+ */
+int fp4idx_q_rope_pack_fp8(const void* q, const void* positions, int positions_int64,
+                           const float* cos_sin, int64_t max_pos, const float* weights,
+                           float weights_scale, int64_t T, int H, int D, int R, int rope_offset,
+                           int is_neox, int apply_hadamard, int scale_fmt, float scale_floor,
+                           uint8_t* q_out, uint16_t* weights_out, void* stream);
+
+int fp4idx_k_rope_pack_store_fp8(const void* k, const void* positions, int positions_int64,
+                                 const float* cos_sin, int64_t max_pos,
+                                 const int64_t* slot_mapping, const void* k_norm_gamma,
+                                 float k_norm_eps, int64_t T, int D, int R, int rope_offset,
+                                 int is_neox, int apply_hadamard, int scale_fmt,
+                                 float scale_floor, uint8_t* kv_cache, float* kv_cache_scale,
+                                 int64_t NB, int BS, void* stream);
 
 /*
  * fp4idx_dequant_debug -- reader side, for tests and debugging: expands

@@ -92,6 +92,18 @@ int check_floor(const char* fn, const char* name, float v) {
     return FP4IDX_OK;
 }
 
+// FP8 scale format; an fp32 scale must stay a normal number (its reciprocal
+// is taken), so that format needs scale_floor >= 2^-126.
+int check_fp8_scale(const char* fn, int scale_fmt, float scale_floor) {
+    if (scale_fmt != FP4IDX_SCALE_UE8M0 && scale_fmt != FP4IDX_SCALE_FP32)
+        return fail(FP4IDX_EINVAL, "%s: scale_fmt must be 0 (ue8m0) or 1 (fp32) (got %d)", fn,
+                    scale_fmt);
+    if (scale_fmt == FP4IDX_SCALE_FP32 && !(scale_floor >= 1.17549435e-38f))
+        return fail(FP4IDX_EINVAL, "%s: scale_floor must be >= 2^-126 with fp32 scales (got %g)",
+                    fn, (double)scale_floor);
+    return FP4IDX_OK;
+}
+
 int check_ptr(const char* fn, const char* name, const void* p, uintptr_t align) {
     if (p == nullptr) return fail(FP4IDX_EINVAL, "%s: %s must not be NULL", fn, name);
     if (!aligned(p, align))
@@ -349,6 +361,103 @@ int fp4idx_k_rope_pack_store_sglang(const void* k, const void* positions, int po
     a.e_lo2 = floor_exponent(pack_floor);
     hipError_t err = fp4idx::launch_k_rope_pack_store_sglang(a, is_neox != 0,
                                                              static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(fn, err);
+    return FP4IDX_OK;
+}
+
+int fp4idx_q_rope_pack_fp8(const void* q, const void* positions, int positions_int64,
+                           const float* cos_sin, int64_t max_pos, const float* weights,
+                           float weights_scale, int64_t T, int H, int D, int R, int rope_offset,
+                           int is_neox, int apply_hadamard, int scale_fmt, float scale_floor,
+                           uint8_t* q_out, uint16_t* weights_out, void* stream) {
+    static const char* fn = "fp4idx_q_rope_pack_fp8";
+    FP4IDX_TRY(check_common(fn, D, R, kGroup, rope_offset, positions_int64, is_neox,
+                            apply_hadamard, scale_floor, T, max_pos));
+    FP4IDX_TRY(check_fp8_scale(fn, scale_fmt, scale_floor));
+    if (!std::isfinite(weights_scale))
+        return fail(FP4IDX_EINVAL, "%s: weights_scale must be finite", fn);
+    if (H <= 0 || H % 16 != 0 || H > kMaxHeads)
+        return fail(FP4IDX_EUNSUPPORTED,
+                    "%s: n_heads H must be a positive multiple of 16 and <= %d (got %d)", fn,
+                    kMaxHeads, H);
+    if (T > INT64_MAX / ((int64_t)H * kHeadDim * 2))
+        return fail(FP4IDX_EINVAL, "%s: T too large (%lld)", fn, (long long)T);
+    if (T == 0) return FP4IDX_OK;
+    FP4IDX_TRY(check_ptr(fn, "q", q, 16));
+    FP4IDX_TRY(check_ptr(fn, "positions", positions, positions_int64 ? 8 : 4));
+    FP4IDX_TRY(check_ptr(fn, "cos_sin", cos_sin, 16));
+    FP4IDX_TRY(check_ptr(fn, "weights", weights, 4));
+    FP4IDX_TRY(check_ptr(fn, "q_out", q_out, 16));
+    FP4IDX_TRY(check_ptr(fn, "weights_out", weights_out, 2));
+    fp4idx::FQArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.positions = positions;
+    a.cos_sin = cos_sin;
+    a.weights = weights;
+    a.q_out = q_out;
+    a.weights_out = weights_out;
+    a.T = T;
+    a.max_pos = max_pos;
+    a.H = H;
+    a.pos64 = positions_int64;
+    a.rope_offset = rope_offset;
+    a.scale_floor = scale_floor;
+    a.weights_scale = weights_scale;
+    hipError_t err = fp4idx::launch_q_rope_pack_fp8(a, is_neox != 0, apply_hadamard != 0,
+                                                    scale_fmt == FP4IDX_SCALE_FP32,
+                                                    static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(fn, err);
+    return FP4IDX_OK;
+}
+
+int fp4idx_k_rope_pack_store_fp8(const void* k, const void* positions, int positions_int64,
+                                 const float* cos_sin, int64_t max_pos,
+                                 const int64_t* slot_mapping, const void* k_norm_gamma,
+                                 float k_norm_eps, int64_t T, int D, int R, int rope_offset,
+                                 int is_neox, int apply_hadamard, int scale_fmt,
+                                 float scale_floor, uint8_t* kv_cache, float* kv_cache_scale,
+                                 int64_t NB, int BS, void* stream) {
+    static const char* fn = "fp4idx_k_rope_pack_store_fp8";
+    FP4IDX_TRY(check_common(fn, D, R, kGroup, rope_offset, positions_int64, is_neox,
+                            apply_hadamard, scale_floor, T, max_pos));
+    FP4IDX_TRY(check_fp8_scale(fn, scale_fmt, scale_floor));
+    if (BS != kKvBlock)
+        return fail(FP4IDX_EUNSUPPORTED, "%s: kv_block_size BS must be 64 (got %d)", fn, BS);
+    if (NB < 0 || NB > INT64_MAX / ((int64_t)kKvBlock * kHeadDim))
+        return fail(FP4IDX_EINVAL, "%s: NB out of range (%lld)", fn, (long long)NB);
+    if (k_norm_gamma != nullptr && (!std::isfinite(k_norm_eps) || k_norm_eps < 0.0f))
+        return fail(FP4IDX_EINVAL, "%s: k_norm_eps must be finite and >= 0 (got %g)", fn,
+                    (double)k_norm_eps);
+    if (T > INT64_MAX / (kHeadDim * 2))
+        return fail(FP4IDX_EINVAL, "%s: T too large (%lld)", fn, (long long)T);
+    if (T == 0) return FP4IDX_OK;
+    FP4IDX_TRY(check_ptr(fn, "k", k, 16));
+    FP4IDX_TRY(check_ptr(fn, "positions", positions, positions_int64 ? 8 : 4));
+    FP4IDX_TRY(check_ptr(fn, "cos_sin", cos_sin, 16));
+    FP4IDX_TRY(check_ptr(fn, "slot_mapping", slot_mapping, 8));
+    if (k_norm_gamma != nullptr) FP4IDX_TRY(check_ptr(fn, "k_norm_gamma", k_norm_gamma, 16));
+    if (NB > 0) {
+        FP4IDX_TRY(check_ptr(fn, "kv_cache", kv_cache, 16));
+        FP4IDX_TRY(check_ptr(fn, "kv_cache_scale", kv_cache_scale, 4));
+    }
+    fp4idx::FKArgs a{};
+    a.k = static_cast<const uint16_t*>(k);
+    a.positions = positions;
+    a.cos_sin = cos_sin;
+    a.slot_mapping = slot_mapping;
+    a.gamma = static_cast<const uint16_t*>(k_norm_gamma);
+    a.kv_cache = kv_cache;
+    a.kv_cache_scale = kv_cache_scale;
+    a.T = T;
+    a.max_pos = max_pos;
+    a.nslots = NB * kKvBlock;
+    a.eps = k_norm_eps;
+    a.pos64 = positions_int64;
+    a.rope_offset = rope_offset;
+    a.scale_floor = scale_floor;
+    hipError_t err = fp4idx::launch_k_rope_pack_store_fp8(a, is_neox != 0, apply_hadamard != 0,
+                                                          scale_fmt == FP4IDX_SCALE_FP32,
+                                                          static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return hip_fail(fn, err);
     return FP4IDX_OK;
 }

@@ -89,6 +89,40 @@ struct SKArgs {
     int e_lo2;
 };
 
+// FP8 output mode: one e4m3fn scale per 128-row.
+struct FQArgs {
+    const uint16_t* q;          // bf16 [T, H, 128]
+    const void* positions;
+    const float* cos_sin;
+    const float* weights;       // fp32 [T, H]
+    uint8_t* q_out;             // e4m3fn [T, H, 128]
+    uint16_t* weights_out;      // bf16 [T, H]: (weights * s) * weights_scale
+    int64_t T;
+    int64_t max_pos;
+    int H;
+    int pos64;
+    int rope_offset;
+    float scale_floor;
+    float weights_scale;
+};
+
+struct FKArgs {
+    const uint16_t* k;          // bf16 [T, 128]
+    const void* positions;
+    const float* cos_sin;
+    const int64_t* slot_mapping;  // [T]
+    const uint16_t* gamma;      // bf16 [128] or nullptr
+    uint8_t* kv_cache;          // e4m3fn [NB, 64, 128]
+    float* kv_cache_scale;      // fp32 [NB, 64]
+    int64_t T;
+    int64_t max_pos;
+    int64_t nslots;             // NB * 64
+    float eps;
+    int pos64;
+    int rope_offset;
+    float scale_floor;
+};
+
 // FP4 paged MQA logits (scorer).
 struct LArgs {
     const uint8_t* q_out;         // u8 [B*next_n, H, 64]
@@ -117,6 +151,10 @@ hipError_t launch_qk_rope_pack_store(const QArgs& qa, const KArgs& ka, bool is_n
                                      hipStream_t stream);
 hipError_t launch_q_rope_pack_sglang(const SQArgs& a, bool is_neox, hipStream_t stream);
 hipError_t launch_k_rope_pack_store_sglang(const SKArgs& a, bool is_neox, hipStream_t stream);
+hipError_t launch_q_rope_pack_fp8(const FQArgs& a, bool is_neox, bool hadamard, bool fp32_scale,
+                                  hipStream_t stream);
+hipError_t launch_k_rope_pack_store_fp8(const FKArgs& a, bool is_neox, bool hadamard,
+                                        bool fp32_scale, hipStream_t stream);
 hipError_t launch_dequant(const DArgs& a, hipStream_t stream);
 hipError_t launch_paged_mqa_logits(const LArgs& a, hipStream_t stream);
 

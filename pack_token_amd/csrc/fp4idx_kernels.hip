@@ -35,6 +35,7 @@ namespace {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x2_t __attribute__((ext_vector_type(2)));
 
 // DPP lane patterns (CDNA data-parallel primitives).
 constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]: lane i <- i ^ 1
@@ -77,6 +78,7 @@ __device__ __forceinline__ uint4 load16(const void* p) {
 // ~5.4 to ~6.5 TB/s.  The small per-token rows (weights, scales) and the key
 // cache writes keep the default policy, which measured faster for them.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint4 load16_stream(const void* p) {
     const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
@@ -698,6 +700,146 @@ __global__ __launch_bounds__(kBlock) void k_sglang_kernel(SKArgs a) {
     if (lane16 == 0) *reinterpret_cast<uint32_t*>(rec + 64) = x;
 }
 
+// ---- FP8 output mode ----------------------------------------------------------
+// (ROCm/aiter PR 5484 "API": the FP8 contract of the same op, with its
+// per-(token, head) q scale folded into weights_out together with
+// weights_scale; scale_fmt ue8m0 or fp32.  ROCm/aiter PR 4029 review: e4m3fn,
+// largest value 448, on gfx950.)  One scale per 128-row (a query head, a key
+// token): s = max(amax / 448, floor), raised to a power of two under ue8m0;
+// codes are the e4m3fn values nearest to x / s, ties to even, sign kept on
+// zero.  A row is the 16 lanes of a DPP row (lane chunk c = chunk_of(lane16)),
+// so its amax takes four DPP steps.
+//
+// ue8m0: the scaled converter divides by the power-of-two scale exactly.
+// fp32: x / s rounded to fp32 first (the value the converter then rounds),
+// computed as y0 = x * r, y = fma(fma(-y0, s, x), r, y0) with r = RN(1/s);
+// for every bf16 x and normal fp32 s this equals RN(x / s) -- checked
+// exhaustively over all 2^31 significand pairs on the CPU.
+__device__ __forceinline__ void store8_stream(void* p, uint2 v) {
+    const u32x2_t w = {v.x, v.y};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(p));
+}
+
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+    return pack_bf16x2(x, 0.0f) & 0xFFFFu;
+}
+
+template <bool FP32>
+__device__ __forceinline__ uint2 quant_fp8_row(uint4 v, float scale_floor, float& s_out) {
+    const u16x2_t a0 = __builtin_bit_cast(u16x2_t, v.x & 0x7FFF7FFFu);
+    const u16x2_t a1 = __builtin_bit_cast(u16x2_t, v.y & 0x7FFF7FFFu);
+    const u16x2_t a2 = __builtin_bit_cast(u16x2_t, v.z & 0x7FFF7FFFu);
+    const u16x2_t a3 = __builtin_bit_cast(u16x2_t, v.w & 0x7FFF7FFFu);
+    const u16x2_t m2 = __builtin_elementwise_max(__builtin_elementwise_max(a0, a1),
+                                                 __builtin_elementwise_max(a2, a3));
+    uint32_t m = max((uint32_t)m2.x, (uint32_t)m2.y);
+    m = max(m, dpp<kDppXor1>(m));
+    m = max(m, dpp<kDppXor2>(m));
+    m = max(m, dpp<kDppHalfMirror>(m));
+    m = max(m, dpp<kDppRor8>(m));
+    float s = __uint_as_float(m << 16) / 448.0f;
+    s = s < scale_floor ? scale_floor : s;
+    s16x2_t lo = {0, 0}, hi = {0, 0};
+    if (!FP32) {
+        const uint32_t b = __float_as_uint(s);
+        const int e = min(max((int)(b >> 23) + ((b & 0x7FFFFFu) != 0u ? 1 : 0), 1), 254);
+        s = __uint_as_float((uint32_t)e << 23);
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, __builtin_bit_cast(bf16x2_t, v.x), s, false);
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, __builtin_bit_cast(bf16x2_t, v.y), s, true);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, __builtin_bit_cast(bf16x2_t, v.z), s, false);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, __builtin_bit_cast(bf16x2_t, v.w), s, true);
+    } else {
+        const float r = rcp_rn(s);
+        float x[8], y[8];
+        unpack8(v, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float y0 = x[e] * r;
+            const float err = __builtin_fmaf(-y0, s, x[e]);
+            // s > 0, so the quotient has the sign of x; the correction alone
+            // would turn -0 into +0
+            y[e] = __builtin_copysignf(__builtin_fmaf(err, r, y0), x[e]);
+        }
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, y[0], y[1], 1.0f, false);
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, y[2], y[3], 1.0f, true);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, y[4], y[5], 1.0f, false);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, y[6], y[7], 1.0f, true);
+    }
+    s_out = s;
+    return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+
+// Query: one token per wavefront, 16 lanes per head, 8 heads per step (two
+// 16-byte loads per lane).  q_out rows are 128 bytes, written by the 16
+// lanes of the head with 8-byte streaming stores; lane 0 of each head writes
+// the folded weight.
+template <bool NEOX, bool HAD, bool FP32>
+__global__ __launch_bounds__(kBlock) void q_fp8_kernel(FQArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    if (t >= a.T) return;
+    const int H = a.H;
+    const int c = chunk_of(lane & 15);
+    const int hsub = lane >> 4;
+    const bool rot_lane = (c >> 3) == (a.rope_offset >> 6);
+    const int64_t pos = clamped_position(a.positions, a.pos64, t, a.max_pos);
+    float C[8], S[8];
+    rope_coeffs<NEOX>(a.cos_sin + pos * 64, c & 7, C, S);
+    const uint16_t* qt = a.q + t * (int64_t)H * 128 + hsub * 128 + 8 * c;
+    uint8_t* ot = a.q_out + t * (int64_t)H * 128 + hsub * 128 + 8 * c;
+    const float* wt = a.weights + t * H;
+    uint16_t* wo = a.weights_out + t * H;
+    for (int hb = 0; hb < H; hb += 8) {
+        const uint4 v0 = load16_stream(qt + hb * 128);
+        const uint4 v1 = load16_stream(qt + (hb + 4) * 128);
+        uint4 w0 = select4(rot_lane, rope8<NEOX>(v0, C, S), v0);
+        uint4 w1 = select4(rot_lane, rope8<NEOX>(v1, C, S), v1);
+        if (HAD) {
+            w0 = hadamard8(w0, c);
+            w1 = hadamard8(w1, c);
+        }
+        float s0, s1;
+        const uint2 q0 = quant_fp8_row<FP32>(w0, a.scale_floor, s0);
+        const uint2 q1 = quant_fp8_row<FP32>(w1, a.scale_floor, s1);
+        store8_stream(ot + hb * 128, q0);
+        store8_stream(ot + (hb + 4) * 128, q1);
+        if ((lane & 15) == 0) {
+            const int h0 = hb + hsub, h1 = h0 + 4;
+            wo[h0] = (uint16_t)bf16_bits((wt[h0] * s0) * a.weights_scale);
+            wo[h1] = (uint16_t)bf16_bits((wt[h1] * s1) * a.weights_scale);
+        }
+    }
+}
+
+// Key: 16 lanes per row as k_row_kernel; the row's 128 code bytes go to
+// kv_cache[slot] and its scale to kv_cache_scale[slot].
+template <bool NEOX, bool NORM, bool HAD, bool FP32>
+__global__ __launch_bounds__(kBlock) void k_fp8_kernel(FKArgs a) {
+    const int lane16 = threadIdx.x & 15;
+    const int64_t t = (int64_t)blockIdx.x * (kBlock / 16) + (threadIdx.x >> 4);
+    if (t >= a.T) return;
+    const int c = chunk_of(lane16);
+    uint4 v = load16_stream(a.k + t * 128 + 8 * c);
+    const int64_t slot = a.slot_mapping[t];
+    const int64_t pos = clamped_position(a.positions, a.pos64, t, a.max_pos);
+    float C[8], S[8];
+    rope_coeffs<NEOX>(a.cos_sin + pos * 64, c & 7, C, S);
+    if (slot < 0 || slot >= a.nslots) return;
+    if (NORM) {
+        float G[8];
+        unpack8(load16(a.gamma + 8 * c), G);
+        v = rmsnorm8(v, G, a.eps);
+    }
+    const bool rot_lane = (c >> 3) == (a.rope_offset >> 6);
+    v = select4(rot_lane, rope8<NEOX>(v, C, S), v);
+    if (HAD) v = hadamard8(v, c);
+    float s;
+    const uint2 q = quant_fp8_row<FP32>(v, a.scale_floor, s);
+    *reinterpret_cast<uint2*>(a.kv_cache + slot * 128 + 8 * c) = q;
+    if (lane16 == 0) a.kv_cache_scale[slot] = s;
+}
+
 // ---- dequantization (debug reader) -------------------------------------------
 // One thread per 8 consecutive values (4 code bytes).
 __device__ __forceinline__ float e2m1_value(uint32_t nib) {
@@ -833,6 +975,45 @@ hipError_t launch_k_rope_pack_store_sglang(const SKArgs& a, bool is_neox, hipStr
                     : launch(k_sglang_kernel<true, false>, blocks, 0, stream, a);
     return norm ? launch(k_sglang_kernel<false, true>, blocks, 0, stream, a)
                 : launch(k_sglang_kernel<false, false>, blocks, 0, stream, a);
+}
+
+hipError_t launch_q_rope_pack_fp8(const FQArgs& a, bool is_neox, bool hadamard, bool fp32_scale,
+                                  hipStream_t stream) {
+    if (a.T == 0) return hipSuccess;
+    const int64_t blocks = (a.T + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int sel = (is_neox ? 4 : 0) | (hadamard ? 2 : 0) | (fp32_scale ? 1 : 0);
+    switch (sel) {
+        case 0: return launch(q_fp8_kernel<false, false, false>, blocks, 0, stream, a);
+        case 1: return launch(q_fp8_kernel<false, false, true>, blocks, 0, stream, a);
+        case 2: return launch(q_fp8_kernel<false, true, false>, blocks, 0, stream, a);
+        case 3: return launch(q_fp8_kernel<false, true, true>, blocks, 0, stream, a);
+        case 4: return launch(q_fp8_kernel<true, false, false>, blocks, 0, stream, a);
+        case 5: return launch(q_fp8_kernel<true, false, true>, blocks, 0, stream, a);
+        case 6: return launch(q_fp8_kernel<true, true, false>, blocks, 0, stream, a);
+        default: return launch(q_fp8_kernel<true, true, true>, blocks, 0, stream, a);
+    }
+}
+
+template <bool NEOX, bool NORM>
+hipError_t launch_k_fp8(const FKArgs& a, bool hadamard, bool fp32_scale, int64_t blocks,
+                        hipStream_t stream) {
+    if (hadamard)
+        return fp32_scale ? launch(k_fp8_kernel<NEOX, NORM, true, true>, blocks, 0, stream, a)
+                          : launch(k_fp8_kernel<NEOX, NORM, true, false>, blocks, 0, stream, a);
+    return fp32_scale ? launch(k_fp8_kernel<NEOX, NORM, false, true>, blocks, 0, stream, a)
+                      : launch(k_fp8_kernel<NEOX, NORM, false, false>, blocks, 0, stream, a);
+}
+
+hipError_t launch_k_rope_pack_store_fp8(const FKArgs& a, bool is_neox, bool hadamard,
+                                        bool fp32_scale, hipStream_t stream) {
+    if (a.T == 0) return hipSuccess;
+    const int64_t blocks = (a.T + kBlock / 16 - 1) / (kBlock / 16);
+    const bool norm = a.gamma != nullptr;
+    if (is_neox)
+        return norm ? launch_k_fp8<true, true>(a, hadamard, fp32_scale, blocks, stream)
+                    : launch_k_fp8<true, false>(a, hadamard, fp32_scale, blocks, stream);
+    return norm ? launch_k_fp8<false, true>(a, hadamard, fp32_scale, blocks, stream)
+                : launch_k_fp8<false, false>(a, hadamard, fp32_scale, blocks, stream);
 }
 
 hipError_t launch_dequant(const DArgs& a, hipStream_t stream) {

@@ -65,6 +65,13 @@ def lib():
                                                           _i, _i, _i, _i, _i, _f, _f, _p, _i64,
                                                           _p]
             L.fp4idx_k_rope_pack_store_sglang.restype = _i
+            L.fp4idx_q_rope_pack_fp8.argtypes = [_p, _p, _i, _p, _i64, _p, _f, _i64, _i, _i, _i, _i,
+                                                 _i, _i, _i, _f, _p, _p, _p]
+            L.fp4idx_q_rope_pack_fp8.restype = _i
+            L.fp4idx_k_rope_pack_store_fp8.argtypes = [_p, _p, _i, _p, _i64, _p, _p, _f, _i64, _i,
+                                                       _i, _i, _i, _i, _i, _f, _p, _p, _i64, _i,
+                                                       _p]
+            L.fp4idx_k_rope_pack_store_fp8.restype = _i
             L.fp4idx_paged_mqa_logits.argtypes = [_p, _p, _p, _f, _p, _p, _i64, _p, _i64, _p,
                                                   _i64, _i, _i, _i, _p, _i64, _p]
             L.fp4idx_paged_mqa_logits.restype = _i
@@ -165,6 +172,64 @@ def k_rope_pack_store(k, positions, cos_sin, slot_mapping, kv_cache, kv_cache_sc
         cos_sin.shape[0], _ptr(slot_mapping), _ptr(k_norm_gamma), k_norm_eps, T, D, ROPE_DIM,
         rope_offset, GROUP, int(is_neox), int(apply_hadamard), scale_floor, _ptr(kv_cache),
         _ptr(kv_cache_scale), NB, KV_BLOCK, _stream_handle(stream))
+    _check(rc)
+    return kv_cache, kv_cache_scale
+
+
+SCALE_UE8M0, SCALE_FP32 = 0, 1
+
+
+def _scale_fmt(fmt):
+    return {"ue8m0": SCALE_UE8M0, "fp32": SCALE_FP32}.get(fmt, fmt)
+
+
+def q_rope_pack_fp8(q, positions, cos_sin, weights, *, weights_scale=1.0, q_out=None,
+                    weights_out=None, is_neox=True, rope_offset=64, apply_hadamard=False,
+                    scale_fmt="ue8m0", scale_floor=DEFAULT_SCALE_FLOOR, stream=None):
+    """fp4idx_q_rope_pack_fp8.  Returns (q_out u8 [T,H,128] holding e4m3fn codes,
+    weights_out bf16 [T,H] = (weights * q_scale) * weights_scale)."""
+    T, H, D = q.shape
+    dev = q.device
+    _require(q, "q", (torch.bfloat16, torch.int16, torch.uint16))
+    _require(positions, "positions", (torch.int32, torch.int64), dev)
+    _require(cos_sin, "cos_sin", (torch.float32,), dev)
+    _require(weights, "weights", (torch.float32,), dev)
+    if q_out is None:
+        q_out = torch.empty((T, H, D), dtype=torch.uint8, device=dev)
+    if weights_out is None:
+        weights_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _require(q_out, "q_out", (torch.uint8,), dev)
+    _require(weights_out, "weights_out", (torch.bfloat16, torch.int16, torch.uint16), dev)
+    rc = lib().fp4idx_q_rope_pack_fp8(
+        _ptr(q), _ptr(positions), int(positions.dtype == torch.int64), _ptr(cos_sin),
+        cos_sin.shape[0], _ptr(weights), weights_scale, T, H, D, ROPE_DIM, rope_offset,
+        int(is_neox), int(apply_hadamard), _scale_fmt(scale_fmt), scale_floor, _ptr(q_out),
+        _ptr(weights_out), _stream_handle(stream))
+    _check(rc)
+    return q_out, weights_out
+
+
+def k_rope_pack_store_fp8(k, positions, cos_sin, slot_mapping, kv_cache, kv_cache_scale, *,
+                          k_norm_gamma=None, k_norm_eps=1e-6, is_neox=True, rope_offset=64,
+                          apply_hadamard=False, scale_fmt="ue8m0", scale_floor=DEFAULT_SCALE_FLOOR,
+                          stream=None):
+    """fp4idx_k_rope_pack_store_fp8.  kv_cache u8 [NB,64,128] (e4m3fn codes) and
+    kv_cache_scale fp32 [NB,64] are updated in place."""
+    T, D = k.shape
+    dev = k.device
+    _require(k, "k", (torch.bfloat16, torch.int16, torch.uint16))
+    _require(positions, "positions", (torch.int32, torch.int64), dev)
+    _require(cos_sin, "cos_sin", (torch.float32,), dev)
+    _require(slot_mapping, "slot_mapping", (torch.int64,), dev)
+    _require(kv_cache, "kv_cache", (torch.uint8,), dev)
+    _require(kv_cache_scale, "kv_cache_scale", (torch.float32,), dev)
+    _require(k_norm_gamma, "k_norm_gamma", (torch.bfloat16, torch.int16, torch.uint16), dev)
+    rc = lib().fp4idx_k_rope_pack_store_fp8(
+        _ptr(k), _ptr(positions), int(positions.dtype == torch.int64), _ptr(cos_sin),
+        cos_sin.shape[0], _ptr(slot_mapping), _ptr(k_norm_gamma), k_norm_eps, T, D, ROPE_DIM,
+        rope_offset, int(is_neox), int(apply_hadamard), _scale_fmt(scale_fmt), scale_floor,
+        _ptr(kv_cache), _ptr(kv_cache_scale), kv_cache.shape[0], KV_BLOCK,
+        _stream_handle(stream))
     _check(rc)
     return kv_cache, kv_cache_scale
 

@@ -26,8 +26,9 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert names == ["fp4idx_dequant_debug", "fp4idx_k_rope_pack_store",
-                     "fp4idx_k_rope_pack_store_sglang", "fp4idx_last_error",
-                     "fp4idx_paged_mqa_logits", "fp4idx_q_rope_pack", "fp4idx_q_rope_pack_sglang",
+                     "fp4idx_k_rope_pack_store_fp8", "fp4idx_k_rope_pack_store_sglang",
+                     "fp4idx_last_error", "fp4idx_paged_mqa_logits", "fp4idx_q_rope_pack",
+                     "fp4idx_q_rope_pack_fp8", "fp4idx_q_rope_pack_sglang",
                      "fp4idx_qk_rope_pack_store"]
     lib = ctypes.CDLL(fp4idx.LIB_PATH)
     for n in names:
@@ -264,6 +265,66 @@ def test_sglang_k_rejections(over, code, msg):
     assert fp4idx.last_error().startswith("fp4idx_k_rope_pack_store_sglang:")
 
 
+def fq_call(**over):
+    a = dict(q=ALIGNED, positions=ALIGNED, positions_int64=1, cos_sin=ALIGNED, max_pos=16,
+             weights=ALIGNED, weights_scale=1.0, T=4, H=32, D=128, R=64, rope_offset=64,
+             is_neox=1, apply_hadamard=0, scale_fmt=0, scale_floor=2.0 ** -126, q_out=ALIGNED,
+             weights_out=ALIGNED, stream=None)
+    a.update(over)
+    return fp4idx.lib().fp4idx_q_rope_pack_fp8(*a.values())
+
+
+def fk_call(**over):
+    a = dict(k=ALIGNED, positions=ALIGNED, positions_int64=1, cos_sin=ALIGNED, max_pos=16,
+             slot_mapping=ALIGNED, k_norm_gamma=None, k_norm_eps=1e-6, T=4, D=128, R=64,
+             rope_offset=64, is_neox=1, apply_hadamard=0, scale_fmt=1, scale_floor=2.0 ** -126,
+             kv_cache=ALIGNED, kv_cache_scale=ALIGNED, NB=2, BS=64, stream=None)
+    a.update(over)
+    return fp4idx.lib().fp4idx_k_rope_pack_store_fp8(*a.values())
+
+
+FQ_REJECT = [
+    (dict(D=64), fp4idx.EUNSUPPORTED, "head_dim"),
+    (dict(H=40), fp4idx.EUNSUPPORTED, "n_heads"),
+    (dict(scale_fmt=2), fp4idx.EINVAL, "scale_fmt"),
+    (dict(scale_fmt=1, scale_floor=0.0), fp4idx.EINVAL, "scale_floor must be >= 2^-126"),
+    (dict(scale_fmt=1, scale_floor=1e-40), fp4idx.EINVAL, "scale_floor must be >= 2^-126"),
+    (dict(scale_floor=-1.0), fp4idx.EINVAL, "scale_floor"),
+    (dict(weights_scale=float("nan")), fp4idx.EINVAL, "weights_scale"),
+    (dict(weights=None), fp4idx.EINVAL, "weights must not be NULL"),
+    (dict(weights_out=None), fp4idx.EINVAL, "weights_out must not be NULL"),
+    (dict(weights_out=ALIGNED + 1), fp4idx.EINVAL, "weights_out must be 2-byte"),
+    (dict(q_out=ALIGNED + 8), fp4idx.EINVAL, "q_out must be 16-byte"),
+    (dict(apply_hadamard=3), fp4idx.EINVAL, "apply_hadamard"),
+]
+
+
+@pytest.mark.parametrize("over,code,msg", FQ_REJECT)
+def test_fp8_q_rejections(over, code, msg):
+    assert fq_call(**over) == code
+    assert msg in fp4idx.last_error(), fp4idx.last_error()
+    assert fp4idx.last_error().startswith("fp4idx_q_rope_pack_fp8:")
+
+
+FK_REJECT = [
+    (dict(BS=32), fp4idx.EUNSUPPORTED, "kv_block_size"),
+    (dict(NB=-1), fp4idx.EINVAL, "NB out of range"),
+    (dict(scale_fmt=-1), fp4idx.EINVAL, "scale_fmt"),
+    (dict(scale_floor=0.0), fp4idx.EINVAL, "scale_floor must be >= 2^-126"),
+    (dict(kv_cache=ALIGNED + 8), fp4idx.EINVAL, "kv_cache must be 16-byte"),
+    (dict(kv_cache_scale=ALIGNED + 2), fp4idx.EINVAL, "kv_cache_scale must be 4-byte"),
+    (dict(k_norm_gamma=ALIGNED, k_norm_eps=float("inf")), fp4idx.EINVAL, "k_norm_eps"),
+    (dict(slot_mapping=None), fp4idx.EINVAL, "slot_mapping must not be NULL"),
+]
+
+
+@pytest.mark.parametrize("over,code,msg", FK_REJECT)
+def test_fp8_k_rejections(over, code, msg):
+    assert fk_call(**over) == code
+    assert msg in fp4idx.last_error(), fp4idx.last_error()
+    assert fp4idx.last_error().startswith("fp4idx_k_rope_pack_store_fp8:")
+
+
 def test_zero_tokens_is_a_noop_even_with_null_buffers():
     assert q_call(T=0, q=None, positions=None, cos_sin=None, q_out=None, q_scale_out=None) == 0
     assert k_call(T=0, k=None, positions=None, cos_sin=None, slot_mapping=None, kv_cache=None,
@@ -273,6 +334,10 @@ def test_zero_tokens_is_a_noop_even_with_null_buffers():
                    q_out=None, q_scale_out=None, kv_cache=None, kv_cache_scale=None) == 0
     assert s_call(B=0, q_out=None, logits=None, block_table=None) == 0
     assert sq_call(T=0, q=None, positions=None, cos_sin=None, q_packed=None) == 0
+    assert fq_call(T=0, q=None, positions=None, cos_sin=None, weights=None, q_out=None,
+                   weights_out=None) == 0
+    assert fk_call(T=0, k=None, positions=None, cos_sin=None, slot_mapping=None, kv_cache=None,
+                   kv_cache_scale=None) == 0
     assert sk_call(T=0, k=None, positions=None, cos_sin=None, slot_mapping=None,
                    index_k_cache=None) == 0
     # but shapes are still checked first
