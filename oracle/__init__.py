@@ -68,7 +68,13 @@ def _lib():
                                                       _i, _i, _f, _f, _p]
             lib.oracle_q_rope_pack_sglang.restype = _i
             lib.oracle_k_rope_pack_store_sglang.argtypes = [_p, _p, _i, _p, _i64, _p, _p, _f, _i64,
-                                                            _i, _i, _i, _i, _i, _f, _f, _p, _i64]
+                                                            _i, _i, _i, _i, _i, _i, _f, _f, _p,
+                                                            _i64]
+            lib.oracle_rope_fake_quant.argtypes = [_p, _i64, _i, _p, _i, _p, _i64, _i, _i, _i, _i,
+                                                   _i, _i, _f, _p]
+            lib.oracle_rope_fake_quant.restype = _i
+            lib.oracle_fake_quant_rows.argtypes = [_p, _i64, _i, _f, _p]
+            lib.oracle_fake_quant_rows.restype = None
             lib.oracle_k_rope_pack_store_sglang.restype = _i
             lib.oracle_quantize_rows_two_stage.argtypes = [_p, _i64, _f, _f, _p]
             lib.oracle_quantize_rows_two_stage.restype = None
@@ -272,7 +278,8 @@ def q_rope_pack_sglang(q_bits, positions, cos_sin, *, is_neox=True, rope_offset=
 
 def k_rope_pack_store_sglang(k_bits, positions, cos_sin, slot_mapping, index_k_cache, *,
                              k_norm_gamma=None, k_norm_eps=1e-6, is_neox=True, rope_offset=64,
-                             fake_quant_floor=DEFAULT_SCALE_FLOOR, pack_floor=DEFAULT_SCALE_FLOOR):
+                             compress_ratio=1, fake_quant_floor=DEFAULT_SCALE_FLOOR,
+                             pack_floor=DEFAULT_SCALE_FLOOR):
     """sglang-compatible key side: writes 68-byte records into index_k_cache u8 [num_slots,68]."""
     k_bits = _c(k_bits, np.uint16)
     T, D = k_bits.shape
@@ -287,8 +294,8 @@ def k_rope_pack_store_sglang(k_bits, positions, cos_sin, slot_mapping, index_k_c
     rc = _lib().oracle_k_rope_pack_store_sglang(
         k_bits.ctypes.data, positions.ctypes.data, pos64, cos_sin.ctypes.data, cos_sin.shape[0],
         slot_mapping.ctypes.data, _ptr(gamma), k_norm_eps, T, D, ROPE_DIM, rope_offset, 32,
-        int(bool(is_neox)), fake_quant_floor, pack_floor, index_k_cache.ctypes.data,
-        index_k_cache.shape[0])
+        int(bool(is_neox)), compress_ratio, fake_quant_floor, pack_floor,
+        index_k_cache.ctypes.data, index_k_cache.shape[0])
     if rc != 0:
         raise ValueError(f"oracle_k_rope_pack_store_sglang rejected its arguments (rc={rc})")
     return index_k_cache
@@ -380,6 +387,36 @@ def quantize_rows_fp8(x, scale_floor=DEFAULT_SCALE_FLOOR, ue8m0=True):
     _lib().oracle_quantize_rows_fp8(x.ctypes.data, n, scale_floor, int(bool(ue8m0)),
                                     codes.ctypes.data, scales.ctypes.data)
     return codes, scales
+
+
+FQ_UE8M0_32, FQ_E4M3_16 = 0, 1
+
+
+def rope_fake_quant(x_bits, positions, cos_sin, *, rows_per_position=1, is_neox=True,
+                    rope_offset=64, compress_ratio=1, mode=FQ_UE8M0_32,
+                    scale_floor=DEFAULT_SCALE_FLOOR):
+    """RoPE tail + FP4 fake quant: bf16 bits [..., 128] -> bf16 bits of the same shape."""
+    x_bits = _c(x_bits, np.uint16)
+    shape = x_bits.shape
+    rows = x_bits.size // 128
+    positions, pos64 = _positions(positions)
+    cos_sin = _c(cos_sin, np.float32)
+    y = np.full(shape, 0xFFFF, np.uint16)
+    rc = _lib().oracle_rope_fake_quant(x_bits.ctypes.data, rows, rows_per_position,
+                                       positions.ctypes.data, pos64, cos_sin.ctypes.data,
+                                       cos_sin.shape[0], 128, ROPE_DIM, rope_offset,
+                                       int(bool(is_neox)), compress_ratio, mode, scale_floor,
+                                       y.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_rope_fake_quant rejected its arguments (rc={rc})")
+    return y
+
+
+def fake_quant_rows(x, mode=FQ_UE8M0_32, scale_floor=DEFAULT_SCALE_FLOOR):
+    x = _c(x, np.float32)
+    y = np.empty(x.shape, np.uint16)
+    _lib().oracle_fake_quant_rows(x.ctypes.data, x.shape[0], mode, scale_floor, y.ctypes.data)
+    return y
 
 
 # ---- step-level entry points (for the pins) ----

@@ -107,9 +107,9 @@ static int group_exponent(const float* v, int n, float scale_floor) {
 /* above 6 saturate to code 7.  Bit 3 is the sign of v, kept on zero    */
 /* codes ([aiter-5484] "One deliberate deviation").                      */
 /* ------------------------------------------------------------------ */
-static uint8_t e2m1_nibble(float v, int e) {
-    float inv = ldexpf(1.0f, 127 - e); /* exact power of two */
-    float m = fabsf(v * inv);
+/* magnitude code of m >= 0: nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to
+   the even code, anything above 6 saturating to 6 */
+static int e2m1_magnitude_code(float m) {
     int code;
     if (m <= 0.25f) code = 0;
     else if (m < 0.75f) code = 1;
@@ -119,6 +119,12 @@ static uint8_t e2m1_nibble(float v, int e) {
     else if (m < 3.5f) code = 5;
     else if (m <= 5.0f) code = 6;
     else code = 7;
+    return code;
+}
+
+static uint8_t e2m1_nibble(float v, int e) {
+    float inv = ldexpf(1.0f, 127 - e); /* exact power of two */
+    int code = e2m1_magnitude_code(fabsf(v * inv));
     int sign = signbit(v) ? 1 : 0;
     return (uint8_t)((sign << 3) | code);
 }
@@ -516,19 +522,25 @@ int oracle_q_rope_pack_sglang(const uint16_t* q, const void* positions, int posi
 }
 
 /* key side: optional RMSNorm, RoPE, two stages, 68-byte record at slot; slot 0
-   (and any slot outside [1, num_slots)) publishes nothing */
+   (and any slot outside [1, num_slots)) publishes nothing.  A compressed key
+   row stands for compress_ratio consecutive tokens and is rotated at the
+   first position of that group ([sglang-39656] Summary: "RoPE at the group's
+   first position"): pos - pos % compress_ratio. */
 int oracle_k_rope_pack_store_sglang(const uint16_t* k, const void* positions, int positions_int64,
                                     const float* cos_sin, int64_t max_pos,
                                     const int64_t* slot_mapping, const uint16_t* k_norm_gamma,
                                     float k_norm_eps, int64_t T, int D, int R, int rope_offset,
-                                    int group_size, int is_neox, float fake_quant_floor,
-                                    float pack_floor, uint8_t* index_k_cache, int64_t num_slots) {
+                                    int group_size, int is_neox, int compress_ratio,
+                                    float fake_quant_floor, float pack_floor,
+                                    uint8_t* index_k_cache, int64_t num_slots) {
     if (check_shape(D, R, rope_offset, group_size) != ORC_OK) return ORC_EINVAL;
     if (num_slots < 0 || T < 0 || max_pos <= 0) return ORC_EINVAL;
+    if (compress_ratio != 1 && compress_ratio != 2 && compress_ratio != 4) return ORC_EINVAL;
     for (int64_t t = 0; t < T; ++t) {
         int64_t slot = slot_mapping[t];
         if (slot <= 0 || slot >= num_slots) continue;
         int64_t pos = read_position(positions, positions_int64, t, max_pos);
+        pos -= pos % compress_ratio;    /* RoPE at the group's first position */
         float x[HEAD_DIM];
         for (int i = 0; i < HEAD_DIM; ++i) x[i] = bf16_to_f32(k[t * HEAD_DIM + i]);
         if (k_norm_gamma) rmsnorm128(x, k_norm_gamma, k_norm_eps);
@@ -688,4 +700,85 @@ void oracle_quantize_rows_fp8(const float* x, int64_t n, float scale_floor, int 
                               uint8_t* codes, float* scales) {
     for (int64_t r = 0; r < n; ++r)
         scales[r] = quantize_row_fp8(x + r * HEAD_DIM, scale_floor, ue8m0, codes + r * HEAD_DIM);
+}
+
+/* ------------------------------------------------------------------ */
+/* RoPE tail + FP4 fake quant ([sglang-39656] Summary: the torch-shaped */
+/* path rotates the tail, keeps the bf16 round trip, and fake-quantizes */
+/* with per-32 UE8M0 scales by default or per-16 E4M3 scales for        */
+/* compressed KV, rounding half to even).  Output: the bf16 values of   */
+/* the quantized rows (code value times scale).                         */
+/* Readings: row r uses positions[r / rows_per_position], rounded down  */
+/* to a multiple of compress_ratio; the E4M3 scale of a 16-group is the */
+/* e4m3fn value nearest to max(amax / 6, floor) (saturating at 448); a  */
+/* zero scale gives signed zeros; codes are the E2M1 values nearest to  */
+/* fl(x / s), ties to even, saturating at 6.                            */
+/* ------------------------------------------------------------------ */
+#define FQ_UE8M0_32 0
+#define FQ_E4M3_16 1
+
+static float e4m3_value(uint8_t c) {
+    const int E = (c >> 3) & 15, m = c & 7;
+    const float v = E == 0 ? ldexpf((float)m, -9) : ldexpf((float)(8 + m), E - 10);
+    return (c & 0x80) ? -v : v;
+}
+
+static void fake_quant_row(const float* x, int mode, float scale_floor, uint16_t* y) {
+    if (mode == FQ_UE8M0_32) {
+        for (int g = 0; g < NGROUPS; ++g) {
+            const float* v = x + g * GROUP;
+            const int e = group_exponent(v, GROUP, scale_floor);
+            for (int i = 0; i < GROUP; ++i) {
+                const float q = e2m1_value(e2m1_nibble(v[i], e)) * e8m0_value((uint8_t)e);
+                y[g * GROUP + i] = f32_to_bf16_bits(q);
+            }
+        }
+        return;
+    }
+    for (int g = 0; g < HEAD_DIM / 16; ++g) {
+        const float* v = x + g * 16;
+        float amax = 0.0f;
+        for (int i = 0; i < 16; ++i) {
+            float a = fabsf(v[i]);
+            if (a > amax) amax = a;
+        }
+        float q = amax / 6.0f;
+        if (q < scale_floor) q = scale_floor;
+        const float s = e4m3_value(e4m3_code(q));
+        for (int i = 0; i < 16; ++i) {
+            float out;
+            if (s == 0.0f) {
+                out = copysignf(0.0f, v[i]);
+            } else {
+                const int code = e2m1_magnitude_code(fabsf(v[i] / s));
+                out = copysignf(e2m1_value((uint8_t)code) * s, v[i]);
+            }
+            y[g * 16 + i] = f32_to_bf16_bits(out);
+        }
+    }
+}
+
+int oracle_rope_fake_quant(const uint16_t* x, int64_t rows, int rows_per_position,
+                           const void* positions, int positions_int64, const float* cos_sin,
+                           int64_t max_pos, int D, int R, int rope_offset, int is_neox,
+                           int compress_ratio, int mode, float scale_floor, uint16_t* y) {
+    if (check_shape(D, R, rope_offset, GROUP) != ORC_OK) return ORC_EINVAL;
+    if (rows < 0 || rows_per_position <= 0 || max_pos <= 0) return ORC_EINVAL;
+    if (compress_ratio != 1 && compress_ratio != 2 && compress_ratio != 4) return ORC_EINVAL;
+    if (mode != FQ_UE8M0_32 && mode != FQ_E4M3_16) return ORC_EINVAL;
+    if (!(scale_floor >= 0.0f)) return ORC_EINVAL;
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t pos = read_position(positions, positions_int64, r / rows_per_position, max_pos);
+        pos -= pos % compress_ratio;
+        float v[HEAD_DIM];
+        for (int i = 0; i < HEAD_DIM; ++i) v[i] = bf16_to_f32(x[r * HEAD_DIM + i]);
+        rope_slice(v + rope_offset, cos_sin + pos * ROPE_DIM, is_neox);
+        fake_quant_row(v, mode, scale_floor, y + r * HEAD_DIM);
+    }
+    return ORC_OK;
+}
+
+/* step-level: fake quant of n rows of 128 (for the pins) */
+void oracle_fake_quant_rows(const float* x, int64_t n, int mode, float scale_floor, uint16_t* y) {
+    for (int64_t r = 0; r < n; ++r) fake_quant_row(x + r * HEAD_DIM, mode, scale_floor, y + r * HEAD_DIM);
 }

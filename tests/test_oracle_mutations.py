@@ -13,7 +13,7 @@ from oracle import build as obuild
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PINS = ["tests/test_oracle_quant.py", "tests/test_oracle_transforms.py",
         "tests/test_oracle_layout.py", "tests/test_oracle_scorer.py",
-        "tests/test_oracle_sglang.py", "tests/test_oracle_fp8.py"]
+        "tests/test_oracle_sglang.py", "tests/test_oracle_fp8.py", "tests/test_oracle_compressed.py"]
 
 MUTATIONS = {
     "tie_at_0.75_goes_down": ("else if (m < 0.75f) code = 1;", "else if (m <= 0.75f) code = 1;"),
@@ -41,8 +41,11 @@ MUTATIONS = {
     "wrong_rope_slice": ("rope_slice(x + rope_offset, cs_row, is_neox);\n    if (apply_hadamard)",
                          "rope_slice(x + 64 - rope_offset, cs_row, is_neox);\n    if (apply_hadamard)"),
     "q_scale_pads_unwritten": ("memset(qs, 0, (size_t)NGROUPS * 16 * J);", ";"),
-    "signed_amax": ("float a = fabsf(v[i]);", "float a = v[i];"),
-    "amax_over_4": ("float q = amax / 6.0f;", "float q = amax / 4.0f;"),
+    "signed_amax": ("    for (int i = 0; i < n; ++i) {\n        float a = fabsf(v[i]);",
+                    "    for (int i = 0; i < n; ++i) {\n        float a = v[i];"),
+    "amax_over_4": ("\n    float q = amax / 6.0f;", "\n    float q = amax / 4.0f;"),
+    "e4m3_16_signed_amax": ("for (int i = 0; i < 16; ++i) {\n            float a = fabsf(v[i]);",
+                            "for (int i = 0; i < 16; ++i) {\n            float a = v[i];"),
     "position_clamp_to_0": ("if (p >= max_pos) p = max_pos - 1;", "if (p >= max_pos) p = 0;"),
     "slot_0_skipped": ("\n        int64_t slot = slot_mapping[t];\n        if (slot < 0 || slot >= nslots) continue;",
                        "\n        int64_t slot = slot_mapping[t];\n        if (slot <= 0 || slot >= nslots) continue;"),
@@ -89,6 +92,17 @@ MUTATIONS = {
     "fp8_key_scale_misplaced": ("kv_cache_scale[slot] = quantize_row_fp8(",
                                 "kv_cache_scale[slot ^ 1] = quantize_row_fp8("),
     "fp8_floor_ignored": ("if (s < scale_floor) s = scale_floor;", "if (0) s = scale_floor;"),
+    "compress_ratio_ignored": ("pos -= pos % compress_ratio;    /* RoPE at the group's first position */",
+                               "pos -= 0 * compress_ratio;"),
+    "fake_quant_ratio_ignored": ("pos -= pos % compress_ratio;\n        float v[HEAD_DIM];",
+                                 "pos -= 0 * compress_ratio;\n        float v[HEAD_DIM];"),
+    "e4m3_16_amax_over_4": ("float q = amax / 6.0f;\n        if (q < scale_floor) q = scale_floor;\n        const float s = e4m3_value",
+                            "float q = amax / 4.0f;\n        if (q < scale_floor) q = scale_floor;\n        const float s = e4m3_value"),
+    "e4m3_16_scale_not_rounded": ("const float s = e4m3_value(e4m3_code(q));",
+                                  "const float s = q + 0.0f * e4m3_value(e4m3_code(q));"),
+    "e4m3_16_zero_scale_unsigned": ("out = copysignf(0.0f, v[i]);", "out = 0.0f;"),
+    "fake_quant_ue8m0_unscaled": ("const float q = e2m1_value(e2m1_nibble(v[i], e)) * e8m0_value((uint8_t)e);",
+                                  "const float q = e2m1_value(e2m1_nibble(v[i], e));"),
     "sglang_query_heads_shifted": ("q_packed + (t * H + h) * SLOT68", "q_packed + (t * H + (h ^ 1)) * SLOT68"),
 }
 
