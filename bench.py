@@ -209,6 +209,75 @@ def bench_fp8(args, dev):
     print(json.dumps(rec), flush=True)
 
 
+def bench_fake_quant(args, dev):
+    """RoPE tail + FP4 fake quant over the large-prefill query input (T = 131072
+    tokens x H = 64 heads = 8.4 M rows of 128, neox, dims 64..127 rotated),
+    per-16 E4M3 scales (the compressed-KV variant); per-32 UE8M0 timed beside it.
+    Algorithmic bytes per token: 256H in + 256H out + 8 (position) + 256 (cos/sin)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from pack_token_amd import fp4idx, workloads
+
+    wl = workloads.large_prefill(T=args.tokens, H=args.heads)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    q, pos, cs = up(wl.q.view(np.int16)), up(wl.positions), up(wl.cos_sin)
+    T, H = wl.T, wl.H
+    y = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run(mode):
+        def call():
+            fp4idx.rope_fake_quant(q, pos, cs, y=y, rows_per_position=H, mode=mode, stream=stream)
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        K = args.steps
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(K):
+            ev[i][0].record(stream)
+            call()
+            ev[i][1].record(stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / K, float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+
+    ms, l_ms = run("e4m3_16")
+    ms8, l_ms8 = run("ue8m0_32")
+    b = (512 * H + 8 + 256) * T
+    gbs = b / (l_ms * 1e-3) / 1e9
+    rec = {
+        "metric": "tokens/s and achieved HBM GB/s, RoPE tail + FP4 fake quant (bf16 in, bf16 out)",
+        "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 (values on the e2m1 x e4m3 grid)",
+        "data": "synthetic",
+        "config": {"workload": "fake_quant_prefill", "tokens": T, "heads": H, "rows": T * H,
+                   "head_dim": 128, "rope": "neox", "rope_offset": 64, "mode": "e4m3_16",
+                   "step": "fp4idx_rope_fake_quant"},
+        "ue8m0_32": {"ms_per_step": ms8, "launch_us": l_ms8 * 1e3,
+                     "GBps": b / (l_ms8 * 1e-3) / 1e9},
+        "roofline": {"kernel": "fake_quant_kernel<neox,e4m3_16>", "bound": "hbm",
+                     "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": b, "launch_us": l_ms * 1e3},
+    }
+    if not args.no_cpu_baseline:
+        n = min(args.cpu_sample_tokens, T, 4096)
+        c0 = time.perf_counter()
+        oracle.rope_fake_quant(wl.q[:n], wl.positions[:n], wl.cos_sin, rows_per_position=H,
+                               mode=oracle.FQ_E4M3_16)
+        dt = time.perf_counter() - c0
+        rec["cpu_baseline"] = {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"first {n} of {T} tokens ({n * H} rows, e4m3_16), "
+                                         f"1 thread, {dt:.2f} s wall"}
+    print(json.dumps(rec), flush=True)
+
+
 def sglang_q_bytes_per_token(H: int) -> int:
     return 256 * H + 8 + 256 + 68 * H
 
@@ -377,13 +446,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large_prefill",
                     choices=["large_prefill", "prefill_norm_rotate", "decode", "decode_scoring",
-                             "sglang_prefill", "fp8_prefill"],
+                             "sglang_prefill", "fp8_prefill", "fake_quant_prefill"],
                     help="large_prefill is the headline configuration; the other two are timed "
                          "for reference")
     ap.add_argument("--tokens", type=int, default=131072,
-                    help="large_prefill, sglang_prefill and fp8_prefill")
-    ap.add_argument("--heads", type=int, default=64,
-                    help="large_prefill, sglang_prefill and fp8_prefill")
+                    help="the prefill workloads")
+    ap.add_argument("--heads", type=int, default=64, help="the prefill workloads")
     ap.add_argument("--cpu-sample-tokens", type=int, default=131072)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
@@ -437,6 +505,9 @@ def main():
         return
     if args.workload == "fp8_prefill":
         bench_fp8(args, dev)
+        return
+    if args.workload == "fake_quant_prefill":
+        bench_fake_quant(args, dev)
         return
     if args.workload == "large_prefill":
         wl = workloads.large_prefill(T=args.tokens, H=args.heads)

@@ -76,6 +76,10 @@ extern "C" {
 #define FP4IDX_EUNSUPPORTED 2
 #define FP4IDX_EHIP 3
 
+/* fake-quant modes */
+#define FP4IDX_FQ_UE8M0_32 0
+#define FP4IDX_FQ_E4M3_16 1
+
 /* FP8 scale formats */
 #define FP4IDX_SCALE_UE8M0 0
 #define FP4IDX_SCALE_FP32 1
@@ -199,6 +203,11 @@ int fp4idx_qk_rope_pack_store(const void* q, const void* k, const void* position
  *   index_k_cache u8 [num_slots, 68], 4-byte aligned: token t's record goes
  *                to row slot_mapping[t] when 1 <= slot < num_slots; slot 0
  *                (and any slot outside that range) publishes nothing.
+ *   compress_ratio 1, 2 or 4: each key row stands for that many consecutive
+ *                tokens (a compressed KV entry) and is rotated at the first
+ *                position of its group, pos - pos % compress_ratio
+ *                (sgl-project/sglang PR 39656 "Summary": RoPE at the group's
+ *                first position; "Verification": ratios 1, 2, 4).
  *   num_slots    >= 0.  Rows that no token maps to are left untouched.
  */
 int fp4idx_q_rope_pack_sglang(const void* q, const void* positions, int positions_int64,
@@ -211,9 +220,9 @@ int fp4idx_k_rope_pack_store_sglang(const void* k, const void* positions, int po
                                     const float* cos_sin, int64_t max_pos,
                                     const int64_t* slot_mapping, const void* k_norm_gamma,
                                     float k_norm_eps, int64_t T, int D, int R, int rope_offset,
-                                    int group_size, int is_neox, float fake_quant_floor,
-                                    float pack_floor, uint8_t* index_k_cache, int64_t num_slots,
-                                    void* stream);
+                                    int group_size, int is_neox, int compress_ratio,
+                                    float fake_quant_floor, float pack_floor,
+                                    uint8_t* index_k_cache, int64_t num_slots, void* stream);
 
 /*
  * fp4idx_q_rope_pack_fp8 / fp4idx_k_rope_pack_store_fp8 -- the FP8 output
@@ -265,6 +274,38 @@ int fp4idx_k_rope_pack_store_fp8(const void* k, const void* positions, int posit
                                  int is_neox, int apply_hadamard, int scale_fmt,
                                  float scale_floor, uint8_t* kv_cache, float* kv_cache_scale,
                                  int64_t NB, int BS, void* stream);
+
+/*
+ * fp4idx_rope_fake_quant -- RoPE tail plus FP4 fake quant for the
+ * torch-shaped path (sgl-project/sglang PR 39656 "Summary": per-32 UE8M0
+ * scales by default and per-16 E4M3 scales for compressed KV, keeping the
+ * bf16 round trip after RoPE and rounding half to even).  Returns the bf16
+ * values of the quantized rows, not codes.
+ *
+ *   x            bf16 [rows, 128], 16-byte aligned (e.g. q [T, H, 128] with
+ *                rows = T*H, or compressed keys [N, 128]).
+ *   rows_per_position  row r uses positions[r / rows_per_position] (H for
+ *                queries, 1 for keys); positions holds
+ *                ceil(rows / rows_per_position) entries.
+ *   positions, positions_int64, cos_sin, max_pos, D, R, rope_offset,
+ *   is_neox: as for fp4idx_q_rope_pack (RoPE on the 64-dim slice, bf16).
+ *   compress_ratio 1, 2 or 4: the rotation uses pos - pos % compress_ratio.
+ *   mode         FP4IDX_FQ_UE8M0_32: per 32-group, e by the block-exponent
+ *                rule with scale_floor, value = E2M1(code) * 2^(e-127) as an
+ *                fp32 product (+-inf when it reaches 2^128), then bf16;
+ *                FP4IDX_FQ_E4M3_16: per 16-group, s = the e4m3fn value nearest
+ *                to max(amax/6, scale_floor) (448 at most), code = E2M1
+ *                value nearest to fl(x/s) (ties to even, 6 at most),
+ *                value = code value * s with the sign of x; s = 0 gives
+ *                signed zeros.
+ *   scale_floor  finite, >= 0.
+ *   y            bf16 [rows, 128], 16-byte aligned (may not alias x).
+ */
+int fp4idx_rope_fake_quant(const void* x, int64_t rows, int64_t rows_per_position,
+                           const void* positions, int positions_int64, const float* cos_sin,
+                           int64_t max_pos, int D, int R, int rope_offset, int is_neox,
+                           int compress_ratio, int mode, float scale_floor, void* y,
+                           void* stream);
 
 /*
  * fp4idx_dequant_debug -- reader side, for tests and debugging: expands

@@ -104,6 +104,13 @@ int check_fp8_scale(const char* fn, int scale_fmt, float scale_floor) {
     return FP4IDX_OK;
 }
 
+int check_ratio(const char* fn, int compress_ratio) {
+    if (compress_ratio != 1 && compress_ratio != 2 && compress_ratio != 4)
+        return fail(FP4IDX_EUNSUPPORTED, "%s: compress_ratio must be 1, 2 or 4 (got %d)", fn,
+                    compress_ratio);
+    return FP4IDX_OK;
+}
+
 int check_ptr(const char* fn, const char* name, const void* p, uintptr_t align) {
     if (p == nullptr) return fail(FP4IDX_EINVAL, "%s: %s must not be NULL", fn, name);
     if (!aligned(p, align))
@@ -322,10 +329,11 @@ int fp4idx_k_rope_pack_store_sglang(const void* k, const void* positions, int po
                                     const float* cos_sin, int64_t max_pos,
                                     const int64_t* slot_mapping, const void* k_norm_gamma,
                                     float k_norm_eps, int64_t T, int D, int R, int rope_offset,
-                                    int group_size, int is_neox, float fake_quant_floor,
-                                    float pack_floor, uint8_t* index_k_cache, int64_t num_slots,
-                                    void* stream) {
+                                    int group_size, int is_neox, int compress_ratio,
+                                    float fake_quant_floor, float pack_floor,
+                                    uint8_t* index_k_cache, int64_t num_slots, void* stream) {
     static const char* fn = "fp4idx_k_rope_pack_store_sglang";
+    FP4IDX_TRY(check_ratio(fn, compress_ratio));
     FP4IDX_TRY(check_floor(fn, "fake_quant_floor", fake_quant_floor));
     FP4IDX_TRY(check_floor(fn, "pack_floor", pack_floor));
     FP4IDX_TRY(check_common(fn, D, R, group_size, rope_offset, positions_int64, is_neox, 0,
@@ -357,6 +365,7 @@ int fp4idx_k_rope_pack_store_sglang(const void* k, const void* positions, int po
     a.eps = k_norm_eps;
     a.pos64 = positions_int64;
     a.rope_offset = rope_offset;
+    a.compress_ratio = compress_ratio;
     a.e_lo1 = floor_exponent(fake_quant_floor);
     a.e_lo2 = floor_exponent(pack_floor);
     hipError_t err = fp4idx::launch_k_rope_pack_store_sglang(a, is_neox != 0,
@@ -458,6 +467,47 @@ int fp4idx_k_rope_pack_store_fp8(const void* k, const void* positions, int posit
     hipError_t err = fp4idx::launch_k_rope_pack_store_fp8(a, is_neox != 0, apply_hadamard != 0,
                                                           scale_fmt == FP4IDX_SCALE_FP32,
                                                           static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(fn, err);
+    return FP4IDX_OK;
+}
+
+int fp4idx_rope_fake_quant(const void* x, int64_t rows, int64_t rows_per_position,
+                           const void* positions, int positions_int64, const float* cos_sin,
+                           int64_t max_pos, int D, int R, int rope_offset, int is_neox,
+                           int compress_ratio, int mode, float scale_floor, void* y,
+                           void* stream) {
+    static const char* fn = "fp4idx_rope_fake_quant";
+    if (mode != FP4IDX_FQ_UE8M0_32 && mode != FP4IDX_FQ_E4M3_16)
+        return fail(FP4IDX_EINVAL, "%s: mode must be 0 (per-32 UE8M0) or 1 (per-16 E4M3) (got %d)",
+                    fn, mode);
+    FP4IDX_TRY(check_ratio(fn, compress_ratio));
+    FP4IDX_TRY(check_common(fn, D, R, kGroup, rope_offset, positions_int64, is_neox, 0,
+                            scale_floor, rows, max_pos));
+    if (rows_per_position < 1)
+        return fail(FP4IDX_EINVAL, "%s: rows_per_position must be >= 1 (got %lld)", fn,
+                    (long long)rows_per_position);
+    if (rows > INT64_MAX / (kHeadDim * 2))
+        return fail(FP4IDX_EINVAL, "%s: rows too large (%lld)", fn, (long long)rows);
+    if (rows == 0) return FP4IDX_OK;
+    FP4IDX_TRY(check_ptr(fn, "x", x, 16));
+    FP4IDX_TRY(check_ptr(fn, "positions", positions, positions_int64 ? 8 : 4));
+    FP4IDX_TRY(check_ptr(fn, "cos_sin", cos_sin, 16));
+    FP4IDX_TRY(check_ptr(fn, "y", y, 16));
+    fp4idx::FakeQArgs a{};
+    a.x = static_cast<const uint16_t*>(x);
+    a.positions = positions;
+    a.cos_sin = cos_sin;
+    a.y = static_cast<uint16_t*>(y);
+    a.rows = rows;
+    a.max_pos = max_pos;
+    a.rows_per_position = rows_per_position;
+    a.pos64 = positions_int64;
+    a.rope_offset = rope_offset;
+    a.compress_ratio = compress_ratio;
+    a.e_lo = floor_exponent(scale_floor);
+    a.scale_floor = scale_floor;
+    hipError_t err = fp4idx::launch_rope_fake_quant(a, is_neox != 0, mode,
+                                                    static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return hip_fail(fn, err);
     return FP4IDX_OK;
 }

@@ -85,8 +85,25 @@ struct SKArgs {
     float eps;
     int pos64;
     int rope_offset;
+    int compress_ratio;         // 1, 2 or 4: RoPE at pos & ~(ratio - 1)
     int e_lo1;
     int e_lo2;
+};
+
+// RoPE tail + FP4 fake quant (bf16 in, bf16 out).
+struct FakeQArgs {
+    const uint16_t* x;          // bf16 [rows, 128]
+    const void* positions;      // [ceil(rows / rows_per_position)]
+    const float* cos_sin;
+    uint16_t* y;                // bf16 [rows, 128]
+    int64_t rows;
+    int64_t max_pos;
+    int64_t rows_per_position;
+    int pos64;
+    int rope_offset;
+    int compress_ratio;
+    int e_lo;                   // clamp(E(scale_floor), 1, 254), UE8M0 mode
+    float scale_floor;          // E4M3 mode
 };
 
 // FP8 output mode: one e4m3fn scale per 128-row.
@@ -155,6 +172,7 @@ hipError_t launch_q_rope_pack_fp8(const FQArgs& a, bool is_neox, bool hadamard, 
                                   hipStream_t stream);
 hipError_t launch_k_rope_pack_store_fp8(const FKArgs& a, bool is_neox, bool hadamard,
                                         bool fp32_scale, hipStream_t stream);
+hipError_t launch_rope_fake_quant(const FakeQArgs& a, bool is_neox, int mode, hipStream_t stream);
 hipError_t launch_dequant(const DArgs& a, hipStream_t stream);
 hipError_t launch_paged_mqa_logits(const LArgs& a, hipStream_t stream);
 

@@ -670,7 +670,9 @@ __global__ __launch_bounds__(kBlock) void q_sglang_kernel(SQArgs a) {
 }
 
 // Key records [num_slots, 68]: 16 lanes per token as k_row_kernel.  Slot 0,
-// like any slot outside [1, num_slots), publishes nothing.  The four group
+// like any slot outside [1, num_slots), publishes nothing.  A compressed key
+// row (compress_ratio consecutive tokens) is rotated at the first position of
+// its group.  The four group
 // exponents are merged into lane 0 of the row (half-row mirror, then ror 8).
 template <bool NEOX, bool NORM>
 __global__ __launch_bounds__(kBlock) void k_sglang_kernel(SKArgs a) {
@@ -680,7 +682,9 @@ __global__ __launch_bounds__(kBlock) void k_sglang_kernel(SKArgs a) {
     const int c = chunk_of(lane16);
     uint4 v = load16_stream(a.k + t * 128 + 8 * c);
     const int64_t slot = a.slot_mapping[t];
-    const int64_t pos = clamped_position(a.positions, a.pos64, t, a.max_pos);
+    // a compressed row is rotated at its group's first position (ratio 1, 2 or 4)
+    const int64_t pos = clamped_position(a.positions, a.pos64, t, a.max_pos) &
+                        ~(int64_t)(a.compress_ratio - 1);
     float C[8], S[8];
     rope_coeffs<NEOX>(a.cos_sin + pos * 64, c & 7, C, S);
     if (slot <= 0 || slot >= a.nslots) return;
@@ -838,6 +842,108 @@ __global__ __launch_bounds__(kBlock) void k_fp8_kernel(FKArgs a) {
     const uint2 q = quant_fp8_row<FP32>(v, a.scale_floor, s);
     *reinterpret_cast<uint2*>(a.kv_cache + slot * 128 + 8 * c) = q;
     if (lane16 == 0) a.kv_cache_scale[slot] = s;
+}
+
+// ---- RoPE tail + FP4 fake quant ----------------------------------------------
+// (sgl-project/sglang PR 39656 "Summary": the torch-shaped path rotates the
+// tail with the bf16 round trip and fake-quantizes with per-32 UE8M0 scales
+// by default or per-16 E4M3 scales for compressed KV, round half to even.)
+// Output: the bf16 values of the quantized rows.  16 lanes per 128-row
+// (lane chunk c = chunk_of(lane16)), 16 rows per block.
+//   UE8M0/32: the main quantizer, then code value * 2^(e-127) in fp32 (a
+//     product of magnitude >= 2^128 is inf, as in fp32) and bf16 (exact).
+//   E4M3/16: a 16-group is chunks 2j, 2j+1 = lanes L, L^1.  s = e4m3fn(
+//     max(amax/6, floor)) through the FP8 converter (saturated at 448 first);
+//     codes of fl(x/s) (reciprocal + FMA correction, exact as in the FP8
+//     path), clamped to 6 before the FP4 converter; value = code value * s,
+//     exact in fp32 and in bf16.  A zero scale gives signed zeros.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+    const uint32_t E = (c >> 3) & 15u, m = c & 7u;
+    return E == 0 ? (float)m * 0.001953125f  // m * 2^-9
+                  : __uint_as_float(((E + 120u) << 23) | (m << 20));
+}
+
+// value of code byte B's two nibbles (exact bf16 grid values at scale 1), times
+// `scale` in fp32
+template <int B>
+__device__ __forceinline__ void scaled_pair(uint32_t codes, float scale, float* out) {
+    const uint32_t g = __builtin_bit_cast(uint32_t,
+                                          __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, B));
+    out[2 * B] = __uint_as_float(g << 16) * scale;
+    out[2 * B + 1] = __uint_as_float(g & 0xFFFF0000u) * scale;
+}
+
+__device__ __forceinline__ void scaled_codes(uint32_t codes, float scale, float out[8]) {
+    scaled_pair<0>(codes, scale, out);
+    scaled_pair<1>(codes, scale, out);
+    scaled_pair<2>(codes, scale, out);
+    scaled_pair<3>(codes, scale, out);
+}
+
+template <int MODE>
+__device__ __forceinline__ uint4 fake_quant8(uint4 v, int e_lo, float scale_floor) {
+    float val[8];
+    if (MODE == 0) {
+        const Q8 q = quant8(v, e_lo);
+        const float sc = __uint_as_float((uint32_t)q.e << 23);
+        scaled_codes(q.codes, sc, val);
+    } else {
+        const u16x2_t a0 = __builtin_bit_cast(u16x2_t, v.x & 0x7FFF7FFFu);
+        const u16x2_t a1 = __builtin_bit_cast(u16x2_t, v.y & 0x7FFF7FFFu);
+        const u16x2_t a2 = __builtin_bit_cast(u16x2_t, v.z & 0x7FFF7FFFu);
+        const u16x2_t a3 = __builtin_bit_cast(u16x2_t, v.w & 0x7FFF7FFFu);
+        const u16x2_t m2 = __builtin_elementwise_max(__builtin_elementwise_max(a0, a1),
+                                                     __builtin_elementwise_max(a2, a3));
+        uint32_t m = max((uint32_t)m2.x, (uint32_t)m2.y);
+        m = max(m, dpp<kDppXor1>(m));
+        float qs = __uint_as_float(m << 16) / 6.0f;
+        qs = qs < scale_floor ? scale_floor : qs;
+        qs = qs < 448.0f ? qs : 448.0f;
+        const s16x2_t sc8 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2_t{0, 0}, qs, qs, 1.0f,
+                                                                     false);
+        const float s = e4m3_to_f32(__builtin_bit_cast(uint32_t, sc8) & 0xFFu);
+        float x[8];
+        unpack8(v, x);
+        if (s == 0.0f) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) val[e] = __builtin_copysignf(0.0f, x[e]);
+        } else {
+            const float r = rcp_rn(s);
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float y0 = x[e] * r;
+                const float err = __builtin_fmaf(-y0, s, x[e]);
+                const float q = __builtin_fmaf(err, r, y0);
+                y[e] = __builtin_copysignf(__builtin_fminf(__builtin_fabsf(q), 6.0f), x[e]);
+            }
+            uint32_t codes = 0;
+            codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[0], y[1], 1.0f, 0);
+            codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[2], y[3], 1.0f, 1);
+            codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[4], y[5], 1.0f, 2);
+            codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[6], y[7], 1.0f, 3);
+            scaled_codes(codes, s, val);
+        }
+    }
+    return pack8(val);
+}
+
+template <bool NEOX, int MODE>
+__global__ __launch_bounds__(kBlock) void fake_quant_kernel(FakeQArgs a) {
+    const int lane16 = threadIdx.x & 15;
+    const int64_t row = (int64_t)blockIdx.x * (kBlock / 16) + (threadIdx.x >> 4);
+    if (row >= a.rows) return;
+    const int c = chunk_of(lane16);
+    const uint4 v = load16_stream(a.x + row * 128 + 8 * c);
+    const int64_t pos = clamped_position(a.positions, a.pos64, row / a.rows_per_position,
+                                         a.max_pos) & ~(int64_t)(a.compress_ratio - 1);
+    float C[8], S[8];
+    rope_coeffs<NEOX>(a.cos_sin + pos * 64, c & 7, C, S);
+    const bool rot_lane = (c >> 3) == (a.rope_offset >> 6);
+    const uint4 w = select4(rot_lane, rope8<NEOX>(v, C, S), v);
+    const uint4 y = fake_quant8<MODE>(w, a.e_lo, a.scale_floor);
+    const u32x4_t o = {y.x, y.y, y.z, y.w};
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(a.y + row * 128 + 8 * c));
 }
 
 // ---- dequantization (debug reader) -------------------------------------------
@@ -1014,6 +1120,16 @@ hipError_t launch_k_rope_pack_store_fp8(const FKArgs& a, bool is_neox, bool hada
                     : launch_k_fp8<true, false>(a, hadamard, fp32_scale, blocks, stream);
     return norm ? launch_k_fp8<false, true>(a, hadamard, fp32_scale, blocks, stream)
                 : launch_k_fp8<false, false>(a, hadamard, fp32_scale, blocks, stream);
+}
+
+hipError_t launch_rope_fake_quant(const FakeQArgs& a, bool is_neox, int mode, hipStream_t stream) {
+    if (a.rows == 0) return hipSuccess;
+    const int64_t blocks = (a.rows + kBlock / 16 - 1) / (kBlock / 16);
+    if (mode == 0)
+        return is_neox ? launch(fake_quant_kernel<true, 0>, blocks, 0, stream, a)
+                       : launch(fake_quant_kernel<false, 0>, blocks, 0, stream, a);
+    return is_neox ? launch(fake_quant_kernel<true, 1>, blocks, 0, stream, a)
+                   : launch(fake_quant_kernel<false, 1>, blocks, 0, stream, a);
 }
 
 hipError_t launch_dequant(const DArgs& a, hipStream_t stream) {

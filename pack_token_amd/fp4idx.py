@@ -62,8 +62,11 @@ def lib():
                                                     _i, _i, _f, _f, _p, _p]
             L.fp4idx_q_rope_pack_sglang.restype = _i
             L.fp4idx_k_rope_pack_store_sglang.argtypes = [_p, _p, _i, _p, _i64, _p, _p, _f, _i64,
-                                                          _i, _i, _i, _i, _i, _f, _f, _p, _i64,
-                                                          _p]
+                                                          _i, _i, _i, _i, _i, _i, _f, _f, _p,
+                                                          _i64, _p]
+            L.fp4idx_rope_fake_quant.argtypes = [_p, _i64, _i64, _p, _i, _p, _i64, _i, _i, _i, _i,
+                                                 _i, _i, _f, _p, _p]
+            L.fp4idx_rope_fake_quant.restype = _i
             L.fp4idx_k_rope_pack_store_sglang.restype = _i
             L.fp4idx_q_rope_pack_fp8.argtypes = [_p, _p, _i, _p, _i64, _p, _f, _i64, _i, _i, _i, _i,
                                                  _i, _i, _i, _f, _p, _p, _p]
@@ -235,6 +238,33 @@ def k_rope_pack_store_fp8(k, positions, cos_sin, slot_mapping, kv_cache, kv_cach
 
 
 SGLANG_RECORD = 68
+FQ_UE8M0_32, FQ_E4M3_16 = 0, 1
+
+
+def rope_fake_quant(x, positions, cos_sin, *, y=None, rows_per_position=1, is_neox=True,
+                    rope_offset=64, compress_ratio=1, mode="ue8m0_32",
+                    scale_floor=DEFAULT_SCALE_FLOOR, stream=None):
+    """fp4idx_rope_fake_quant.  x bf16 [..., 128]; returns y bf16 of the same shape
+    (the fake-quantized values).  mode: "ue8m0_32" or "e4m3_16"."""
+    dev = x.device
+    _require(x, "x", (torch.bfloat16, torch.int16, torch.uint16))
+    _require(positions, "positions", (torch.int32, torch.int64), dev)
+    _require(cos_sin, "cos_sin", (torch.float32,), dev)
+    if x.shape[-1] != HEAD_DIM:
+        raise ValueError("x must end in a 128-dim axis")
+    rows = x.numel() // HEAD_DIM
+    if rows and positions.numel() * rows_per_position < rows:
+        raise ValueError("positions has fewer than ceil(rows / rows_per_position) entries")
+    if y is None:
+        y = torch.empty(x.shape, dtype=torch.bfloat16, device=dev)
+    _require(y, "y", (torch.bfloat16, torch.int16, torch.uint16), dev)
+    m = {"ue8m0_32": FQ_UE8M0_32, "e4m3_16": FQ_E4M3_16}.get(mode, mode)
+    rc = lib().fp4idx_rope_fake_quant(
+        _ptr(x), rows, rows_per_position, _ptr(positions), int(positions.dtype == torch.int64),
+        _ptr(cos_sin), cos_sin.shape[0], HEAD_DIM, ROPE_DIM, rope_offset, int(is_neox),
+        compress_ratio, m, scale_floor, _ptr(y), _stream_handle(stream))
+    _check(rc)
+    return y
 
 
 def q_rope_pack_sglang(q, positions, cos_sin, *, q_packed=None, is_neox=True, rope_offset=64,
@@ -261,8 +291,8 @@ def q_rope_pack_sglang(q, positions, cos_sin, *, q_packed=None, is_neox=True, ro
 
 def k_rope_pack_store_sglang(k, positions, cos_sin, slot_mapping, index_k_cache, *,
                              k_norm_gamma=None, k_norm_eps=1e-6, is_neox=True, rope_offset=64,
-                             fake_quant_floor=DEFAULT_SCALE_FLOOR, pack_floor=DEFAULT_SCALE_FLOOR,
-                             stream=None):
+                             compress_ratio=1, fake_quant_floor=DEFAULT_SCALE_FLOOR,
+                             pack_floor=DEFAULT_SCALE_FLOOR, stream=None):
     """fp4idx_k_rope_pack_store_sglang.  k bf16 [T,128]; index_k_cache u8 [num_slots,68] is
     updated in place (slot 0 publishes nothing)."""
     T, D = k.shape
@@ -278,8 +308,8 @@ def k_rope_pack_store_sglang(k, positions, cos_sin, slot_mapping, index_k_cache,
     rc = lib().fp4idx_k_rope_pack_store_sglang(
         _ptr(k), _ptr(positions), int(positions.dtype == torch.int64), _ptr(cos_sin),
         cos_sin.shape[0], _ptr(slot_mapping), _ptr(k_norm_gamma), k_norm_eps, T, D, ROPE_DIM,
-        rope_offset, GROUP, int(is_neox), fake_quant_floor, pack_floor, _ptr(index_k_cache),
-        index_k_cache.shape[0], _stream_handle(stream))
+        rope_offset, GROUP, int(is_neox), compress_ratio, fake_quant_floor, pack_floor,
+        _ptr(index_k_cache), index_k_cache.shape[0], _stream_handle(stream))
     _check(rc)
     return index_k_cache
 

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
                      "fp4idx_k_rope_pack_store_fp8", "fp4idx_k_rope_pack_store_sglang",
                      "fp4idx_last_error", "fp4idx_paged_mqa_logits", "fp4idx_q_rope_pack",
                      "fp4idx_q_rope_pack_fp8", "fp4idx_q_rope_pack_sglang",
-                     "fp4idx_qk_rope_pack_store"]
+                     "fp4idx_qk_rope_pack_store", "fp4idx_rope_fake_quant"]
     lib = ctypes.CDLL(fp4idx.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -215,8 +215,9 @@ def sq_call(**over):
 def sk_call(**over):
     a = dict(k=ALIGNED, positions=ALIGNED, positions_int64=1, cos_sin=ALIGNED, max_pos=16,
              slot_mapping=ALIGNED, k_norm_gamma=None, k_norm_eps=1e-6, T=4, D=128, R=64,
-             rope_offset=64, group_size=32, is_neox=1, fake_quant_floor=2.0 ** -126,
-             pack_floor=1e-10, index_k_cache=ALIGNED, num_slots=128, stream=None)
+             rope_offset=64, group_size=32, is_neox=1, compress_ratio=1,
+             fake_quant_floor=2.0 ** -126, pack_floor=1e-10, index_k_cache=ALIGNED, num_slots=128,
+             stream=None)
     a.update(over)
     return fp4idx.lib().fp4idx_k_rope_pack_store_sglang(*a.values())
 
@@ -245,6 +246,8 @@ def test_sglang_q_rejections(over, code, msg):
 
 SK_REJECT = [
     (dict(group_size=64), fp4idx.EUNSUPPORTED, "group_size"),
+    (dict(compress_ratio=3), fp4idx.EUNSUPPORTED, "compress_ratio"),
+    (dict(compress_ratio=0), fp4idx.EUNSUPPORTED, "compress_ratio"),
     (dict(num_slots=-1), fp4idx.EINVAL, "num_slots"),
     (dict(num_slots=1 << 62), fp4idx.EINVAL, "num_slots"),
     (dict(fake_quant_floor=float("-inf")), fp4idx.EINVAL, "fake_quant_floor"),
@@ -325,6 +328,35 @@ def test_fp8_k_rejections(over, code, msg):
     assert fp4idx.last_error().startswith("fp4idx_k_rope_pack_store_fp8:")
 
 
+def fq8_call(**over):
+    a = dict(x=ALIGNED, rows=64, rows_per_position=16, positions=ALIGNED, positions_int64=1,
+             cos_sin=ALIGNED, max_pos=16, D=128, R=64, rope_offset=64, is_neox=1,
+             compress_ratio=1, mode=1, scale_floor=2.0 ** -126, y=ALIGNED, stream=None)
+    a.update(over)
+    return fp4idx.lib().fp4idx_rope_fake_quant(*a.values())
+
+
+FQUANT_REJECT = [
+    (dict(mode=2), fp4idx.EINVAL, "mode"),
+    (dict(compress_ratio=8), fp4idx.EUNSUPPORTED, "compress_ratio"),
+    (dict(rows_per_position=0), fp4idx.EINVAL, "rows_per_position"),
+    (dict(rows=-1), fp4idx.EINVAL, "T must be"),
+    (dict(D=256), fp4idx.EUNSUPPORTED, "head_dim"),
+    (dict(rope_offset=8), fp4idx.EUNSUPPORTED, "rope_offset"),
+    (dict(scale_floor=float("nan")), fp4idx.EINVAL, "scale_floor"),
+    (dict(x=ALIGNED + 4), fp4idx.EINVAL, "x must be 16-byte"),
+    (dict(y=None), fp4idx.EINVAL, "y must not be NULL"),
+    (dict(positions=None), fp4idx.EINVAL, "positions must not be NULL"),
+]
+
+
+@pytest.mark.parametrize("over,code,msg", FQUANT_REJECT)
+def test_fake_quant_rejections(over, code, msg):
+    assert fq8_call(**over) == code
+    assert msg in fp4idx.last_error(), fp4idx.last_error()
+    assert fp4idx.last_error().startswith("fp4idx_rope_fake_quant:")
+
+
 def test_zero_tokens_is_a_noop_even_with_null_buffers():
     assert q_call(T=0, q=None, positions=None, cos_sin=None, q_out=None, q_scale_out=None) == 0
     assert k_call(T=0, k=None, positions=None, cos_sin=None, slot_mapping=None, kv_cache=None,
@@ -338,6 +370,7 @@ def test_zero_tokens_is_a_noop_even_with_null_buffers():
                    weights_out=None) == 0
     assert fk_call(T=0, k=None, positions=None, cos_sin=None, slot_mapping=None, kv_cache=None,
                    kv_cache_scale=None) == 0
+    assert fq8_call(rows=0, x=None, positions=None, cos_sin=None, y=None) == 0
     assert sk_call(T=0, k=None, positions=None, cos_sin=None, slot_mapping=None,
                    index_k_cache=None) == 0
     # but shapes are still checked first

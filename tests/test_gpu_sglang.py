@@ -47,7 +47,7 @@ def gpu_k(k, positions, cos_sin, slots, num_slots, gamma=None, **kw):
     return cache.cpu().numpy()
 
 
-def check_both(wl, slots, num_slots, gamma=None, floors=(FMIN, FMIN)):
+def check_both(wl, slots, num_slots, gamma=None, floors=(FMIN, FMIN), ratio=1):
     kw = dict(is_neox=wl.is_neox, rope_offset=wl.rope_offset, fake_quant_floor=floors[0],
               pack_floor=floors[1])
     say(f"case sglang {wl.name}: T={wl.T} H={wl.H} neox={wl.is_neox} ro={wl.rope_offset} "
@@ -55,10 +55,12 @@ def check_both(wl, slots, num_slots, gamma=None, floors=(FMIN, FMIN)):
     got_q = gpu_q(wl.q, wl.positions, wl.cos_sin, **kw)
     ref_q = oracle.q_rope_pack_sglang(wl.q, wl.positions, wl.cos_sin, **kw)
     assert_same("q_packed", got_q, ref_q)
-    got_k = gpu_k(wl.k, wl.positions, wl.cos_sin, slots, num_slots, gamma, k_norm_eps=1e-6, **kw)
+    got_k = gpu_k(wl.k, wl.positions, wl.cos_sin, slots, num_slots, gamma, k_norm_eps=1e-6,
+                  compress_ratio=ratio, **kw)
     ref_k = np.full((num_slots, 68), SENTINEL, np.uint8)
     oracle.k_rope_pack_store_sglang(wl.k, wl.positions, wl.cos_sin, slots, ref_k,
-                                    k_norm_gamma=gamma, k_norm_eps=1e-6, **kw)
+                                    k_norm_gamma=gamma, k_norm_eps=1e-6, compress_ratio=ratio,
+                                    **kw)
     assert_same("index_k_cache", got_k, ref_k)
 
 
@@ -80,6 +82,16 @@ def test_row_matrix(T, pos32):
     wl = workloads.edge_mix(seed=300 + T, T=T, positions_int32=pos32)
     slots, n = with_slot_zero(wl)
     check_both(wl, slots, n)
+
+
+@pytest.mark.parametrize("ratio", [2, 4])
+@pytest.mark.parametrize("pos32", [False, True])
+def test_compress_ratio(ratio, pos32):
+    """Compressed key rows rotated at their group's first position (sglang PR
+    39656 "Verification": compress ratios 1, 2, 4; ratio 1 is every other test)."""
+    wl = workloads.edge_mix(seed=330 + ratio, T=300, positions_int32=pos32)
+    slots, n = with_slot_zero(wl)
+    check_both(wl, slots, n, ratio=ratio)
 
 
 @pytest.mark.parametrize("floors", sorted(FLOORS))
