@@ -32,6 +32,8 @@ KERNEL_SRC = os.path.join(ROOT, "pack_token_amd", "csrc", "fp4idx_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qk_kernel_large_prefill_traffic.json")
 SGLANG_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q_sglang_kernel_sglang_prefill_traffic.json")
 FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q_fp8_kernel_fp8_prefill_traffic.json")
+FQ_TRAFFIC_FILE = os.path.join(ROOT, "profiles",
+                               "fake_quant_kernel_fake_quant_prefill_traffic.json")
 
 
 def q_bytes_per_token(H: int) -> int:
@@ -263,7 +265,9 @@ def bench_fake_quant(args, dev):
                      "GBps": b / (l_ms8 * 1e-3) / 1e9},
         "roofline": {"kernel": "fake_quant_kernel<neox,e4m3_16>", "bound": "hbm",
                      "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(FQ_TRAFFIC_FILE) if (T, H) == (131072, 64)
+                     else None,
                      "algorithmic_bytes_per_launch": b, "launch_us": l_ms * 1e3},
     }
     if not args.no_cpu_baseline:
