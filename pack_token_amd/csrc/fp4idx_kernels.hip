@@ -85,6 +85,11 @@ __device__ __forceinline__ uint4 load16_stream(const void* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+__device__ __forceinline__ void store16_stream(void* p, uint4 v) {
+    const u32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+}
+
 __device__ __forceinline__ void store4_plain(void* p, uint32_t v) {
     *reinterpret_cast<uint32_t*>(p) = v;
 }
@@ -716,7 +721,8 @@ __global__ __launch_bounds__(kBlock) void k_sglang_kernel(SKArgs a) {
 //
 // ue8m0: the scaled converter divides by the power-of-two scale exactly.
 // fp32: x / s rounded to fp32 first (the value the converter then rounds),
-// computed as y0 = x * r, y = fma(fma(-y0, s, x), r, y0) with r = RN(1/s);
+// computed as y0 = x * r, y = fma(fma(-y0, s, x), r, y0) with r = RN(1/s)
+// (the correctly rounded fp32 reciprocal);
 // for every bf16 x and normal fp32 s this equals RN(x / s) -- checked
 // exhaustively over all 2^31 significand pairs on the CPU.
 __device__ __forceinline__ void store8_stream(void* p, uint2 v) {
@@ -753,7 +759,7 @@ __device__ __forceinline__ uint2 quant_fp8_row(uint4 v, float scale_floor, float
         hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, __builtin_bit_cast(bf16x2_t, v.z), s, false);
         hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, __builtin_bit_cast(bf16x2_t, v.w), s, true);
     } else {
-        const float r = rcp_rn(s);
+        const float r = __frcp_rn(s);  // RN(1/s)
         float x[8], y[8];
         unpack8(v, x);
 #pragma unroll
@@ -908,7 +914,7 @@ __device__ __forceinline__ uint4 fake_quant8(uint4 v, int e_lo, float scale_floo
 #pragma unroll
             for (int e = 0; e < 8; ++e) val[e] = __builtin_copysignf(0.0f, x[e]);
         } else {
-            const float r = rcp_rn(s);
+            const float r = __frcp_rn(s);  // RN(1/s)
             float y[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -928,6 +934,7 @@ __device__ __forceinline__ uint4 fake_quant8(uint4 v, int e_lo, float scale_floo
     return pack8(val);
 }
 
+// One row per 16 lanes, for rows_per_position < 4 (keys: one row per position).
 template <bool NEOX, int MODE>
 __global__ __launch_bounds__(kBlock) void fake_quant_kernel(FakeQArgs a) {
     const int lane16 = threadIdx.x & 15;
@@ -935,15 +942,55 @@ __global__ __launch_bounds__(kBlock) void fake_quant_kernel(FakeQArgs a) {
     if (row >= a.rows) return;
     const int c = chunk_of(lane16);
     const uint4 v = load16_stream(a.x + row * 128 + 8 * c);
-    const int64_t pos = clamped_position(a.positions, a.pos64, row / a.rows_per_position,
-                                         a.max_pos) & ~(int64_t)(a.compress_ratio - 1);
+    const int64_t pidx = a.rows_per_position == 1 ? row : row / a.rows_per_position;
+    const int64_t pos = clamped_position(a.positions, a.pos64, pidx, a.max_pos) &
+                        ~(int64_t)(a.compress_ratio - 1);
     float C[8], S[8];
     rope_coeffs<NEOX>(a.cos_sin + pos * 64, c & 7, C, S);
     const bool rot_lane = (c >> 3) == (a.rope_offset >> 6);
     const uint4 w = select4(rot_lane, rope8<NEOX>(v, C, S), v);
     const uint4 y = fake_quant8<MODE>(w, a.e_lo, a.scale_floor);
-    const u32x4_t o = {y.x, y.y, y.z, y.w};
-    __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(a.y + row * 128 + 8 * c));
+    store16_stream(a.y + row * 128 + 8 * c, y);
+}
+
+// One position per wavefront for rows_per_position >= 4 (queries: the H heads
+// of a token): the RoPE coefficients are formed once, and each step handles 8
+// rows (two 16-byte loads per lane, lanes 16k..16k+15 on rows k and k+4).  A
+// row past the token's last leaves as a whole 16-lane group, so every DPP
+// pattern still reads lanes of its own row.
+template <bool NEOX, int MODE>
+__global__ __launch_bounds__(kBlock) void fake_quant_token_kernel(FakeQArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    const int64_t r0 = t * a.rows_per_position;
+    if (r0 >= a.rows) return;
+    const int64_t r_end = min(r0 + a.rows_per_position, a.rows);
+    const int c = chunk_of(lane & 15);
+    const int rsub = lane >> 4;
+    const int64_t pos = clamped_position(a.positions, a.pos64, t, a.max_pos) &
+                        ~(int64_t)(a.compress_ratio - 1);
+    float C[8], S[8];
+    rope_coeffs<NEOX>(a.cos_sin + pos * 64, c & 7, C, S);
+    const bool rot_lane = (c >> 3) == (a.rope_offset >> 6);
+    for (int64_t rb = r0; rb < r_end; rb += 8) {
+        const int64_t ra = rb + rsub, rc = ra + 4;
+        if (rc < r_end) {
+            const uint4 v0 = load16_stream(a.x + ra * 128 + 8 * c);
+            const uint4 v1 = load16_stream(a.x + rc * 128 + 8 * c);
+            const uint4 y0 = fake_quant8<MODE>(select4(rot_lane, rope8<NEOX>(v0, C, S), v0),
+                                               a.e_lo, a.scale_floor);
+            const uint4 y1 = fake_quant8<MODE>(select4(rot_lane, rope8<NEOX>(v1, C, S), v1),
+                                               a.e_lo, a.scale_floor);
+            store16_stream(a.y + ra * 128 + 8 * c, y0);
+            store16_stream(a.y + rc * 128 + 8 * c, y1);
+        } else if (ra < r_end) {
+            const uint4 v0 = load16_stream(a.x + ra * 128 + 8 * c);
+            const uint4 y0 = fake_quant8<MODE>(select4(rot_lane, rope8<NEOX>(v0, C, S), v0),
+                                               a.e_lo, a.scale_floor);
+            store16_stream(a.y + ra * 128 + 8 * c, y0);
+        }
+    }
 }
 
 // ---- dequantization (debug reader) -------------------------------------------
@@ -1124,6 +1171,15 @@ hipError_t launch_k_rope_pack_store_fp8(const FKArgs& a, bool is_neox, bool hada
 
 hipError_t launch_rope_fake_quant(const FakeQArgs& a, bool is_neox, int mode, hipStream_t stream) {
     if (a.rows == 0) return hipSuccess;
+    if (a.rows_per_position >= 4) {
+        const int64_t npos = (a.rows + a.rows_per_position - 1) / a.rows_per_position;
+        const int64_t blocks = (npos + kWavesPerBlock - 1) / kWavesPerBlock;
+        if (mode == 0)
+            return is_neox ? launch(fake_quant_token_kernel<true, 0>, blocks, 0, stream, a)
+                           : launch(fake_quant_token_kernel<false, 0>, blocks, 0, stream, a);
+        return is_neox ? launch(fake_quant_token_kernel<true, 1>, blocks, 0, stream, a)
+                       : launch(fake_quant_token_kernel<false, 1>, blocks, 0, stream, a);
+    }
     const int64_t blocks = (a.rows + kBlock / 16 - 1) / (kBlock / 16);
     if (mode == 0)
         return is_neox ? launch(fake_quant_kernel<true, 0>, blocks, 0, stream, a)
