@@ -96,6 +96,11 @@ def test_floors_and_tiny_rows(fmt):
         check(wl, fmt, floor=floor)
 
 
+@pytest.mark.parametrize("fmt", ["ue8m0", "fp32"])
+def test_maximum_heads(fmt):
+    check(workloads.sweep_case(779, 5, 2048, True, 64), fmt, weights_scale=2.0, had=True)
+
+
 def test_empty():
     wl = workloads.tiny(T=0, H=16)
     q_out, w_out = gpu_q(wl.q, wl.positions, wl.cos_sin, wl.weights)

@@ -63,6 +63,17 @@ def test_modes_ragged(is_neox, rope_offset, norm, had, fused):
 
 
 @FUSED
+@pytest.mark.parametrize("had", [False, True])
+def test_maximum_heads(had, fused):
+    """H = 2048, the largest head count the ABI accepts (J = 128 q-scale
+    columns; 32 KB of LDS per block), on 6 tokens including a skipped slot."""
+    wl = workloads.sweep_case(777, 6, 2048, True, 64)
+    wl.apply_hadamard = had
+    wl.slot_mapping[2] = -1
+    check(wl, fused=fused)
+
+
+@FUSED
 def test_no_weights_and_scale_floor(fused):
     wl = workloads.edge_mix(seed=21, T=64)
     wl.scale_floor = float(np.float32(1e-10))   # all-zero groups get e = 94

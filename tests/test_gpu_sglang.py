@@ -110,6 +110,13 @@ def test_modes_with_rmsnorm(neox, ro):
     check_both(wl, slots, n, gamma=gamma)
 
 
+def test_maximum_heads():
+    """H = 2048 query records (139 KB per token) and ragged T."""
+    wl = workloads.sweep_case(778, 5, 2048, False, 0)
+    slots, n = with_slot_zero(wl)
+    check_both(wl, slots, n)
+
+
 def test_empty():
     wl = workloads.tiny(T=0, H=16)
     got = gpu_q(wl.q, wl.positions, wl.cos_sin)
