@@ -28,7 +28,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "pack_token_amd", "csrc", "fp4idx_kernels.hip")
+CSRC = os.path.join(ROOT, "pack_token_amd", "csrc")
+# the sources each profiled kernel is built from (a traffic record is used only
+# while their hash matches the one it was taken on)
+MAIN_SOURCES = ("fp4idx_device.h", "fp4idx_kernels.hip")
+MODE_SOURCES = ("fp4idx_device.h", "fp4idx_modes.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qk_kernel_large_prefill_traffic.json")
 SGLANG_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q_sglang_kernel_sglang_prefill_traffic.json")
 FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q_fp8_kernel_fp8_prefill_traffic.json")
@@ -49,21 +53,24 @@ def step_bytes_per_token(H: int) -> int:
     return q_bytes_per_token(H) + k_bytes_per_token()
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def kernel_source_hash(sources=MAIN_SOURCES) -> str:
+    h = hashlib.sha256()
+    for name in sources:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
-def measured_traffic(path=TRAFFIC_FILE):
+def measured_traffic(path=TRAFFIC_FILE, sources=MAIN_SOURCES):
     """HBM bytes of one launch of the profiled kernel from committed rocprofv3
     FETCH_SIZE / WRITE_SIZE counts (scaled by a plain copy's counts), if they
-    were taken on the current kernel source; otherwise None."""
+    were taken on the current kernel sources; otherwise None."""
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
+    if rec.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
     return int(rec["bytes_per_launch"])
 
@@ -192,7 +199,7 @@ def bench_fp8(args, dev):
                         "q_kernel_GBps": qb / (q_ms32 * 1e-3) / 1e9},
         "roofline": {"kernel": "q_fp8_kernel<neox,ue8m0>", "bound": "hbm", "achieved": q_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": q_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(FP8_TRAFFIC_FILE) if (T, H) == (131072, 64)
+                     "traffic": measured_traffic(FP8_TRAFFIC_FILE, MODE_SOURCES) if (T, H) == (131072, 64)
                      else None,
                      "algorithmic_bytes_per_launch": qb, "launch_us": q_ms * 1e3},
     }
@@ -266,7 +273,7 @@ def bench_fake_quant(args, dev):
         "roofline": {"kernel": "fake_quant_kernel<neox,e4m3_16>", "bound": "hbm",
                      "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(FQ_TRAFFIC_FILE) if (T, H) == (131072, 64)
+                     "traffic": measured_traffic(FQ_TRAFFIC_FILE, MODE_SOURCES) if (T, H) == (131072, 64)
                      else None,
                      "algorithmic_bytes_per_launch": b, "launch_us": l_ms * 1e3},
     }
@@ -357,7 +364,7 @@ def bench_sglang(args, dev):
         "k_kernel_GBps": kb / (k_ms * 1e-3) / 1e9,
         "roofline": {"kernel": "q_sglang_kernel<neox>", "bound": "hbm", "achieved": q_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": q_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(SGLANG_TRAFFIC_FILE) if (T, H) == (131072, 64)
+                     "traffic": measured_traffic(SGLANG_TRAFFIC_FILE, MODE_SOURCES) if (T, H) == (131072, 64)
                      else None,
                      "algorithmic_bytes_per_launch": qb,
                      "launch_us": q_ms * 1e3},

@@ -1,5 +1,6 @@
 // fp4idx_internal.h -- launch descriptors shared by the C-ABI layer
-// (fp4idx_api.cpp) and the kernels (fp4idx_kernels.hip).  Not installed.
+// (fp4idx_api.cpp) and the kernels (fp4idx_kernels.hip, fp4idx_modes.hip,
+// fp4idx_scorer.hip).  Not installed.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
