@@ -37,7 +37,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qk_kernel_large_prefill_traffic.j
 SGLANG_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q_sglang_kernel_sglang_prefill_traffic.json")
 FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q_fp8_kernel_fp8_prefill_traffic.json")
 FQ_TRAFFIC_FILE = os.path.join(ROOT, "profiles",
-                               "fake_quant_kernel_fake_quant_prefill_traffic.json")
+                               "fake_quant_token_kernel_fake_quant_prefill_traffic.json")
 
 
 def q_bytes_per_token(H: int) -> int:
@@ -270,7 +270,7 @@ def bench_fake_quant(args, dev):
                    "step": "fp4idx_rope_fake_quant"},
         "ue8m0_32": {"ms_per_step": ms8, "launch_us": l_ms8 * 1e3,
                      "GBps": b / (l_ms8 * 1e-3) / 1e9},
-        "roofline": {"kernel": "fake_quant_kernel<neox,e4m3_16>", "bound": "hbm",
+        "roofline": {"kernel": "fake_quant_token_kernel<neox,e4m3_16>", "bound": "hbm",
                      "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic(FQ_TRAFFIC_FILE, MODE_SOURCES) if (T, H) == (131072, 64)
