@@ -241,6 +241,84 @@ __global__ __launch_bounds__(kBlock) void qk_kernel(QArgs qa, KArgs ka) {
         k_row<NEOX, NORM, HAD>(ka, kv, kslot, lane & 15, KC, KS);
 }
 
+// ---- small batches -------------------------------------------------------------
+// Below kSmallBatchTokens tokens the per-token kernels leave fewer than two
+// wavefronts per CU.  Here one wavefront takes a (token, group of 8 heads), so
+// a decode batch spreads over H/8 times as many wavefronts and each carries
+// one step of work (measured: 256 tokens x 32 heads, 5.4 -> 5.1 us, and with
+// key RMSNorm + Hadamard 8.9 -> 5.9 us; from 1024 tokens on the per-token
+// kernels are faster).  The group's scale bytes go
+// straight to q_scale_out (each byte has one writer; group 0 writes the zero
+// pads); group 0 also copies the token's weights and, with WITH_KEY, does the
+// token's key row on lanes 0..15, its loads issued first.
+template <bool NEOX, bool HAD, bool NORM, bool WITH_KEY>
+__global__ __launch_bounds__(kBlock) void qk_small_kernel(QArgs qa, KArgs ka) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int groups = qa.H >> 3;
+    const int64_t wid = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    const int64_t t = wid / groups;
+    if (t >= qa.T) return;
+    const int g8 = (int)(wid - t * groups);
+    const int H = qa.H;
+    const int J = qa.J;
+    const bool krow = WITH_KEY && g8 == 0 && lane < 16;
+    uint4 kv = make_uint4(0u, 0u, 0u, 0u);
+    int64_t kslot = -1;
+    float KC[8], KS[8];
+    if (krow) {
+        kv = load16_stream(ka.k + t * 128 + 8 * chunk_of(lane));
+        kslot = ka.slot_mapping[t];
+        const int64_t kpos = clamped_position(ka.positions, ka.pos64, t, ka.max_pos);
+        rope_coeffs<NEOX>(ka.cos_sin + kpos * 64, chunk_of(lane & 7), KC, KS);
+    }
+    uint8_t* qs = qa.q_scale_out + t * 64 * (int64_t)J;
+    if (g8 == 0) {
+        if (qa.weights != nullptr)
+            for (int h = lane; h < H; h += 64) qa.weights_out[t * H + h] = qa.weights[t * H + h];
+        const int used = H >> 4;
+        for (int i = lane; i < 64 * J; i += 64)
+            if ((i % J) >= used) qs[i] = 0;
+    }
+    const int64_t pos = clamped_position(qa.positions, qa.pos64, t, qa.max_pos);
+    float C[8], S[8];
+    rope_coeffs<NEOX>(qa.cos_sin + pos * 64, chunk_of(lane & 7), C, S);
+    const int ro = qa.rope_offset;
+    if (!HAD) {
+        const int c = chunk_of(lane & 7);
+        const int h = 8 * g8 + (lane >> 3);
+        const uint16_t* qt = qa.q + (t * H + h) * 128 + 8 * c;
+        const uint4 p = load16_stream(qt + 64 - ro);
+        const uint4 r = load16_stream(qt + ro);
+        const Q8 qp = quant8(p, qa.e_lo);
+        const Q8 qr = quant8(rope8<NEOX>(r, C, S), qa.e_lo);
+        uint8_t* o = qa.q_out + (t * H + h) * 64 + 4 * c;
+        store4_stream(o + (64 - ro) / 2, qp.codes);
+        store4_stream(o + ro / 2, qr.codes);
+        if ((lane & 3) == 0) {
+            const int gp = (64 - ro) / 32 + (c >> 2), gr = ro / 32 + (c >> 2);
+            qs[(gp * 16 + (h & 15)) * J + (h >> 4)] = (uint8_t)qp.e;
+            qs[(gr * 16 + (h & 15)) * J + (h >> 4)] = (uint8_t)qr.e;
+        }
+    } else {
+        const int c = chunk_of(lane & 15);
+        const bool rot_lane = (c >> 3) == (ro >> 6);
+        const int h0 = 8 * g8 + (lane >> 4), h1 = h0 + 4;
+        const uint4 v0 = load16_stream(qa.q + (t * H + h0) * 128 + 8 * c);
+        const uint4 v1 = load16_stream(qa.q + (t * H + h1) * 128 + 8 * c);
+        const Q8 q0 = quant8(hadamard8(select4(rot_lane, rope8<NEOX>(v0, C, S), v0), c), qa.e_lo);
+        const Q8 q1 = quant8(hadamard8(select4(rot_lane, rope8<NEOX>(v1, C, S), v1), c), qa.e_lo);
+        store4_stream(qa.q_out + (t * H + h0) * 64 + 4 * c, q0.codes);
+        store4_stream(qa.q_out + (t * H + h1) * 64 + 4 * c, q1.codes);
+        if ((lane & 3) == 0) {
+            const int g = c >> 2;
+            qs[(g * 16 + (h0 & 15)) * J + (h0 >> 4)] = (uint8_t)q0.e;
+            qs[(g * 16 + (h1 & 15)) * J + (h1 >> 4)] = (uint8_t)q1.e;
+        }
+    }
+    if (krow && kslot >= 0 && kslot < ka.nslots) k_row<NEOX, NORM, HAD>(ka, kv, kslot, lane, KC, KS);
+}
+
 // ---- dequantization (debug reader) -------------------------------------------
 // One thread per 8 consecutive values (4 code bytes).
 __device__ __forceinline__ float e2m1_value(uint32_t nib) {
@@ -295,8 +373,31 @@ __global__ __launch_bounds__(256) void dequant_kernel(DArgs a) {
 }  // namespace
 
 
+// a small batch goes to qk_small_kernel (see there)
+constexpr int64_t kSmallBatchTokens = 512;
+
+template <bool WITH_KEY>
+hipError_t launch_small(const QArgs& qa, const KArgs& ka, bool is_neox, bool hadamard,
+                        hipStream_t stream) {
+    const int64_t waves = qa.T * (int64_t)(qa.H / 8);
+    const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    const bool norm = WITH_KEY && ka.gamma != nullptr;
+    const int sel = (is_neox ? 4 : 0) | (hadamard ? 2 : 0) | (norm ? 1 : 0);
+    switch (sel) {
+        case 0: return launch2(qk_small_kernel<false, false, false, WITH_KEY>, blocks, 0, stream, qa, ka);
+        case 1: return launch2(qk_small_kernel<false, false, true, WITH_KEY>, blocks, 0, stream, qa, ka);
+        case 2: return launch2(qk_small_kernel<false, true, false, WITH_KEY>, blocks, 0, stream, qa, ka);
+        case 3: return launch2(qk_small_kernel<false, true, true, WITH_KEY>, blocks, 0, stream, qa, ka);
+        case 4: return launch2(qk_small_kernel<true, false, false, WITH_KEY>, blocks, 0, stream, qa, ka);
+        case 5: return launch2(qk_small_kernel<true, false, true, WITH_KEY>, blocks, 0, stream, qa, ka);
+        case 6: return launch2(qk_small_kernel<true, true, false, WITH_KEY>, blocks, 0, stream, qa, ka);
+        default: return launch2(qk_small_kernel<true, true, true, WITH_KEY>, blocks, 0, stream, qa, ka);
+    }
+}
+
 hipError_t launch_q_rope_pack(const QArgs& a, bool is_neox, bool hadamard, hipStream_t stream) {
     if (a.T == 0) return hipSuccess;
+    if (a.T < kSmallBatchTokens) return launch_small<false>(a, KArgs{}, is_neox, hadamard, stream);
     const int64_t blocks = (a.T + kWavesPerBlock - 1) / kWavesPerBlock;
     const size_t lds = (size_t)kWavesPerBlock * 16 * a.J * sizeof(uint32_t);
     if (hadamard)
@@ -327,6 +428,7 @@ hipError_t launch_k_rope_pack_store(const KArgs& a, bool is_neox, bool hadamard,
 hipError_t launch_qk_rope_pack_store(const QArgs& qa, const KArgs& ka, bool is_neox, bool hadamard,
                                      hipStream_t stream) {
     if (qa.T == 0) return hipSuccess;
+    if (qa.T < kSmallBatchTokens) return launch_small<true>(qa, ka, is_neox, hadamard, stream);
     const int64_t blocks = (qa.T + kWavesPerBlock - 1) / kWavesPerBlock;
     const size_t lds = (size_t)kWavesPerBlock * 16 * qa.J * sizeof(uint32_t);
     const bool norm = ka.gamma != nullptr;

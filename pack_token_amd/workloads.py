@@ -203,7 +203,7 @@ def edge_mix(seed: int = 1, T: int = 300, H: int = 64, positions_int32: bool = F
     positions = rng.integers(0, max_pos, T, dtype=np.int64)
     if positions_int32:
         positions = positions.astype(np.int32)
-    NB = 8
+    NB = 8 if T <= 8 * KV_BLOCK else -(-T // KV_BLOCK) + 1
     slots = rng.permutation(NB * KV_BLOCK)[:T].astype(np.int64)
     n_skip = max(1, round(0.05 * T)) if T else 0
     if n_skip:

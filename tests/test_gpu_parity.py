@@ -32,8 +32,9 @@ def test_tiny(fused):
 
 @FUSED
 @pytest.mark.parametrize("pos32", [False, True])
-def test_edge_mix(pos32, fused):
-    check(workloads.edge_mix(positions_int32=pos32), fused=fused)
+@pytest.mark.parametrize("T", [300, 700])
+def test_edge_mix(T, pos32, fused):
+    check(workloads.edge_mix(T=T, positions_int32=pos32), fused=fused)
 
 
 @FUSED
@@ -52,8 +53,9 @@ def test_sweep(T, H, is_neox, rope_offset, fused):
 @pytest.mark.parametrize("had", [False, True])
 def test_modes_ragged(is_neox, rope_offset, norm, had, fused):
     """Every kernel variant on a ragged token count (not a multiple of the 4
-    or 16 tokens a block covers) and 16, 48 and 80 heads."""
-    for T, H in [(1, 16), (37, 48), (301, 80)]:
+    or 16 tokens a block covers) and 16, 48 and 80 heads; below 512 tokens the
+    query side runs the small-batch kernel, at 613 the per-token kernels."""
+    for T, H in [(1, 16), (37, 48), (301, 80), (613, 48)]:
         wl = workloads.sweep_case(7 * T + H, T, H, is_neox, rope_offset)
         wl.apply_hadamard = had
         if norm:
