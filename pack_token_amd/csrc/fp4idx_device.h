@@ -326,12 +326,12 @@ hipError_t launch(K kernel, int64_t blocks, size_t lds, hipStream_t stream, cons
 
 template <typename K>
 hipError_t launch2(K kernel, int64_t blocks, size_t lds, hipStream_t stream, const QArgs& qa,
-                   const KArgs& ka) {
+                   const KArgs& ka, unsigned threads = kBlock) {
     QArgs q = qa;
     KArgs k = ka;
     void* args[] = {&q, &k};
     return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)blocks),
-                           dim3(kBlock), args, lds, stream);
+                           dim3(threads), args, lds, stream);
 }
 
 }  // namespace

@@ -203,24 +203,37 @@ __global__ __launch_bounds__(kBlock) void k_row_kernel(KArgs a) {
 }
 
 // Both sides of a token in one launch (ROCm/aiter PR 5484: one kernel writes
-// all five outputs).  One wavefront per token for the query heads as above;
-// wavefront 0 of each block also does the key rows of the block's 4 tokens,
-// one per 16-lane row (rather than every wavefront doing its own key on a
-// quarter of its lanes).  The key loads are issued before the query work.
+// all five outputs).  One wavefront per token for the query heads as above,
+// and the key rows of the block's 4 tokens one per 16-lane row:
+//   without the Hadamard, on a fifth wavefront of the block (the query side is
+//     memory-bound and the extra wavefront fills idle issue slots: 443 -> 436
+//     us at 131072 x 64);
+//   with it, on wavefront 0 after its query token, its key loads issued first
+//     (a fifth wavefront competes for the VALU there: 85 -> 89 us at 16384).
 // The RoPE coefficients of lane L for a key row are those of slice chunk
-// chunk_of(L & 15) & 7 = chunk_of(L & 7).
+// chunk_of(L & 15) & 7 = chunk_of(L & 7).  Rows past T and rows whose slot is
+// outside the cache leave as a whole 16-lane row.
 template <bool NEOX, bool HAD, bool NORM>
-__global__ __launch_bounds__(kBlock) void qk_kernel(QArgs qa, KArgs ka) {
+__global__ __launch_bounds__(HAD ? kBlock : kBlock + 64) void qk_kernel(QArgs qa, KArgs ka) {
     extern __shared__ uint32_t smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t tk = (int64_t)blockIdx.x * kWavesPerBlock + (lane >> 4);
+    if (!HAD && wave == kWavesPerBlock) {
+        if (tk >= ka.T) return;
+        const uint4 kv = load16_stream(ka.k + tk * 128 + 8 * chunk_of(lane & 15));
+        const int64_t kslot = ka.slot_mapping[tk];
+        const int64_t kpos = clamped_position(ka.positions, ka.pos64, tk, ka.max_pos);
+        float KC[8], KS[8];
+        rope_coeffs<NEOX>(ka.cos_sin + kpos * 64, chunk_of(lane & 7), KC, KS);
+        if (kslot < 0 || kslot >= ka.nslots) return;
+        k_row<NEOX, NORM, HAD>(ka, kv, kslot, lane & 15, KC, KS);
+        return;
+    }
     const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
     if (t >= qa.T) return;
     uint32_t* sc = smem + wave * 16 * qa.J;
-    // key row of token tk on the 16-lane row lane / 16 of wavefront 0; rows past
-    // T and rows whose slot is outside the cache leave as a whole row
-    const int64_t tk = (int64_t)blockIdx.x * kWavesPerBlock + (lane >> 4);
-    const bool krow = wave == 0 && tk < ka.T;
+    const bool krow = HAD && wave == 0 && tk < ka.T;
     uint4 kv = make_uint4(0u, 0u, 0u, 0u);
     int64_t kslot = -1;
     float KC[8], KS[8];
@@ -433,13 +446,14 @@ hipError_t launch_qk_rope_pack_store(const QArgs& qa, const KArgs& ka, bool is_n
     const size_t lds = (size_t)kWavesPerBlock * 16 * qa.J * sizeof(uint32_t);
     const bool norm = ka.gamma != nullptr;
     const int sel = (is_neox ? 4 : 0) | (hadamard ? 2 : 0) | (norm ? 1 : 0);
+    const unsigned kw = kBlock + 64;  // a fifth wavefront for the key rows (no Hadamard)
     switch (sel) {
-        case 0: return launch2(qk_kernel<false, false, false>, blocks, lds, stream, qa, ka);
-        case 1: return launch2(qk_kernel<false, false, true>, blocks, lds, stream, qa, ka);
+        case 0: return launch2(qk_kernel<false, false, false>, blocks, lds, stream, qa, ka, kw);
+        case 1: return launch2(qk_kernel<false, false, true>, blocks, lds, stream, qa, ka, kw);
         case 2: return launch2(qk_kernel<false, true, false>, blocks, lds, stream, qa, ka);
         case 3: return launch2(qk_kernel<false, true, true>, blocks, lds, stream, qa, ka);
-        case 4: return launch2(qk_kernel<true, false, false>, blocks, lds, stream, qa, ka);
-        case 5: return launch2(qk_kernel<true, false, true>, blocks, lds, stream, qa, ka);
+        case 4: return launch2(qk_kernel<true, false, false>, blocks, lds, stream, qa, ka, kw);
+        case 5: return launch2(qk_kernel<true, false, true>, blocks, lds, stream, qa, ka, kw);
         case 6: return launch2(qk_kernel<true, true, false>, blocks, lds, stream, qa, ka);
         default: return launch2(qk_kernel<true, true, true>, blocks, lds, stream, qa, ka);
     }
