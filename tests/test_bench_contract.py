@@ -1,0 +1,28 @@
+"""CPU checks of bench.py's contract that need no GPU: more than one GPU is
+refused with a message (the path has no collective; every GPU runs its own
+tokens), and the algorithmic byte counts match their stated formulas."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_byte_counts():
+    import bench
+    # query: 256H q + 4H weights + 8 position + 256 cos/sin + 64H codes + 64J scales + 4H weights_out
+    assert bench.q_bytes_per_token(64) == 16384 + 256 + 8 + 256 + 4096 + 256 + 256
+    assert bench.k_bytes_per_token() == 256 + 8 + 64 + 4
+    assert bench.step_bytes_per_token(64) == 21844
+    assert bench.step_bytes_per_token(64) * 131072 == 2863136768
+    assert bench.q_bytes_per_token(48) == 256 * 48 + 4 * 48 + 8 + 256 + 64 * 48 + 64 * 4 + 4 * 48
+    assert bench.sglang_q_bytes_per_token(64) == 21000
+    assert bench.fp8_q_bytes_per_token(64) == 25224
