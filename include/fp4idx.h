@@ -98,7 +98,7 @@ extern "C" {
  *   weights      fp32 [T, H] or NULL, 4-byte aligned.
  *   T, H         tokens (>= 0), heads (multiple of 16, <= 2048).
  *   D, R, group_size   must be 128, 64, 32.
- *   rope_offset  first rotated dim: 64 (the "RoPE tail") or 0.
+ *   rope_offset  first rotated dim: 64 (the tail of the row) or 0.
  *   is_neox      1: pairs (i, i+32) of the slice; 0: pairs (2i, 2i+1).
  *                Rotation a' = bf16(a*c - b*s), b' = bf16(b*c + a*s), each
  *                product rounded to fp32 separately (no fused multiply-add).
@@ -158,7 +158,7 @@ int fp4idx_k_rope_pack_store(const void* k, const void* positions, int positions
 /*
  * fp4idx_qk_rope_pack_store -- both sides of the producer in one launch, as
  * the pages' producer writes all five outputs from one kernel (ROCm/aiter PR
- * 5484 "Verification": zero mismatching bytes "across all five outputs").
+ * 5484 "Verification" compares all five outputs of that kernel).
  * Arguments mean what they mean for fp4idx_q_rope_pack and
  * fp4idx_k_rope_pack_store (q and k share T, positions, cos_sin, rope_offset,
  * is_neox, apply_hadamard and scale_floor); every check of both calls
@@ -328,7 +328,7 @@ int fp4idx_dequant_debug(int which, const uint8_t* packed, const uint8_t* scales
 /*
  * fp4idx_paged_mqa_logits -- the scorer that consumes the producer's bytes
  * (ROCm/aiter PR 5484, intro: flydsl_pa_mqa_logits_fp4 scores the FP4 keys
- * "straight out of the paged cache"; "API": the MFMA consumes the per-group
+ * directly from the paged cache; "API": the MFMA consumes the per-group
  * e8m0 scales directly and the scorer applies its own fp32 weights_scale).
  * Runs on the gfx950 scaled-FP4 matrix cores.
  *

@@ -23,7 +23,8 @@
  *
  * Readings where the pages are silent (each is listed in the design notes):
  *   - RoPE acts on dims [rope_offset, rope_offset+64) of a 128-dim row
- *     (sglang's kernel is a "RoPE tail", so the default offset is 64).
+ *     (sglang's kernel rotates the tail of the row, so the default
+ *     offset is 64).
  *   - cos/sin table: fp32 [max_pos, 64], cols 0..31 cos, 32..63 sin; pair i
  *     uses column i.  neox pairs (i, i+32); interleaved pairs (2i, 2i+1).
  *   - RoPE: a' = bf16(a*c - b*s), b' = bf16(b*c + a*s), products rounded
@@ -222,7 +223,7 @@ static int check_shape(int D, int R, int rope_offset, int group_size) {
 /* public: query path                                                   */
 /* q_out [T,H,64]; q_scale_out [T,1,4,16,J], J = round_up(H/16, 4),     */
 /* entry [t,0,g,h%16,h/16] = e, pad entries 0 ([aiter-5484] API and     */
-/* Verification: "qs_pad zero-padding"); weights_out = plain weights.   */
+/* Verification, which tests the zero padding); weights_out = plain.    */
 /* ------------------------------------------------------------------ */
 int oracle_q_rope_pack(const uint16_t* q, const void* positions, int positions_int64,
                        const float* cos_sin, int64_t max_pos, const float* weights,
@@ -257,7 +258,7 @@ int oracle_q_rope_pack(const uint16_t* q, const void* positions, int positions_i
 /* kv_cache [NB,1,4,BS,16]: kv_cache[blk,0,g,pos,:] = the 16 bytes of   */
 /* group g ([aiter-5484] API); kv_cache_scale [NB,1,4,BS] with the       */
 /* exponent of group g at (pos%16)*(BS/16) + pos/16 ([aiter-4029]       */
-/* Changes, "KV e8m0 scale layout fix").                                */
+/* Changes: the interleaved KV scale layout).                          */
 /* ------------------------------------------------------------------ */
 int oracle_k_rope_pack_store(const uint16_t* k, const void* positions, int positions_int64,
                              const float* cos_sin, int64_t max_pos, const int64_t* slot_mapping,
@@ -473,7 +474,7 @@ int oracle_paged_mqa_logits(const uint8_t* q_out, const uint8_t* q_scale_out, co
 /* sglang-compatible mode ([sglang-39656] Summary and review).          */
 /* Two quantization stages with their own floors: stage 1 fake-quantizes */
 /* each 32-group to the UE8M0 E2M1 grid (values, not codes); stage 2     */
-/* ("the indexer packer") recomputes the exponent from the fake-quant    */
+/* (the packer) recomputes the exponent from the fake-quant            */
 /* values with its own floor and packs codes whose sign bit is set only  */
 /* when the magnitude code is nonzero (sign = (x < 0) & (idx != 0)).     */
 /* Record: 64 code bytes then the 4 stage-2 exponents = 68 bytes.        */
@@ -524,8 +525,8 @@ int oracle_q_rope_pack_sglang(const uint16_t* q, const void* positions, int posi
 /* key side: optional RMSNorm, RoPE, two stages, 68-byte record at slot; slot 0
    (and any slot outside [1, num_slots)) publishes nothing.  A compressed key
    row stands for compress_ratio consecutive tokens and is rotated at the
-   first position of that group ([sglang-39656] Summary: "RoPE at the group's
-   first position"): pos - pos % compress_ratio. */
+   first position of that group ([sglang-39656] Summary):
+   pos - pos % compress_ratio. */
 int oracle_k_rope_pack_store_sglang(const uint16_t* k, const void* positions, int positions_int64,
                                     const float* cos_sin, int64_t max_pos,
                                     const int64_t* slot_mapping, const uint16_t* k_norm_gamma,

@@ -1,9 +1,9 @@
 """Pins for the oracle's sglang-compatible mode (sgl-project/sglang PR 39656:
 "Summary" -- two quantization stages and the 68-byte index-K record of 64
 e2m1 bytes plus four block exponents; review -- the clear_negative_zero mask
-and the packer's sign = (x < 0) & (idx != 0); "the indexer packer has a
-different scale floor from fake_quant_fp4, so directly packing the first
-stage is not equivalent")."""
+and the packer's sign = (x < 0) & (idx != 0); the packer's floor differs
+from the fake quant's, so packing the first stage directly gives other
+bytes)."""
 import numpy as np
 
 import oracle
