@@ -75,42 +75,62 @@ def measured_traffic(path=TRAFFIC_FILE, sources=MAIN_SOURCES):
     return int(rec["bytes_per_launch"])
 
 
+def host_cpu() -> dict:
+    """The host the CPU baseline ran on: CPU model, logical CPUs, CPUs usable here."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "host_cpu_count": os.cpu_count(),
+            "usable_cpus": len(os.sched_getaffinity(0))}
+
+
+def median_wall(fn, reps: int = 3) -> float:
+    """Median wall time (s) of reps calls of fn."""
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return sorted(ts)[len(ts) // 2]
+
+
+def oracle_baseline(run, n: int, what: str, T: int, threads: int = 1) -> dict:
+    """cpu_baseline record for run() processing n tokens (median of 3 walls)."""
+    dt = median_wall(run)
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {T} tokens ({what}), {threads} thread(s), median of 3 "
+                      f"runs, {dt:.2f} s wall", **host_cpu()}
+
+
 def cpu_baseline(wl, n_tokens: int, threads: int):
     """The CPU oracle (test infrastructure) on the first n_tokens tokens of the
-    same workload, query + key path, timed on the host cores."""
-    import numpy as np
-
+    same workload, query + key path, timed on the host cores (median of 3 runs),
+    and single-threaded on a smaller slice."""
     import oracle
 
-    sl = slice(0, n_tokens)
-    kv, ks = wl.empty_cache()
-    t0 = time.perf_counter()
-    oracle.q_rope_pack(wl.q[sl], wl.positions[sl], wl.cos_sin, wl.weights[sl],
-                       is_neox=wl.is_neox, rope_offset=wl.rope_offset,
-                       apply_hadamard=wl.apply_hadamard, threads=threads)
-    oracle.k_rope_pack_store(wl.k[sl], wl.positions[sl], wl.cos_sin, wl.slot_mapping[sl], kv, ks,
-                             k_norm_gamma=wl.k_norm_gamma, k_norm_eps=wl.k_norm_eps,
-                             is_neox=wl.is_neox, rope_offset=wl.rope_offset,
-                             apply_hadamard=wl.apply_hadamard, threads=threads)
-    dt = time.perf_counter() - t0
-    # single-threaded on a smaller slice of the same workload
+    def run(n, th):
+        kv, ks = wl.empty_cache()
+        oracle.q_rope_pack(wl.q[:n], wl.positions[:n], wl.cos_sin, wl.weights[:n],
+                           is_neox=wl.is_neox, rope_offset=wl.rope_offset,
+                           apply_hadamard=wl.apply_hadamard, threads=th)
+        oracle.k_rope_pack_store(wl.k[:n], wl.positions[:n], wl.cos_sin, wl.slot_mapping[:n], kv,
+                                 ks, k_norm_gamma=wl.k_norm_gamma, k_norm_eps=wl.k_norm_eps,
+                                 is_neox=wl.is_neox, rope_offset=wl.rope_offset,
+                                 apply_hadamard=wl.apply_hadamard, threads=th)
+
+    rec = oracle_baseline(lambda: run(n_tokens, threads), n_tokens,
+                          "query + key path of the same workload", wl.T, threads)
     n1 = min(n_tokens, 8192)
-    kv, ks = wl.empty_cache()
-    t1 = time.perf_counter()
-    oracle.q_rope_pack(wl.q[:n1], wl.positions[:n1], wl.cos_sin, wl.weights[:n1],
-                       is_neox=wl.is_neox, rope_offset=wl.rope_offset,
-                       apply_hadamard=wl.apply_hadamard, threads=1)
-    oracle.k_rope_pack_store(wl.k[:n1], wl.positions[:n1], wl.cos_sin, wl.slot_mapping[:n1], kv,
-                             ks, k_norm_gamma=wl.k_norm_gamma, k_norm_eps=wl.k_norm_eps,
-                             is_neox=wl.is_neox, rope_offset=wl.rope_offset,
-                             apply_hadamard=wl.apply_hadamard, threads=1)
-    dt1 = time.perf_counter() - t1
-    del np
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n_tokens} of {wl.T} tokens of the same workload (query + key "
-                      f"path), {threads} threads, {dt:.2f} s wall",
-            "single_thread_value": n1 / dt1,
-            "single_thread_sample": f"first {n1} tokens, 1 thread, {dt1:.2f} s wall"}
+    dt1 = median_wall(lambda: run(n1, 1))
+    rec["single_thread_value"] = n1 / dt1
+    rec["single_thread_sample"] = f"first {n1} tokens, 1 thread, median of 3 runs, {dt1:.2f} s wall"
+    return rec
 
 
 FP4_MFMA_PEAK_TFLOPS = 10100.0
@@ -205,16 +225,15 @@ def bench_fp8(args, dev):
     }
     if not args.no_cpu_baseline:
         n = min(args.cpu_sample_tokens, T, 16384)
-        c0 = time.perf_counter()
-        oracle.q_rope_pack_fp8(wl.q[:n], wl.positions[:n], wl.cos_sin, wl.weights[:n])
-        rkv = np.zeros((wl.NB, 64, 128), np.uint8)
-        rks = np.zeros((wl.NB, 64), np.float32)
-        oracle.k_rope_pack_store_fp8(wl.k[:n], wl.positions[:n], wl.cos_sin, wl.slot_mapping[:n],
-                                     rkv, rks)
-        dt = time.perf_counter() - c0
-        rec["cpu_baseline"] = {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                               "sample": f"first {n} of {T} tokens (query + key, ue8m0), "
-                                         f"1 thread, {dt:.2f} s wall"}
+
+        def run():
+            oracle.q_rope_pack_fp8(wl.q[:n], wl.positions[:n], wl.cos_sin, wl.weights[:n])
+            rkv = np.zeros((wl.NB, 64, 128), np.uint8)
+            rks = np.zeros((wl.NB, 64), np.float32)
+            oracle.k_rope_pack_store_fp8(wl.k[:n], wl.positions[:n], wl.cos_sin,
+                                         wl.slot_mapping[:n], rkv, rks)
+
+        rec["cpu_baseline"] = oracle_baseline(run, n, "query + key, ue8m0", T)
     print(json.dumps(rec), flush=True)
 
 
@@ -279,13 +298,10 @@ def bench_fake_quant(args, dev):
     }
     if not args.no_cpu_baseline:
         n = min(args.cpu_sample_tokens, T, 4096)
-        c0 = time.perf_counter()
-        oracle.rope_fake_quant(wl.q[:n], wl.positions[:n], wl.cos_sin, rows_per_position=H,
-                               mode=oracle.FQ_E4M3_16)
-        dt = time.perf_counter() - c0
-        rec["cpu_baseline"] = {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                               "sample": f"first {n} of {T} tokens ({n * H} rows, e4m3_16), "
-                                         f"1 thread, {dt:.2f} s wall"}
+        rec["cpu_baseline"] = oracle_baseline(
+            lambda: oracle.rope_fake_quant(wl.q[:n], wl.positions[:n], wl.cos_sin,
+                                           rows_per_position=H, mode=oracle.FQ_E4M3_16),
+            n, f"{n * H} rows, e4m3_16", T)
     print(json.dumps(rec), flush=True)
 
 
@@ -371,15 +387,14 @@ def bench_sglang(args, dev):
     }
     if not args.no_cpu_baseline:
         n = min(args.cpu_sample_tokens, T, 16384)
-        c0 = time.perf_counter()
-        oracle.q_rope_pack_sglang(wl.q[:n], wl.positions[:n], wl.cos_sin)
-        ref = np.zeros((n + 1, 68), np.uint8)
-        oracle.k_rope_pack_store_sglang(wl.k[:n], wl.positions[:n], wl.cos_sin,
-                                        np.arange(1, n + 1, dtype=np.int64), ref)
-        dt = time.perf_counter() - c0
-        rec["cpu_baseline"] = {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                               "sample": f"first {n} of {T} tokens (query + key records), "
-                                         f"1 thread, {dt:.2f} s wall"}
+
+        def run():
+            oracle.q_rope_pack_sglang(wl.q[:n], wl.positions[:n], wl.cos_sin)
+            ref = np.zeros((n + 1, 68), np.uint8)
+            oracle.k_rope_pack_store_sglang(wl.k[:n], wl.positions[:n], wl.cos_sin,
+                                            np.arange(1, n + 1, dtype=np.int64), ref)
+
+        rec["cpu_baseline"] = oracle_baseline(run, n, "query + key records", T)
     print(json.dumps(rec), flush=True)
 
 
@@ -570,7 +585,8 @@ def main():
 
     def timed(calls, K, W):
         """Run W untimed then K timed steps of `calls` (launched back to back on
-        `stream`); returns (ms per step, [mean ms of each call's launch])."""
+        `stream`); returns (ms per step, [mean ms of each call's launch],
+        [median ms of each call's launch])."""
         for _ in range(W):
             for c in calls:
                 c()
@@ -587,9 +603,9 @@ def main():
                 ev[i][j + 1].record(stream)
         t1.record(stream)
         torch.cuda.synchronize()
-        per_call = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]))
-                    for j in range(len(calls))]
-        return t0.elapsed_time(t1) / K, per_call
+        per_launch = [[e[j].elapsed_time(e[j + 1]) for e in ev] for j in range(len(calls))]
+        return (t0.elapsed_time(t1) / K, [float(np.mean(d)) for d in per_launch],
+                [float(np.median(d)) for d in per_launch])
 
     use_graph = args.graph == "on" or (args.graph == "auto" and wl.name == "decode")
 
@@ -614,14 +630,14 @@ def main():
 
     K = args.steps
     # per-launch durations always come from eager launches bracketed by events
-    ms_per_step, (fused_ms,) = timed([qk_call], K, args.warmup)
-    two_ms, (q_ms, k_ms) = timed([q_call, k_call], K, args.warmup)
+    ms_per_step, (fused_ms,), (fused_med_ms,) = timed([qk_call], K, args.warmup)
+    two_ms, (q_ms, k_ms), _ = timed([q_call, k_call], K, args.warmup)
     if use_graph:
         # step time from graph replays: K steps = ceil(K / G) replays of G steps
         reps = -(-K // G)
         K = reps * G
-        g_ms, _ = timed([graphed([qk_call])], reps, max(1, args.warmup // G))
-        g2_ms, _ = timed([graphed([q_call, k_call])], reps, max(1, args.warmup // G))
+        g_ms, _, _ = timed([graphed([qk_call])], reps, max(1, args.warmup // G))
+        g2_ms, _, _ = timed([graphed([q_call, k_call])], reps, max(1, args.warmup // G))
         eager_ms_per_step, eager_two_ms = ms_per_step, two_ms
         ms_per_step, two_ms = g_ms / G, g2_ms / G
 
@@ -660,8 +676,12 @@ def main():
                      "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": step_bytes,
-                     "launch_us": fused_ms * 1e3},
+                     "launch_us": fused_ms * 1e3, "launch_us_median": fused_med_ms * 1e3},
     }
+    if wl.name == "prefill_norm_rotate":
+        rec["cache_note"] = ("%.1f MB per step against a 256 MB Infinity Cache: part of the "
+                             "step's bytes can stay cache-resident between back-to-back steps, "
+                             "so the HBM fraction is an upper estimate" % (step_bytes / 1e6))
     if use_graph:
         rec["eager_ms_per_step"] = eager_ms_per_step
         rec["two_call_step"]["eager_ms_per_step"] = eager_two_ms

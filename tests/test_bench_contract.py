@@ -1,6 +1,7 @@
 """CPU checks of bench.py's contract that need no GPU: more than one GPU is
 refused with a message (the path has no collective; every GPU runs its own
-tokens), and the algorithmic byte counts match their stated formulas."""
+tokens), the algorithmic byte counts match their stated formulas, and the CPU
+baseline record is complete."""
 import os
 import subprocess
 import sys
@@ -26,3 +27,19 @@ def test_byte_counts():
     assert bench.q_bytes_per_token(48) == 256 * 48 + 4 * 48 + 8 + 256 + 64 * 48 + 64 * 4 + 4 * 48
     assert bench.sglang_q_bytes_per_token(64) == 21000
     assert bench.fp8_q_bytes_per_token(64) == 25224
+
+
+def test_cpu_baseline_record():
+    """The oracle baseline record carries the contract's keys plus the host's
+    CPU model and counts, timed as a median of 3 runs."""
+    import bench
+    from pack_token_amd import workloads
+
+    wl = workloads.RECIPES["tiny"]()
+    rec = bench.cpu_baseline(wl, wl.T, 2)
+    for key in ("value", "unit", "cores", "kind", "sample", "cpu_model", "host_cpu_count",
+                "usable_cpus", "single_thread_value", "single_thread_sample"):
+        assert key in rec, key
+    assert rec["kind"] == "oracle" and rec["cores"] == 2 and rec["value"] > 0
+    assert rec["host_cpu_count"] == os.cpu_count()
+    assert "median of 3" in rec["sample"]
