@@ -93,6 +93,7 @@ __device__ __forceinline__ void q_split_token(const QArgs& a, int64_t t, int lan
 // With the Hadamard every output mixes the whole 128-row, so a wave-load is 4
 // full heads (16 lanes each, lane chunk c = chunk_of(lane & 15)); RoPE is
 // computed on every lane and kept only on the lanes of the rotated slice.
+// H is a multiple of 16 (checked by the C-ABI layer).
 template <bool NEOX>
 __device__ __forceinline__ void q_row_token(const QArgs& a, int64_t t, int lane, uint8_t* scb,
                                             const float C[8], const float S[8]) {
@@ -106,19 +107,22 @@ __device__ __forceinline__ void q_row_token(const QArgs& a, int64_t t, int lane,
     const uint16_t* qt = a.q + t * (int64_t)H * 128 + hsub * 128 + 8 * c;
     uint8_t* ot = a.q_out + t * (int64_t)H * 64 + hsub * 64 + 4 * c;
 
-    for (int hb = 0; hb < H; hb += 8) {
-        const uint4 v0 = load16_stream(qt + hb * 128);
-        const uint4 v1 = load16_stream(qt + (hb + 4) * 128);
-        const uint4 w0 = hadamard8(select4(rot_lane, rope8<NEOX>(v0, C, S), v0), c);
-        const uint4 w1 = hadamard8(select4(rot_lane, rope8<NEOX>(v1, C, S), v1), c);
-        const Q8 q0 = quant8(w0, a.e_lo);
-        const Q8 q1 = quant8(w1, a.e_lo);
-        store4_stream(ot + hb * 64, q0.codes);
-        store4_stream(ot + (hb + 4) * 64, q1.codes);
-        if (writer) {
-            const int h0 = hb + hsub, h1 = h0 + 4;
-            scb[(g * 16 + (h0 & 15)) * J + (h0 >> 4)] = (uint8_t)q0.e;
-            scb[(g * 16 + (h1 & 15)) * J + (h1 >> 4)] = (uint8_t)q1.e;
+    // 16 heads (4 wave-loads) per step, all loads issued before any compute:
+    // 4% faster at 16384 x 64 than 8 heads per step; 32 heads per step, or
+    // the next step's loads issued ahead, measured slower (more VGPRs).
+    for (int hb = 0; hb < H; hb += 16) {
+        uint4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = load16_stream(qt + (hb + 4 * u) * 128);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint4 w = hadamard8(select4(rot_lane, rope8<NEOX>(v[u], C, S), v[u]), c);
+            const Q8 q = quant8(w, a.e_lo);
+            store4_stream(ot + (hb + 4 * u) * 64, q.codes);
+            if (writer) {
+                const int h = hb + 4 * u + hsub;
+                scb[(g * 16 + (h & 15)) * J + (h >> 4)] = (uint8_t)q.e;
+            }
         }
     }
 }
