@@ -142,7 +142,9 @@ __device__ __forceinline__ Q8 quant8(uint4 v, int e_lo) {
     m = max(m, dpp<kDppXor2>(m));
     const int e = max((int)((m + 0x3Fu) >> 7) - 2, e_lo);
     const float scale = __uint_as_float((uint32_t)e << 23);
-    uint32_t r = 0;
+    // each converter writes one byte of its first operand and the four calls
+    // cover all of it, so a dead value seeds the chain (no zeroing move)
+    uint32_t r = v.x;
     r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, v.x), scale, 0);
     r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, v.y), scale, 1);
     r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, v.z), scale, 2);

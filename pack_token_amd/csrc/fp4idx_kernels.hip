@@ -90,39 +90,141 @@ __device__ __forceinline__ void q_split_token(const QArgs& a, int64_t t, int lan
     }
 }
 
-// With the Hadamard every output mixes the whole 128-row, so a wave-load is 4
-// full heads (16 lanes each, lane chunk c = chunk_of(lane & 15)); RoPE is
-// computed on every lane and kept only on the lanes of the rotated slice.
-// H is a multiple of 16 (checked by the C-ABI layer).
+// With the Hadamard the query side is bound by VALU issue, not by HBM (with
+// every access made L2-resident it runs in about the same time), so its layout
+// minimises VALU work: a quad of lanes holds one head, lane r = lane & 3 of the
+// quad holding chunks r, r+4, r+8, r+12, i.e. element 32j + 8r + e in x[j][e].
+// Index bits 0-2 (e) and 5-6 (j) are inside the lane and bits 3-4 (r) across
+// the quad, so the neox RoPE partner (slice element + 32) and five of the
+// seven FWHT strides (1, 2, 4, 32, 64) need no lane exchange, RoPE runs only
+// on the two rotated chunks, and each 32-group (row j) is one quad, as quant8
+// expects.  Against 16 lanes per head (RoPE on every lane, four of the seven
+// strides across lanes) this is 2208 instead of 2952 VALU instructions per
+// token at H = 64.
+
+// RoPE coefficients of quad lane r: neox pairs (s, s + 32) with s = 8r + e;
+// interleaved pairs (2i, 2i + 1) with i = 16q + 4r + p for rotated chunk q.
 template <bool NEOX>
-__device__ __forceinline__ void q_row_token(const QArgs& a, int64_t t, int lane, uint8_t* scb,
-                                            const float C[8], const float S[8]) {
+__device__ __forceinline__ void rope_coeffs_quad(const float* cs_row, int r, float C[8],
+                                                 float S[8]) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int i0 = NEOX ? 8 * r + 4 * q : 16 * q + 4 * r;
+        const float4 c4 = *reinterpret_cast<const float4*>(cs_row + i0);
+        const float4 s4 = *reinterpret_cast<const float4*>(cs_row + 32 + i0);
+        C[4 * q] = c4.x, C[4 * q + 1] = c4.y, C[4 * q + 2] = c4.z, C[4 * q + 3] = c4.w;
+        S[4 * q] = s4.x, S[4 * q + 1] = s4.y, S[4 * q + 2] = s4.z, S[4 * q + 3] = s4.w;
+    }
+}
+
+// RoPE of the rotated chunks lo (slice elements 8r + e) and hi (32 + 8r + e),
+// then the bf16 round trip: a' = a c - b s, b' = b c + a s.
+template <bool NEOX>
+__device__ __forceinline__ void rope_quad(float lo[8], float hi[8], const float C[8],
+                                          const float S[8]) {
+    float y[16];
+    if (NEOX) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            y[e] = lo[e] * C[e] - hi[e] * S[e];
+            y[8 + e] = hi[e] * C[e] + lo[e] * S[e];
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const float* x = q ? hi : lo;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const float c = C[4 * q + p], sn = S[4 * q + p];
+                y[8 * q + 2 * p] = x[2 * p] * c - x[2 * p + 1] * sn;
+                y[8 * q + 2 * p + 1] = x[2 * p + 1] * c + x[2 * p] * sn;
+            }
+        }
+    }
+    unpack8(pack8(y), lo);
+    unpack8(pack8(y + 8), hi);
+}
+
+// Natural-order FWHT of the quad's head: strides 1, 2, 4 inside each chunk,
+// 8 and 16 across the quad (quad lanes r ^ 1, r ^ 2), 32 and 64 between the
+// lane's chunks; then the orthonormal scale.
+__device__ __forceinline__ void hadamard_quad(float x[4][8], int r) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (e & h) continue;
+                const float u = x[j][e], w = x[j][e + h];
+                x[j][e] = u + w;
+                x[j][e + h] = u - w;
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fwht_cross<kDppXor1>(x[j], (r & 1) != 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fwht_cross<kDppXor2>(x[j], (r & 2) != 0);
+#pragma unroll
+    for (int h = 1; h < 4; h <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j & h) continue;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float u = x[j][e], w = x[j + h][e];
+                x[j][e] = u + w;
+                x[j + h][e] = u - w;
+            }
+        }
+    }
+    const float sc = __uint_as_float(kHadamardScaleBits);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[j][e] = x[j][e] * sc;
+}
+
+// 16 heads per wave step.  Each lane loads its four 16-byte chunks with the
+// default cache policy: one load instruction covers 64 bytes of every head, the
+// other half of each 128-byte line comes from the next instruction, and L2
+// joins them (streaming loads measured ~12% slower here).  The code bytes go
+// through the wave's 1 KB LDS `stage` so that one 16-byte store per lane writes
+// the 16 heads' 1024 output bytes contiguously.  TAIL: rope_offset == 64 (a
+// template parameter, so the rotated chunks are fixed registers).
+template <bool NEOX, bool TAIL>
+__device__ __forceinline__ void q_quad_token(const QArgs& a, int64_t t, int lane, uint8_t* scb,
+                                             const float C[8], const float S[8], uint32_t* stage) {
     const int H = a.H;
     const int J = a.J;
-    const int c = chunk_of(lane & 15);
-    const int hsub = lane >> 4;
-    const bool rot_lane = (c >> 3) == (a.rope_offset >> 6);
-    const int g = c >> 2;
-    const bool writer = (lane & 3) == 0;
-    const uint16_t* qt = a.q + t * (int64_t)H * 128 + hsub * 128 + 8 * c;
-    uint8_t* ot = a.q_out + t * (int64_t)H * 64 + hsub * 64 + 4 * c;
-
-    // 16 heads (4 wave-loads) per step, all loads issued before any compute:
-    // 4% faster at 16384 x 64 than 8 heads per step; 32 heads per step, or
-    // the next step's loads issued ahead, measured slower (more VGPRs).
+    const int r = lane & 3;
+    const int hs = lane >> 2;
+    const uint16_t* qt = a.q + t * (int64_t)H * 128 + hs * 128 + 8 * r;
     for (int hb = 0; hb < H; hb += 16) {
         uint4 v[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = load16_stream(qt + (hb + 4 * u) * 128);
+        for (int j = 0; j < 4; ++j) v[j] = load16(qt + hb * 128 + 32 * j);
+        float x[4][8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint4 w = hadamard8(select4(rot_lane, rope8<NEOX>(v[u], C, S), v[u]), c);
-            const Q8 q = quant8(w, a.e_lo);
-            store4_stream(ot + (hb + 4 * u) * 64, q.codes);
-            if (writer) {
-                const int h = hb + 4 * u + hsub;
-                scb[(g * 16 + (h & 15)) * J + (h >> 4)] = (uint8_t)q.e;
-            }
+        for (int j = 0; j < 4; ++j) unpack8(v[j], x[j]);
+        rope_quad<NEOX>(x[TAIL ? 2 : 0], x[TAIL ? 3 : 1], C, S);
+        hadamard_quad(x, r);
+        const int h = hb + hs;
+        int eg[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const Q8 q = quant8(pack8(x[g]), a.e_lo);
+            stage[hs * 16 + 4 * g + r] = q.codes;  // bytes 16g + 4r of head hs
+            eg[g] = q.e;
+        }
+        wave_sync();
+        store16_stream(a.q_out + (t * (int64_t)H + hb) * 64 + 16 * lane,
+                       *reinterpret_cast<const uint4*>(stage + 4 * lane));
+        wave_sync();
+        if (r == 0) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) scb[(g * 16 + (h & 15)) * J + (h >> 4)] = (uint8_t)eg[g];
         }
     }
 }
@@ -183,8 +285,12 @@ __global__ __launch_bounds__(kBlock) void q_row_kernel(QArgs a) {
     q_token_prologue(a, t, lane, sc);
     const int64_t pos = clamped_position(a.positions, a.pos64, t, a.max_pos);
     float C[8], S[8];
-    rope_coeffs<NEOX>(a.cos_sin + pos * 64, chunk_of(lane & 7), C, S);
-    q_row_token<NEOX>(a, t, lane, reinterpret_cast<uint8_t*>(sc), C, S);
+    rope_coeffs_quad<NEOX>(a.cos_sin + pos * 64, lane & 3, C, S);
+    __shared__ __attribute__((aligned(16))) uint32_t qstage[kWavesPerBlock * 256];
+    if (a.rope_offset != 0)
+        q_quad_token<NEOX, true>(a, t, lane, reinterpret_cast<uint8_t*>(sc), C, S, qstage + wave * 256);
+    else
+        q_quad_token<NEOX, false>(a, t, lane, reinterpret_cast<uint8_t*>(sc), C, S, qstage + wave * 256);
     q_token_epilogue(a, t, lane, sc);
 }
 
@@ -250,9 +356,19 @@ __global__ __launch_bounds__(HAD ? kBlock : kBlock + 64) void qk_kernel(QArgs qa
     q_token_prologue(qa, t, lane, sc);
     const int64_t pos = clamped_position(qa.positions, qa.pos64, t, qa.max_pos);
     float C[8], S[8];
-    rope_coeffs<NEOX>(qa.cos_sin + pos * 64, chunk_of(lane & 7), C, S);
-    if (HAD) q_row_token<NEOX>(qa, t, lane, reinterpret_cast<uint8_t*>(sc), C, S);
-    else q_split_token<NEOX>(qa, t, lane, reinterpret_cast<uint8_t*>(sc), C, S);
+    if (HAD) {
+        rope_coeffs_quad<NEOX>(qa.cos_sin + pos * 64, lane & 3, C, S);
+        __shared__ __attribute__((aligned(16))) uint32_t qstage[kWavesPerBlock * 256];
+        if (qa.rope_offset != 0)
+            q_quad_token<NEOX, true>(qa, t, lane, reinterpret_cast<uint8_t*>(sc), C, S,
+                                     qstage + wave * 256);
+        else
+            q_quad_token<NEOX, false>(qa, t, lane, reinterpret_cast<uint8_t*>(sc), C, S,
+                                      qstage + wave * 256);
+    } else {
+        rope_coeffs<NEOX>(qa.cos_sin + pos * 64, chunk_of(lane & 7), C, S);
+        q_split_token<NEOX>(qa, t, lane, reinterpret_cast<uint8_t*>(sc), C, S);
+    }
     q_token_epilogue(qa, t, lane, sc);
     if (krow && kslot >= 0 && kslot < ka.nslots)
         k_row<NEOX, NORM, HAD>(ka, kv, kslot, lane & 15, KC, KS);
