@@ -319,7 +319,8 @@ __global__ __launch_bounds__(kBlock) void k_row_kernel(KArgs a) {
 //     memory-bound and the extra wavefront fills idle issue slots: 443 -> 436
 //     us at 131072 x 64);
 //   with it, on wavefront 0 after its query token, its key loads issued first
-//     (a fifth wavefront competes for the VALU there: 85 -> 89 us at 16384).
+//     (a fifth wavefront competes for the VALU there: 66.8 -> 68.4 us at
+//     16384 x 64).
 // The RoPE coefficients of lane L for a key row are those of slice chunk
 // chunk_of(L & 15) & 7 = chunk_of(L & 7).  Rows past T and rows whose slot is
 // outside the cache leave as a whole 16-lane row.
