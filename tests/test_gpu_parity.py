@@ -76,6 +76,21 @@ def test_maximum_heads(had, fused):
 
 
 @FUSED
+@pytest.mark.parametrize("had", [False, True])
+def test_maximum_heads_per_token_kernels(had, fused):
+    """H = 2048 above the small-batch threshold (521 tokens): the per-token
+    kernels loop 128 times over 16 heads, and the Hadamard query path stages
+    its code bytes in LDS beside the 32 KB scale rows; interleaved RoPE on
+    dims 0..63 with key RMSNorm."""
+    wl = workloads.sweep_case(778, 521, 2048, False, 0)
+    wl.apply_hadamard = had
+    rng = np.random.default_rng(778)
+    wl.k_norm_gamma = workloads.to_bf16_bits((1 + 0.1 * rng.standard_normal(128)).astype(np.float32))
+    wl.slot_mapping[5] = -1
+    check(wl, fused=fused)
+
+
+@FUSED
 def test_no_weights_and_scale_floor(fused):
     wl = workloads.edge_mix(seed=21, T=64)
     wl.scale_floor = float(np.float32(1e-10))   # all-zero groups get e = 94
