@@ -152,6 +152,19 @@ __device__ __forceinline__ Q8 quant8(uint4 v, int e_lo) {
     return {r, e};
 }
 
+// ---- division by a constant ---------------------------------------------------
+// RN(x / d) for a non-negative bf16 x and the constants d = 6 and 448, from
+// the reciprocal rc = RN(1/d) and one FMA correction instead of the IEEE
+// division sequence.  Checked on the CPU for every finite bf16 x, subnormal
+// quotients included (0 mismatches for either d).
+constexpr float kRcp6 = 0x1.555556p-3f;    // RN(1/6)
+constexpr float kRcp448 = 0x1.24924ap-9f;  // RN(1/448)
+
+__device__ __forceinline__ float div_const_rn(float x, float d, float rc) {
+    const float y0 = x * rc;
+    return __builtin_fmaf(__builtin_fmaf(-y0, d, x), rc, y0);
+}
+
 // ---- RoPE ------------------------------------------------------------------
 // Slice chunk j (0..7) of the 64-wide rotated slice holds slice elements
 // 8j..8j+7.  Every element is updated as x' = bf16(fl(x*C) + fl(p*S)) where p

@@ -208,7 +208,7 @@ __device__ __forceinline__ uint2 quant_fp8_row(uint4 v, float scale_floor, float
     m = max(m, dpp<kDppXor2>(m));
     m = max(m, dpp<kDppHalfMirror>(m));
     m = max(m, dpp<kDppRor8>(m));
-    float s = __uint_as_float(m << 16) / 448.0f;
+    float s = div_const_rn(__uint_as_float(m << 16), 448.0f, kRcp448);
     s = s < scale_floor ? scale_floor : s;
     s16x2_t lo = {0, 0}, hi = {0, 0};
     if (!FP32) {
@@ -304,7 +304,7 @@ __device__ __forceinline__ float fp8_head_scale(uint4 p, uint4 r, float scale_fl
     m = max(m, dpp<kDppXor1>(m));
     m = max(m, dpp<kDppXor2>(m));
     m = max(m, dpp<kDppHalfMirror>(m));
-    float s = __uint_as_float(m << 16) / 448.0f;
+    float s = div_const_rn(__uint_as_float(m << 16), 448.0f, kRcp448);
     s = s < scale_floor ? scale_floor : s;
     if (!FP32) {
         const uint32_t b = __float_as_uint(s);
@@ -465,7 +465,7 @@ __device__ __forceinline__ uint4 fake_quant8(uint4 v, int e_lo, float scale_floo
                                                      __builtin_elementwise_max(a2, a3));
         uint32_t m = max((uint32_t)m2.x, (uint32_t)m2.y);
         m = max(m, dpp<kDppXor1>(m));
-        float qs = __uint_as_float(m << 16) / 6.0f;
+        float qs = div_const_rn(__uint_as_float(m << 16), 6.0f, kRcp6);
         qs = qs < scale_floor ? scale_floor : qs;
         qs = qs < 448.0f ? qs : 448.0f;
         const s16x2_t sc8 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2_t{0, 0}, qs, qs, 1.0f,
@@ -477,7 +477,12 @@ __device__ __forceinline__ uint4 fake_quant8(uint4 v, int e_lo, float scale_floo
 #pragma unroll
             for (int e = 0; e < 8; ++e) val[e] = __builtin_copysignf(0.0f, x[e]);
         } else {
-            const float r = __frcp_rn(s);  // RN(1/s)
+            // RN(1/s): s is an e4m3fn value (at most 4 significant bits); one
+            // Newton step from any reciprocal within 2 ulp of RN(1/s) lands on
+            // it (checked on the CPU for every positive finite e4m3fn value),
+            // and the hardware reciprocal is within 1 ulp
+            const float r0 = __builtin_amdgcn_rcpf(s);
+            const float r = __builtin_fmaf(r0, __builtin_fmaf(-s, r0, 1.0f), r0);
             float y[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -486,7 +491,7 @@ __device__ __forceinline__ uint4 fake_quant8(uint4 v, int e_lo, float scale_floo
                 const float q = __builtin_fmaf(err, r, y0);
                 y[e] = __builtin_copysignf(__builtin_fminf(__builtin_fabsf(q), 6.0f), x[e]);
             }
-            uint32_t codes = 0;
+            uint32_t codes = __float_as_uint(y[0]);  // all four bytes are overwritten
             codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[0], y[1], 1.0f, 0);
             codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[2], y[3], 1.0f, 1);
             codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[4], y[5], 1.0f, 2);
