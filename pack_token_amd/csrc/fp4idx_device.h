@@ -41,9 +41,13 @@ constexpr int kBlock = 64 * kWavesPerBlock;
 // fp32(1/sqrt(128)), the orthonormal Hadamard scale.
 constexpr uint32_t kHadamardScaleBits = 0x3DB504F3u;
 
+// Rows and banks all enabled, and a lane whose source is invalid gets 0
+// (bound_ctrl) -- the result the form with an explicit old value of 0 gives,
+// without zeroing a register first.  (Every pattern used here reads an active
+// lane of the same row for every lane anyway.)
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
 }
 template <int CTRL>
 __device__ __forceinline__ float dppf(float v) {
