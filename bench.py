@@ -53,11 +53,38 @@ def step_bytes_per_token(H: int) -> int:
     return q_bytes_per_token(H) + k_bytes_per_token()
 
 
+def code_text(src: str) -> str:
+    """C++ source with comments removed and whitespace runs collapsed (string
+    and character literals kept), so that a comment edit does not change the
+    hash of the code a traffic record was taken on."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash(sources=MAIN_SOURCES) -> str:
+    """SHA-256 of the code of the sources a profiled kernel is built from."""
     h = hashlib.sha256()
     for name in sources:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name)) as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()
 
 

@@ -10,9 +10,11 @@
 //   scale row.  The register layout and the shared helpers are in
 //   fp4idx_device.h.
 //
-// Nothing here is a dense contraction, so there is no MFMA: the path is
-// bound by HBM bandwidth, and the kernels are written to stream q once with
-// 16-byte loads and to issue no more VALU work than the stream can hide.
+// Nothing here is a dense contraction, so there is no MFMA.  Without the
+// Hadamard the path is bound by HBM bandwidth, and the kernels stream q once
+// with 16-byte loads and issue no more VALU work than the stream can hide;
+// with it the query side is bound by VALU issue, and its layout (a quad of
+// lanes per head) is chosen to minimise VALU instructions.
 #include "fp4idx_device.h"
 
 namespace fp4idx {
@@ -274,6 +276,9 @@ __global__ __launch_bounds__(kBlock) void q_split_kernel(QArgs a) {
     q_token_epilogue(a, t, lane, sc);
 }
 
+// Query side with the Hadamard: one token per wavefront, a quad of lanes per
+// head (q_quad_token), 1 KB of static LDS per wavefront for the code staging
+// beside the dynamic scale rows.
 template <bool NEOX>
 __global__ __launch_bounds__(kBlock) void q_row_kernel(QArgs a) {
     extern __shared__ uint32_t smem[];

@@ -43,3 +43,16 @@ def test_cpu_baseline_record():
     assert rec["kind"] == "oracle" and rec["cores"] == 2 and rec["value"] > 0
     assert rec["host_cpu_count"] == os.cpu_count()
     assert "median of 3" in rec["sample"]
+
+
+def test_traffic_hash_ignores_comments_only():
+    """A traffic record stays valid across comment and whitespace edits of the
+    kernel sources and is dropped when the code changes."""
+    import bench
+
+    base = 'int f(int x) {\n  return x + 1;  // one\n}\nconst char* s = "a // b";\n'
+    same = '/* header */\nint f(int x)   {\n  return x + 1;\n}\n// note\nconst char* s = "a // b";\n'
+    assert bench.code_text(base) == bench.code_text(same)
+    assert bench.code_text(base) != bench.code_text(base.replace("x + 1", "x + 2"))
+    assert bench.code_text(base) != bench.code_text(base.replace('"a // b"', '"a // c"'))
+    assert bench.measured_traffic() is not None  # the committed record matches the code
