@@ -55,4 +55,3 @@ def test_traffic_hash_ignores_comments_only():
     assert bench.code_text(base) == bench.code_text(same)
     assert bench.code_text(base) != bench.code_text(base.replace("x + 1", "x + 2"))
     assert bench.code_text(base) != bench.code_text(base.replace('"a // b"', '"a // c"'))
-    assert bench.measured_traffic() is not None  # the committed record matches the code
