@@ -127,11 +127,12 @@ def median_wall(fn, reps: int = 3) -> float:
     return sorted(ts)[len(ts) // 2]
 
 
-def oracle_baseline(run, n: int, what: str, T: int, threads: int = 1) -> dict:
-    """cpu_baseline record for run() processing n tokens (median of 3 walls)."""
+def oracle_baseline(run, n: int, what: str, T: int, threads: int = 1,
+                    noun: str = "tokens") -> dict:
+    """cpu_baseline record for run() processing n units (median of 3 walls)."""
     dt = median_wall(run)
-    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} of {T} tokens ({what}), {threads} thread(s), median of 3 "
+    return {"value": n / dt, "unit": f"{noun}/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {T} {noun} ({what}), {threads} thread(s), median of 3 "
                       f"runs, {dt:.2f} s wall", **host_cpu()}
 
 
@@ -489,6 +490,20 @@ def bench_scorer(args, dev):
                               "frac": tfs / FP4_MFMA_PEAK_TFLOPS,
                               "algorithmic_flops_per_launch": flops}},
     }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        # the first sequences of the batch, about 100 k keys
+        nseq = int(np.searchsorted(np.cumsum(sc.context_lens.astype(np.int64)), 100_000)) + 1
+        nseq = min(nseq, B)
+        nq = nseq * next_n
+        nkeys = int(sc.context_lens[:nseq].astype(np.int64).sum())
+        rec["cpu_baseline"] = oracle_baseline(
+            lambda: oracle.paged_mqa_logits(sc.q_out[:nq], sc.q_scale_out[:nq], sc.weights[:nq],
+                                            sc.kv_cache, sc.kv_cache_scale,
+                                            sc.block_table[:nseq], sc.context_lens[:nseq],
+                                            next_n),
+            nkeys, f"{nseq} sequence(s) x {next_n} query tokens x {H} heads", keys, noun="keys")
     print(json.dumps(rec), flush=True)
 
 
