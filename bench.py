@@ -162,6 +162,20 @@ def cpu_baseline(wl, n_tokens: int, threads: int):
 
 
 FP4_MFMA_PEAK_TFLOPS = 10100.0
+# fp32 vector operations per second, one per lane per cycle (adds and multiplies
+# that are not fused; packed fp32 is not used): 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+VALU_PEAK_GOPS = 256 * 4 * 16 * 2.4
+
+
+def alu_ops_per_token(H: int, hadamard: bool, norm: bool) -> int:
+    """Algorithmic fp32 operations of one token on the Hadamard path: per
+    128-row, RoPE 3 per rotated element (2 multiplies, 1 add), the FWHT 7 adds
+    per element, its scale 1 multiply per element and the quantizer's scaling
+    1 per element; the key RMSNorm 3 per element (square, sum, scale by the
+    reciprocal root and gamma counted as one) -- comparisons, conversions and
+    data movement not counted."""
+    row = 64 * 3 + 128 * (1 + (8 if hadamard else 0))
+    return (H + 1) * row + (128 * 3 if norm else 0)
 
 
 def fp8_q_bytes_per_token(H: int) -> int:
@@ -724,6 +738,17 @@ def main():
         rec["cache_note"] = ("%.1f MB per step against a 256 MB Infinity Cache: part of the "
                              "step's bytes can stay cache-resident between back-to-back steps, "
                              "so the HBM fraction is an upper estimate" % (step_bytes / 1e6))
+        # with the Hadamard the kernel is bound by VALU issue, not by HBM
+        ops = alu_ops_per_token(H, True, wl.k_norm_gamma is not None) * T
+        gops = ops / (fused_ms * 1e-3) / 1e9
+        hbm = rec["roofline"]
+        rec["roofline"] = {"kernel": hbm["kernel"], "bound": "alu", "achieved": gops,
+                           "peak": VALU_PEAK_GOPS, "unit": "Gop/s", "frac": gops / VALU_PEAK_GOPS,
+                           "traffic": None, "algorithmic_ops_per_launch": ops,
+                           "launch_us": hbm["launch_us"],
+                           "launch_us_median": hbm["launch_us_median"]}
+        rec["hbm_view"] = {k: hbm[k] for k in ("achieved", "peak", "unit", "frac",
+                                               "algorithmic_bytes_per_launch")}
     if use_graph:
         rec["eager_ms_per_step"] = eager_ms_per_step
         rec["two_call_step"]["eager_ms_per_step"] = eager_two_ms
