@@ -521,6 +521,79 @@ def bench_scorer(args, dev):
     print(json.dumps(rec), flush=True)
 
 
+def bench_prefill_scoring(args, dev):
+    """fp4idx_paged_mqa_logits on a chunked-prefill shape: one sequence of
+    65,536 keys whose last 4,096 tokens are the queries (next_n = 4096, query
+    tiles of 4), H = 64, random FP4 bytes and e8m0 exponents U[118, 130].
+    Algorithmic work counts the causal pairs (key s at or before the query's
+    position): 2 * 128 * H flops per pair on the matrix cores and 2 VALU
+    operations per pair and head (ReLU, weighted accumulate); bytes are the
+    inputs read once plus every logit of the [4096, 65536] rows written."""
+    import numpy as np
+    import torch
+
+    from pack_token_amd import fp4idx, workloads
+
+    B, next_n, H, ctx_len = 1, 4096, 64, 65536
+    sc = workloads.scorer_case(11, B, next_n, H, ctx_len, ctx_len)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    q, qs, w = up(sc.q_out), up(sc.q_scale_out), up(sc.weights)
+    kv, ks = up(sc.kv_cache), up(sc.kv_cache_scale)
+    table, ctx = up(sc.block_table), up(sc.context_lens)
+    stride = sc.max_blocks * 64
+    logits = torch.empty((B * next_n, stride), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        fp4idx.paged_mqa_logits(q, qs, w, kv, ks, table, ctx, next_n, logits=logits)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        call()
+        ev[i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / K
+    launch_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    pos = np.arange(ctx_len - next_n, ctx_len, dtype=np.int64)
+    pairs = int((pos + 1).sum())
+    flops = 2.0 * 128 * H * pairs
+    valu_ops = 2.0 * H * pairs
+    J = workloads.q_scale_cols(H)
+    bytes_ = (ctx_len * (64 + 4) + next_n * (64 * H + 64 * J + 4 * H) + next_n * ctx_len * 4
+              + (ctx_len // 64) * 4 + 4)
+    tfs = flops / (launch_ms * 1e-3) / 1e12
+    gops = valu_ops / (launch_ms * 1e-3) / 1e9
+    gbs = bytes_ / (launch_ms * 1e-3) / 1e9
+    rec = {
+        "metric": "FP4 paged MQA logits, chunked prefill: causal query-key pairs scored per second",
+        "value": pairs / (ms_per_step * 1e-3), "unit": "pairs/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "e2m1 x e2m1 -> fp32 (scaled MFMA)",
+        "data": "synthetic",
+        "config": {"workload": "prefill_scoring", "sequences": B, "next_n": next_n, "heads": H,
+                   "head_dim": 128, "kv_block_size": 64, "context": ctx_len, "relu": True,
+                   "causal_pairs": pairs},
+        "roofline": {"kernel": "mqa_logits_kernel<4,4,relu>", "bound": "alu", "achieved": gops,
+                     "peak": VALU_PEAK_GOPS, "unit": "Gop/s", "frac": gops / VALU_PEAK_GOPS,
+                     "traffic": None, "algorithmic_ops_per_launch": valu_ops,
+                     "launch_us": launch_ms * 1e3},
+        "mfma_view": {"achieved_TFLOPs": tfs, "peak_TFLOPs": FP4_MFMA_PEAK_TFLOPS,
+                      "frac": tfs / FP4_MFMA_PEAK_TFLOPS, "algorithmic_flops_per_launch": flops},
+        "hbm_view": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": bytes_},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -528,7 +601,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large_prefill",
                     choices=["large_prefill", "prefill_norm_rotate", "decode", "decode_scoring",
-                             "sglang_prefill", "fp8_prefill", "fake_quant_prefill"],
+                             "prefill_scoring", "sglang_prefill", "fp8_prefill",
+                             "fake_quant_prefill"],
                     help="large_prefill is the headline configuration; the other two are timed "
                          "for reference")
     ap.add_argument("--tokens", type=int, default=131072,
@@ -581,6 +655,9 @@ def main():
     t_gen = time.perf_counter()
     if args.workload == "decode_scoring":
         bench_scorer(args, dev)
+        return
+    if args.workload == "prefill_scoring":
+        bench_prefill_scoring(args, dev)
         return
     if args.workload == "sglang_prefill":
         bench_sglang(args, dev)

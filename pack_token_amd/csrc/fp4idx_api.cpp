@@ -28,6 +28,8 @@ constexpr int kRopeDim = 64;
 constexpr int kGroup = 32;
 constexpr int kKvBlock = 64;
 constexpr int kMaxHeads = 2048;
+// query tiles of 4 tokens on the third grid dimension (at most 65535)
+constexpr int kMaxNextN = 4 * 65535;
 
 int fail(int code, const char* fmt, ...) {
     char buf[512];
@@ -567,8 +569,9 @@ int fp4idx_paged_mqa_logits(const uint8_t* q_out, const uint8_t* q_scale_out, co
     if (H <= 0 || H % 16 != 0 || H > 64)
         return fail(FP4IDX_EUNSUPPORTED,
                     "%s: n_heads H must be 16, 32, 48 or 64 (got %d)", fn, H);
-    if (next_n < 1 || next_n > 4)
-        return fail(FP4IDX_EUNSUPPORTED, "%s: next_n must be 1..4 (got %d)", fn, next_n);
+    if (next_n < 1 || next_n > kMaxNextN)
+        return fail(FP4IDX_EUNSUPPORTED, "%s: next_n must be 1..%d (got %d)", fn, kMaxNextN,
+                    next_n);
     if (!is_flag(apply_relu))
         return fail(FP4IDX_EINVAL, "%s: apply_relu must be 0 or 1 (got %d)", fn, apply_relu);
     if (!std::isfinite(weights_scale))

@@ -134,11 +134,19 @@ __device__ __forceinline__ float transpose_reduce(const float acc[4]) {
     return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
-template <int NQ, int HT, bool RELU>
+// Query tokens come in tiles of NQ: with next_n <= 4 one tile of next_n
+// tokens (decode with multi-token prediction; TILED = false, everything known
+// at compile time), with larger next_n (chunked prefill; TILED = true) tiles
+// of 4 on blockIdx.z and a last tile of next_n % 4.  A key block that lies
+// entirely after the tile's last position holds -inf for every query of the
+// tile and is not read.
+template <int NQ, int HT, bool RELU, bool TILED>
 __global__ __launch_bounds__(64 * kWaves) void mqa_logits_kernel(LArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t b = blockIdx.y;
+    const int j0 = TILED ? (int)blockIdx.z * NQ : 0;  // first query of the tile
+    const int nq = TILED ? min(NQ, a.next_n - j0) : NQ;  // queries in the tile (>= 1)
     int64_t ctx = a.context_lens[b];
     ctx = ctx < 0 ? 0 : ctx;
     ctx = ctx > a.max_blocks * 64 ? a.max_blocks * 64 : ctx;
@@ -150,28 +158,43 @@ __global__ __launch_bounds__(64 * kWaves) void mqa_logits_kernel(LArgs a) {
     const int g = lane >> 4;
     const int H = HT * 16;
     const int J = a.J;
+    const int64_t t0 = b * a.next_n + j0;            // token row of the tile's first query
+    const int64_t p_last = ctx - a.next_n + j0 + nq - 1;
 
-    // query operands of the sequence's next_n tokens, kept in registers
+    // query operands of the tile's tokens, kept in registers (zeros past nq)
     i32x8_t A[NQ][HT];
     int SA[NQ][(HT + 3) / 4];
     float4 W[NQ][HT];
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
-        const int64_t t = b * NQ + j;
+        const int64_t t = t0 + j;
+        const bool live = j < nq;
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
-            A[j][ht] = as_operand(*reinterpret_cast<const u32x4_t*>(
-                a.q_out + ((t * H + 16 * ht + n) * 64 + 16 * g)));
-            W[j][ht] = *reinterpret_cast<const float4*>(a.weights + t * H + 16 * ht + 4 * g);
+            A[j][ht] = live ? as_operand(*reinterpret_cast<const u32x4_t*>(
+                                  a.q_out + ((t * H + 16 * ht + n) * 64 + 16 * g)))
+                            : i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+            W[j][ht] = live ? *reinterpret_cast<const float4*>(a.weights + t * H + 16 * ht + 4 * g)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
         for (int d = 0; d < (HT + 3) / 4; ++d)
-            SA[j][d] = *reinterpret_cast<const int*>(a.q_scale_out + t * 64 * (int64_t)J +
-                                                     (g * 16 + n) * J + 4 * d);
+            SA[j][d] = live ? *reinterpret_cast<const int*>(a.q_scale_out + t * 64 * (int64_t)J +
+                                                            (g * 16 + n) * J + 4 * d)
+                            : 0;
     }
 
     const int64_t kb_end = kb0 + kBlocksPerWave < nblk ? kb0 + kBlocksPerWave : nblk;
     for (int64_t kb = kb0; kb < kb_end; ++kb) {
+        const int64_t s = kb * 64 + lane;
+        if (TILED && kb * 64 > p_last) {  // after every query of the tile
+#pragma unroll
+            for (int j = 0; j < NQ; ++j)
+                if (j < nq && s < ctx)
+                    __builtin_nontemporal_store(-__builtin_huge_valf(),
+                                                a.logits + (t0 + j) * a.stride + s);
+            continue;
+        }
         const int32_t blk = a.block_table[b * a.max_blocks + kb];
         const bool valid = blk >= 0 && (int64_t)blk < a.nblocks;
         i32x8_t Bk[4];
@@ -185,28 +208,38 @@ __global__ __launch_bounds__(64 * kWaves) void mqa_logits_kernel(LArgs a) {
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) Bk[kt] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
         }
-        const int64_t s = kb * 64 + lane;
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
-            float acc[4] = {0.f, 0.f, 0.f, 0.f};
-            HeadLoop<HT, 0, RELU>::run(A[j], SA[j], W[j], Bk, sb, acc);
-            const float v = transpose_reduce(acc);
-            const int64_t t = b * NQ + j;
-            const int64_t pos = ctx - NQ + j;
-            const float out = (!valid || s > pos) ? -__builtin_huge_valf() : a.weights_scale * v;
-            if (s < ctx) __builtin_nontemporal_store(out, a.logits + t * a.stride + s);
+            if (j < nq) {  // uniform: the tile's token count
+                float acc[4] = {0.f, 0.f, 0.f, 0.f};
+                HeadLoop<HT, 0, RELU>::run(A[j], SA[j], W[j], Bk, sb, acc);
+                const float v = transpose_reduce(acc);
+                const int64_t pos = p_last - (nq - 1) + j;
+                const float out =
+                    (!valid || s > pos) ? -__builtin_huge_valf() : a.weights_scale * v;
+                if (s < ctx) __builtin_nontemporal_store(out, a.logits + (t0 + j) * a.stride + s);
+            }
         }
     }
+}
+
+template <int NQ, int HT, bool RELU>
+const void* kernel_for(bool tiled) {
+    if constexpr (NQ == 4)
+        if (tiled) return reinterpret_cast<const void*>(mqa_logits_kernel<NQ, HT, RELU, true>);
+    return reinterpret_cast<const void*>(mqa_logits_kernel<NQ, HT, RELU, false>);
 }
 
 template <int NQ, int HT>
 hipError_t launch_nq_ht(const LArgs& a, hipStream_t stream) {
     const int64_t per_wg = (int64_t)kWaves * kBlocksPerWave;
-    dim3 grid((unsigned)((a.max_blocks + per_wg - 1) / per_wg), (unsigned)a.B);
+    dim3 grid((unsigned)((a.max_blocks + per_wg - 1) / per_wg), (unsigned)a.B,
+              (unsigned)((a.next_n + NQ - 1) / NQ));
     LArgs copy = a;
     void* args[] = {&copy};
-    const void* fn = a.apply_relu ? reinterpret_cast<const void*>(mqa_logits_kernel<NQ, HT, true>)
-                                  : reinterpret_cast<const void*>(mqa_logits_kernel<NQ, HT, false>);
+    const bool tiled = a.next_n > NQ;  // only with NQ = 4
+    const void* fn = a.apply_relu ? kernel_for<NQ, HT, true>(tiled)
+                                  : kernel_for<NQ, HT, false>(tiled);
     return hipLaunchKernel(fn, grid, dim3(64 * kWaves), args, 0, stream);
 }
 
@@ -224,7 +257,7 @@ hipError_t launch_nq(const LArgs& a, hipStream_t stream) {
 
 hipError_t launch_paged_mqa_logits(const LArgs& a, hipStream_t stream) {
     if (a.B == 0 || a.max_blocks == 0) return hipSuccess;
-    switch (a.next_n) {
+    switch (a.next_n) {  // above 4: tiles of 4 query tokens
         case 1: return launch_nq<1>(a, stream);
         case 2: return launch_nq<2>(a, stream);
         case 3: return launch_nq<3>(a, stream);

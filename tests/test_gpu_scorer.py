@@ -135,3 +135,25 @@ def test_producer_to_scorer_end_to_end(next_n):
         overlaps.append(len(a & b) / 64)
     say(f"top-64 overlap mean {np.mean(overlaps):.4f} min {np.min(overlaps):.4f}")
     assert np.mean(overlaps) >= 0.99
+
+
+@pytest.mark.parametrize("next_n,H,relu", [(5, 32, True), (8, 64, False), (67, 32, True),
+                                           (130, 16, True)])
+def test_scorer_prefill_tiles(next_n, H, relu):
+    """next_n above 4 (chunked prefill): query tiles of 4 with a ragged last
+    tile, contexts shorter than, equal to and longer than next_n (queries at
+    negative positions see only -inf), whole key blocks after a tile's last
+    query (written -inf without being read) and invalid block entries."""
+    sc = workloads.scorer_case(900 + next_n + H, 4, next_n, H, 1, 700, signed_weights=not relu)
+    sc.context_lens[0] = max(1, next_n - 3)
+    sc.context_lens[1] = next_n
+    nb1 = -(-int(sc.context_lens[2]) // 64)
+    if nb1 > 1:
+        sc.block_table[2, nb1 // 2] = -1
+    say(f"case scorer prefill next_n={next_n} H={H} relu={relu} ctx={list(sc.context_lens)}")
+    got = run_gpu_scorer(sc, 0.75, relu)
+    ref, bound = oracle.paged_mqa_logits(sc.q_out, sc.q_scale_out, sc.weights, sc.kv_cache,
+                                         sc.kv_cache_scale, sc.block_table, sc.context_lens,
+                                         next_n, weights_scale=0.75, apply_relu=relu,
+                                         with_bound=True)
+    check_scorer(got, ref, bound, H)
