@@ -496,7 +496,7 @@ def bench_scorer(args, dev):
         "config": {"workload": "decode_scoring", "sequences": B, "next_n": next_n, "heads": H,
                    "head_dim": 128, "kv_block_size": 64, "keys": keys, "context": "U[4096,131072]",
                    "relu": True},
-        "roofline": {"kernel": "mqa_logits_kernel<4,2,relu>", "bound": "hbm", "achieved": gbs,
+        "roofline": {"kernel": "mqa_logits_kernel<4,2,relu,decode>", "bound": "hbm", "achieved": gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                      "traffic": None, "algorithmic_bytes_per_launch": bytes_,
                      "launch_us": launch_ms * 1e3,
@@ -524,7 +524,7 @@ def bench_scorer(args, dev):
 def bench_prefill_scoring(args, dev):
     """fp4idx_paged_mqa_logits on a chunked-prefill shape: one sequence of
     65,536 keys whose last 4,096 tokens are the queries (next_n = 4096, query
-    tiles of 4), H = 64, random FP4 bytes and e8m0 exponents U[118, 130].
+    tiles of 2), H = 64, random FP4 bytes and e8m0 exponents U[118, 130].
     Algorithmic work counts the causal pairs (key s at or before the query's
     position): 2 * 128 * H flops per pair on the matrix cores and 2 VALU
     operations per pair and head (ReLU, weighted accumulate); bytes are the
@@ -582,7 +582,7 @@ def bench_prefill_scoring(args, dev):
         "config": {"workload": "prefill_scoring", "sequences": B, "next_n": next_n, "heads": H,
                    "head_dim": 128, "kv_block_size": 64, "context": ctx_len, "relu": True,
                    "causal_pairs": pairs},
-        "roofline": {"kernel": "mqa_logits_kernel<4,4,relu>", "bound": "alu", "achieved": gops,
+        "roofline": {"kernel": "mqa_logits_kernel<2,4,relu,tiled>", "bound": "alu", "achieved": gops,
                      "peak": VALU_PEAK_GOPS, "unit": "Gop/s", "frac": gops / VALU_PEAK_GOPS,
                      "traffic": None, "algorithmic_ops_per_launch": valu_ops,
                      "launch_us": launch_ms * 1e3},

@@ -350,9 +350,9 @@ int fp4idx_dequant_debug(int which, const uint8_t* packed, const uint8_t* scales
  *   block_table  int32 [B, max_blocks]; only entries s/64 < ctx_b are read.
  *   context_lens int32 [B]; clamped to [0, min(max_blocks*64, stride)].
  *   H            16, 32, 48 or 64;  B <= 65535.
- *   next_n       1..262140.  1..4: decode, one tile of next_n query tokens per
+ *   next_n       1..131070.  1..4: decode, one tile of next_n query tokens per
  *                sequence (multi-token prediction).  Larger: chunked prefill,
- *                the next_n queries in tiles of 4 (the last one next_n % 4);
+ *                the next_n queries in tiles of 4 (H = 32) or 2 (other H);
  *                a key block that lies entirely after a tile's last position
  *                is written as -inf without being read.
  *   logits       fp32 [T, stride].

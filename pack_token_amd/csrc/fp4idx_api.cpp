@@ -28,8 +28,8 @@ constexpr int kRopeDim = 64;
 constexpr int kGroup = 32;
 constexpr int kKvBlock = 64;
 constexpr int kMaxHeads = 2048;
-// query tiles of 4 tokens on the third grid dimension (at most 65535)
-constexpr int kMaxNextN = 4 * 65535;
+// query tiles of 2 tokens (4 at H = 32) on the third grid dimension (at most 65535)
+constexpr int kMaxNextN = 2 * 65535;
 
 int fail(int code, const char* fmt, ...) {
     char buf[512];

@@ -137,7 +137,7 @@ __device__ __forceinline__ float transpose_reduce(const float acc[4]) {
 // Query tokens come in tiles of NQ: with next_n <= 4 one tile of next_n
 // tokens (decode with multi-token prediction; TILED = false, everything known
 // at compile time), with larger next_n (chunked prefill; TILED = true) tiles
-// of 4 on blockIdx.z and a last tile of next_n % 4.  A key block that lies
+// of NQ = 2 or 4 on blockIdx.z and a last tile of next_n % NQ.  A key block that lies
 // entirely after the tile's last position holds -inf for every query of the
 // tile and is not read.
 template <int NQ, int HT, bool RELU, bool TILED>
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(64 * kWaves) void mqa_logits_kernel(LArgs a) {
 
 template <int NQ, int HT, bool RELU>
 const void* kernel_for(bool tiled) {
-    if constexpr (NQ == 4)
+    if constexpr (NQ == 2 || NQ == 4)
         if (tiled) return reinterpret_cast<const void*>(mqa_logits_kernel<NQ, HT, RELU, true>);
     return reinterpret_cast<const void*>(mqa_logits_kernel<NQ, HT, RELU, false>);
 }
@@ -237,7 +237,7 @@ hipError_t launch_nq_ht(const LArgs& a, hipStream_t stream) {
               (unsigned)((a.next_n + NQ - 1) / NQ));
     LArgs copy = a;
     void* args[] = {&copy};
-    const bool tiled = a.next_n > NQ;  // only with NQ = 4
+    const bool tiled = a.next_n > NQ;  // only with NQ = 2 or 4
     const void* fn = a.apply_relu ? kernel_for<NQ, HT, true>(tiled)
                                   : kernel_for<NQ, HT, false>(tiled);
     return hipLaunchKernel(fn, grid, dim3(64 * kWaves), args, 0, stream);
@@ -257,7 +257,13 @@ hipError_t launch_nq(const LArgs& a, hipStream_t stream) {
 
 hipError_t launch_paged_mqa_logits(const LArgs& a, hipStream_t stream) {
     if (a.B == 0 || a.max_blocks == 0) return hipSuccess;
-    switch (a.next_n) {  // above 4: tiles of 4 query tokens
+    // Above 4 query tokens (chunked prefill), tiles of 4 at H = 32 and of 2
+    // otherwise: at H = 48 and 64, four tokens' query operands and weights take
+    // ~180 VGPRs (2 wavefronts per SIMD) and tiles of 2 ran 13% faster at
+    // 4096 x 65536, H = 64 (1 token per tile was 8% slower than 2); at H = 32
+    // tiles of 4 were 5% faster, at H = 16 tiles of 2 were 9% faster.
+    if (a.next_n > 4) return a.H == 32 ? launch_nq<4>(a, stream) : launch_nq<2>(a, stream);
+    switch (a.next_n) {
         case 1: return launch_nq<1>(a, stream);
         case 2: return launch_nq<2>(a, stream);
         case 3: return launch_nq<3>(a, stream);

@@ -183,7 +183,7 @@ def s_call(**over):
 S_REJECT = [
     (dict(H=128), fp4idx.EUNSUPPORTED, "n_heads"),
     (dict(H=24), fp4idx.EUNSUPPORTED, "n_heads"),
-    (dict(next_n=4 * 65535 + 1), fp4idx.EUNSUPPORTED, "next_n"),
+    (dict(next_n=2 * 65535 + 1), fp4idx.EUNSUPPORTED, "next_n"),
     (dict(next_n=0), fp4idx.EUNSUPPORTED, "next_n"),
     (dict(apply_relu=2), fp4idx.EINVAL, "apply_relu"),
     (dict(weights_scale=float("inf")), fp4idx.EINVAL, "weights_scale"),
