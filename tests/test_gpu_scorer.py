@@ -138,7 +138,7 @@ def test_producer_to_scorer_end_to_end(next_n):
 
 
 @pytest.mark.parametrize("next_n,H,relu", [(5, 32, True), (8, 64, False), (67, 32, True),
-                                           (130, 16, True)])
+                                           (130, 16, True), (21, 48, False)])
 def test_scorer_prefill_tiles(next_n, H, relu):
     """next_n above 4 (chunked prefill): query tiles of 4 with a ragged last
     tile, contexts shorter than, equal to and longer than next_n (queries at
