@@ -147,6 +147,30 @@ __device__ __forceinline__ void rope_quad(float lo[8], float hi[8], const float 
     unpack8(pack8(y + 8), hi);
 }
 
+// A cross-lane FWHT butterfly stage for a quad of lanes holding N chunks each,
+// with the partner fetched through the LDS crossbar (ds_swizzle in quad-permute mode,
+// which takes no VALU issue slot) and one fused multiply-add per element:
+// x' = x * s + p with s = +1 on the lower lane (x + p) and -1 on the upper
+// (p - x).  The product by +-1 is exact, so the FMA rounds p + s*x once, the
+// IEEE add or subtract itself, signed zeros included.  All of a stage's
+// swizzles are issued before its first FMA.
+constexpr int kSwzXor1 = 0x8000 | kDppXor1;  // ds_swizzle quad_perm [1,0,3,2]
+constexpr int kSwzXor2 = 0x8000 | kDppXor2;  // ds_swizzle quad_perm [2,3,0,1]
+
+template <int PAT, int N>
+__device__ __forceinline__ void fwht_cross_swz(float (*x)[8], float s) {
+    float p[N][8];
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            p[j][e] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x[j][e]), PAT));
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[j][e] = __builtin_fmaf(x[j][e], s, p[j][e]);
+}
+
 // Natural-order FWHT of the quad's head: strides 1, 2, 4 inside each chunk,
 // 8 and 16 across the quad (quad lanes r ^ 1, r ^ 2), 32 and 64 between the
 // lane's chunks; then the orthonormal scale.
@@ -164,10 +188,8 @@ __device__ __forceinline__ void hadamard_quad(float x[4][8], int r) {
             }
         }
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fwht_cross<kDppXor1>(x[j], (r & 1) != 0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fwht_cross<kDppXor2>(x[j], (r & 2) != 0);
+    fwht_cross_swz<kSwzXor1, 4>(x, (r & 1) ? -1.0f : 1.0f);
+    fwht_cross_swz<kSwzXor2, 4>(x, (r & 2) ? -1.0f : 1.0f);
 #pragma unroll
     for (int h = 1; h < 4; h <<= 1) {
 #pragma unroll
@@ -323,9 +345,11 @@ __global__ __launch_bounds__(kBlock) void k_row_kernel(KArgs a) {
 //   without the Hadamard, on a fifth wavefront of the block (the query side is
 //     memory-bound and the extra wavefront fills idle issue slots: 443 -> 436
 //     us at 131072 x 64);
-//   with it, on wavefront 0 after its query token, its key loads issued first
-//     (a fifth wavefront competes for the VALU there: 66.8 -> 68.4 us at
-//     16384 x 64).
+//   with it, on wavefront 0 after its query token (a fifth wavefront competes
+//     for the VALU there: 66.8 -> 68.4 us at 16384 x 64).  The key loads are
+//     issued only then: held across the query loop, the key row's registers
+//     took the kernel from 78 to 115 VGPRs (6 -> 4 wavefronts per SIMD) and
+//     the launch from 69-71 to 74-76 us.
 // The RoPE coefficients of lane L for a key row are those of slice chunk
 // chunk_of(L & 15) & 7 = chunk_of(L & 7).  Rows past T and rows whose slot is
 // outside the cache leave as a whole 16-lane row.
@@ -349,16 +373,6 @@ __global__ __launch_bounds__(HAD ? kBlock : kBlock + 64) void qk_kernel(QArgs qa
     const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
     if (t >= qa.T) return;
     uint32_t* sc = smem + wave * 16 * qa.J;
-    const bool krow = HAD && wave == 0 && tk < ka.T;
-    uint4 kv = make_uint4(0u, 0u, 0u, 0u);
-    int64_t kslot = -1;
-    float KC[8], KS[8];
-    if (krow) {
-        kv = load16_stream(ka.k + tk * 128 + 8 * chunk_of(lane & 15));
-        kslot = ka.slot_mapping[tk];
-        const int64_t kpos = clamped_position(ka.positions, ka.pos64, tk, ka.max_pos);
-        rope_coeffs<NEOX>(ka.cos_sin + kpos * 64, chunk_of(lane & 7), KC, KS);
-    }
     q_token_prologue(qa, t, lane, sc);
     const int64_t pos = clamped_position(qa.positions, qa.pos64, t, qa.max_pos);
     float C[8], S[8];
@@ -376,8 +390,14 @@ __global__ __launch_bounds__(HAD ? kBlock : kBlock + 64) void qk_kernel(QArgs qa
         q_split_token<NEOX>(qa, t, lane, reinterpret_cast<uint8_t*>(sc), C, S);
     }
     q_token_epilogue(qa, t, lane, sc);
-    if (krow && kslot >= 0 && kslot < ka.nslots)
-        k_row<NEOX, NORM, HAD>(ka, kv, kslot, lane & 15, KC, KS);
+    if (HAD && wave == 0 && tk < ka.T) {
+        const uint4 kv = load16_stream(ka.k + tk * 128 + 8 * chunk_of(lane & 15));
+        const int64_t kslot = ka.slot_mapping[tk];
+        const int64_t kpos = clamped_position(ka.positions, ka.pos64, tk, ka.max_pos);
+        float KC[8], KS[8];
+        rope_coeffs<NEOX>(ka.cos_sin + kpos * 64, chunk_of(lane & 7), KC, KS);
+        if (kslot >= 0 && kslot < ka.nslots) k_row<NEOX, NORM, HAD>(ka, kv, kslot, lane & 15, KC, KS);
+    }
 }
 
 // ---- small batches -------------------------------------------------------------

@@ -118,6 +118,66 @@ def test_prefill_norm_rotate(fused):
     check(workloads.prefill_norm_rotate(), fused=fused)
 
 
+def _cancelling_rows(rng, n):
+    """bf16 rows whose Hadamard transform meets exact zeros, where only the
+    IEEE rules for signed zeros and exact cancellation (x - x = +0) decide the
+    sign bit of a code: all +0, all -0, mixed +-0, one nonzero among zeros,
+    period 8 (every stride-8 difference cancels), x[j + 8] = -x[j] (every
+    stride-8 sum cancels), equal pairs (every stride-1 difference cancels), and
+    subnormal-only rows."""
+    rows = np.zeros((n, 128), np.uint16)
+    for i in range(n):
+        kind = i % 8
+        base = workloads.to_bf16_bits(rng.standard_normal(128).astype(np.float32))
+        signs = (rng.integers(0, 2, 128) * 0x8000).astype(np.uint16)
+        if kind == 0:
+            r = np.zeros(128, np.uint16)
+        elif kind == 1:
+            r = np.full(128, 0x8000, np.uint16)
+        elif kind == 2:
+            r = signs
+        elif kind == 3:
+            r = signs.copy()
+            r[rng.integers(0, 128)] = base[0]
+        elif kind == 4:
+            r = np.tile(base[:8], 16)
+        elif kind == 5:
+            r = np.tile(base[:8], 16) ^ np.repeat(np.tile(np.array([0, 0x8000], np.uint16), 8), 8)
+        elif kind == 6:
+            r = np.repeat(base[:64], 2)
+        else:
+            r = rng.integers(1, 0x80, 128).astype(np.uint16) | signs
+        rows[i] = r
+    return rows
+
+
+@FUSED
+@pytest.mark.parametrize("is_neox", [True, False])
+@pytest.mark.parametrize("T", [37, 613])
+def test_hadamard_signed_zeros_and_cancellation(T, is_neox, fused):
+    """The Hadamard path on rows built so that exact zeros reach the
+    quantizer: the sign of each zero code must follow the IEEE operations of
+    the natural-order transform exactly (the cross-lane butterflies included).
+    Half the tokens sit at position 0 (cos 1, sin 0), so the patterns also
+    cross the rotated slice; 37 tokens take the small-batch kernel, 613 the
+    per-token one."""
+    H = 48
+    rng = np.random.default_rng(1000 + T)
+    wl = workloads.sweep_case(31 * T, T, H, is_neox, 64)
+    wl.apply_hadamard = True
+    wl.positions[::2] = 0
+    q = wl.q.reshape(T * H, 128)
+    pick = rng.random(T * H) < 0.5
+    q[pick] = _cancelling_rows(rng, int(pick.sum()))
+    kp = rng.random(T) < 0.5
+    wl.k[kp] = _cancelling_rows(rng, int(kp.sum()))
+    wl.k_norm_gamma = workloads.to_bf16_bits((1 + 0.1 * rng.standard_normal(128)).astype(np.float32))
+    got = check(wl, fused=fused)
+    # the case must actually reach zero codes of both signs
+    codes = np.concatenate([got[0].reshape(-1) & 0x0F, got[0].reshape(-1) >> 4])
+    assert (codes == 0x0).any() and (codes == 0x8).any()
+
+
 def test_non_default_stream():
     import torch
 
