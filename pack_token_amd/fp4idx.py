@@ -120,6 +120,50 @@ def _require(t, name, dtypes, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+def _shape(t, name, shape):
+    """Exact shape check (None entries match any size).  Runs before the device
+    checks: the library sees only pointers, so a tensor of the wrong size would
+    be read or written out of bounds on the GPU."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    got = tuple(t.shape)
+    if len(got) != len(shape) or any(e is not None and g != e for g, e in zip(got, shape)):
+        want = tuple("*" if e is None else e for e in shape)
+        raise ValueError(f"{name} has shape {got}; expected {want}")
+
+
+def _numel(t, name, n):
+    """Element-count check for buffers whose layout the library defines."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.numel() != n:
+        raise ValueError(f"{name} has {t.numel()} elements (shape {tuple(t.shape)}); expected {n}")
+
+
+def _check_rows(T, positions, slot_mapping=None):
+    _shape(positions, "positions", (T,))
+    _shape(slot_mapping, "slot_mapping", (T,))
+
+
+def _check_cos_sin(cos_sin):
+    _shape(cos_sin, "cos_sin", (None, ROPE_DIM))
+
+
+def _check_fp4_cache(kv_cache, kv_cache_scale):
+    """kv_cache u8 [NB,1,4,64,16], kv_cache_scale u8 [NB,1,4,64] (any shapes with
+    those element counts)."""
+    if not isinstance(kv_cache, torch.Tensor):
+        raise TypeError("kv_cache must be a torch.Tensor")
+    NB = kv_cache.shape[0] if kv_cache.dim() else 0
+    _numel(kv_cache, "kv_cache", NB * 4 * KV_BLOCK * 16)
+    _numel(kv_cache_scale, "kv_cache_scale", NB * 4 * KV_BLOCK)
+    return NB
+
+
 def q_scale_cols(H: int) -> int:
     return ((H // 16) + 3) // 4 * 4
 
@@ -131,11 +175,17 @@ def q_rope_pack(q, positions, cos_sin, weights=None, *, q_out=None, q_scale_out=
     [max_pos,64]; weights fp32 [T,H] or None.  Returns (q_out, q_scale_out, weights_out)."""
     T, H, D = q.shape
     dev = q.device
+    J = q_scale_cols(H)
+    _check_rows(T, positions)
+    _check_cos_sin(cos_sin)
+    _shape(weights, "weights", (T, H))
+    _numel(q_out, "q_out", T * H * (D // 2))
+    _numel(q_scale_out, "q_scale_out", T * 4 * 16 * J)
+    _numel(weights_out, "weights_out", T * H)
     _require(q, "q", (torch.bfloat16, torch.int16, torch.uint16))
     _require(positions, "positions", (torch.int32, torch.int64), dev)
     _require(cos_sin, "cos_sin", (torch.float32,), dev)
     _require(weights, "weights", (torch.float32,), dev)
-    J = q_scale_cols(H)
     if q_out is None:
         q_out = torch.empty((T, H, D // 2), dtype=torch.uint8, device=dev)
     if q_scale_out is None:
@@ -162,6 +212,10 @@ def k_rope_pack_store(k, positions, cos_sin, slot_mapping, kv_cache, kv_cache_sc
     [NB,1,4,64,16] and kv_cache_scale u8 [NB,1,4,64] are updated in place."""
     T, D = k.shape
     dev = k.device
+    _check_rows(T, positions, slot_mapping)
+    _check_cos_sin(cos_sin)
+    NB = _check_fp4_cache(kv_cache, kv_cache_scale)
+    _numel(k_norm_gamma, "k_norm_gamma", D)
     _require(k, "k", (torch.bfloat16, torch.int16, torch.uint16))
     _require(positions, "positions", (torch.int32, torch.int64), dev)
     _require(cos_sin, "cos_sin", (torch.float32,), dev)
@@ -169,7 +223,6 @@ def k_rope_pack_store(k, positions, cos_sin, slot_mapping, kv_cache, kv_cache_sc
     _require(kv_cache, "kv_cache", (torch.uint8,), dev)
     _require(kv_cache_scale, "kv_cache_scale", (torch.uint8,), dev)
     _require(k_norm_gamma, "k_norm_gamma", (torch.bfloat16, torch.int16, torch.uint16), dev)
-    NB = kv_cache.shape[0]
     rc = lib().fp4idx_k_rope_pack_store(
         _ptr(k), _ptr(positions), int(positions.dtype == torch.int64), _ptr(cos_sin),
         cos_sin.shape[0], _ptr(slot_mapping), _ptr(k_norm_gamma), k_norm_eps, T, D, ROPE_DIM,
@@ -193,6 +246,11 @@ def q_rope_pack_fp8(q, positions, cos_sin, weights, *, weights_scale=1.0, q_out=
     weights_out bf16 [T,H] = (weights * q_scale) * weights_scale)."""
     T, H, D = q.shape
     dev = q.device
+    _check_rows(T, positions)
+    _check_cos_sin(cos_sin)
+    _shape(weights, "weights", (T, H))
+    _numel(q_out, "q_out", T * H * D)
+    _numel(weights_out, "weights_out", T * H)
     _require(q, "q", (torch.bfloat16, torch.int16, torch.uint16))
     _require(positions, "positions", (torch.int32, torch.int64), dev)
     _require(cos_sin, "cos_sin", (torch.float32,), dev)
@@ -220,6 +278,14 @@ def k_rope_pack_store_fp8(k, positions, cos_sin, slot_mapping, kv_cache, kv_cach
     kv_cache_scale fp32 [NB,64] are updated in place."""
     T, D = k.shape
     dev = k.device
+    _check_rows(T, positions, slot_mapping)
+    _check_cos_sin(cos_sin)
+    if not isinstance(kv_cache, torch.Tensor):
+        raise TypeError("kv_cache must be a torch.Tensor")
+    NB = kv_cache.shape[0] if kv_cache.dim() else 0
+    _numel(kv_cache, "kv_cache", NB * KV_BLOCK * D)
+    _numel(kv_cache_scale, "kv_cache_scale", NB * KV_BLOCK)
+    _numel(k_norm_gamma, "k_norm_gamma", D)
     _require(k, "k", (torch.bfloat16, torch.int16, torch.uint16))
     _require(positions, "positions", (torch.int32, torch.int64), dev)
     _require(cos_sin, "cos_sin", (torch.float32,), dev)
@@ -247,14 +313,16 @@ def rope_fake_quant(x, positions, cos_sin, *, y=None, rows_per_position=1, is_ne
     """fp4idx_rope_fake_quant.  x bf16 [..., 128]; returns y bf16 of the same shape
     (the fake-quantized values).  mode: "ue8m0_32" or "e4m3_16"."""
     dev = x.device
-    _require(x, "x", (torch.bfloat16, torch.int16, torch.uint16))
-    _require(positions, "positions", (torch.int32, torch.int64), dev)
-    _require(cos_sin, "cos_sin", (torch.float32,), dev)
-    if x.shape[-1] != HEAD_DIM:
+    if x.dim() == 0 or x.shape[-1] != HEAD_DIM:
         raise ValueError("x must end in a 128-dim axis")
     rows = x.numel() // HEAD_DIM
     if rows and positions.numel() * rows_per_position < rows:
         raise ValueError("positions has fewer than ceil(rows / rows_per_position) entries")
+    _check_cos_sin(cos_sin)
+    _numel(y, "y", x.numel())
+    _require(x, "x", (torch.bfloat16, torch.int16, torch.uint16))
+    _require(positions, "positions", (torch.int32, torch.int64), dev)
+    _require(cos_sin, "cos_sin", (torch.float32,), dev)
     if y is None:
         y = torch.empty(x.shape, dtype=torch.bfloat16, device=dev)
     _require(y, "y", (torch.bfloat16, torch.int16, torch.uint16), dev)
@@ -273,6 +341,8 @@ def q_rope_pack_sglang(q, positions, cos_sin, *, q_packed=None, is_neox=True, ro
     """fp4idx_q_rope_pack_sglang.  q bf16 [T,H,128]; returns q_packed u8 [T,H,68]."""
     T, H, D = q.shape
     dev = q.device
+    _check_rows(T, positions)
+    _check_cos_sin(cos_sin)
     _require(q, "q", (torch.bfloat16, torch.int16, torch.uint16))
     _require(positions, "positions", (torch.int32, torch.int64), dev)
     _require(cos_sin, "cos_sin", (torch.float32,), dev)
@@ -297,6 +367,9 @@ def k_rope_pack_store_sglang(k, positions, cos_sin, slot_mapping, index_k_cache,
     updated in place (slot 0 publishes nothing)."""
     T, D = k.shape
     dev = k.device
+    _check_rows(T, positions, slot_mapping)
+    _check_cos_sin(cos_sin)
+    _numel(k_norm_gamma, "k_norm_gamma", D)
     _require(k, "k", (torch.bfloat16, torch.int16, torch.uint16))
     _require(positions, "positions", (torch.int32, torch.int64), dev)
     _require(cos_sin, "cos_sin", (torch.float32,), dev)
@@ -322,6 +395,16 @@ def qk_rope_pack_store(q, k, positions, cos_sin, slot_mapping, kv_cache, kv_cach
     Returns (q_out, q_scale_out, weights_out); the cache tensors are updated in place."""
     T, H, D = q.shape
     dev = q.device
+    J = q_scale_cols(H)
+    _shape(k, "k", (T, D))
+    _check_rows(T, positions, slot_mapping)
+    _check_cos_sin(cos_sin)
+    _shape(weights, "weights", (T, H))
+    _check_fp4_cache(kv_cache, kv_cache_scale)
+    _numel(k_norm_gamma, "k_norm_gamma", D)
+    _numel(q_out, "q_out", T * H * (D // 2))
+    _numel(q_scale_out, "q_scale_out", T * 4 * 16 * J)
+    _numel(weights_out, "weights_out", T * H)
     _require(q, "q", (torch.bfloat16, torch.int16, torch.uint16))
     _require(k, "k", (torch.bfloat16, torch.int16, torch.uint16), dev)
     _require(positions, "positions", (torch.int32, torch.int64), dev)
@@ -362,6 +445,15 @@ def paged_mqa_logits(q_out, q_scale_out, weights, kv_cache, kv_cache_scale, bloc
     B, max_blocks = block_table.shape
     if T != B * next_n:
         raise ValueError(f"q_out has {T} tokens, expected B*next_n = {B * next_n}")
+    _shape(q_out, "q_out", (T, H, HEAD_DIM // 2))
+    _numel(q_scale_out, "q_scale_out", T * 4 * 16 * q_scale_cols(H))
+    _shape(weights, "weights", (T, H))
+    _check_fp4_cache(kv_cache, kv_cache_scale)
+    _shape(context_lens, "context_lens", (B,))
+    if logits is not None:
+        _shape(logits, "logits", (T, None))
+        if stride is not None and stride != logits.shape[1]:
+            raise ValueError(f"stride {stride} differs from logits.shape[1] = {logits.shape[1]}")
     _require(q_out, "q_out", (torch.uint8,))
     _require(q_scale_out, "q_scale_out", (torch.uint8,), dev)
     _require(weights, "weights", (torch.float32,), dev)
@@ -385,6 +477,9 @@ def paged_mqa_logits(q_out, q_scale_out, weights, kv_cache, kv_cache_scale, bloc
 def dequant_q(q_out, q_scale_out, *, out=None, stream=None):
     """fp4idx_dequant_debug(which=0): fp32 [T,H,128]."""
     T, H, _ = q_out.shape
+    _shape(q_out, "q_out", (T, H, HEAD_DIM // 2))
+    _numel(q_scale_out, "q_scale_out", T * 4 * 16 * q_scale_cols(H))
+    _numel(out, "out", T * H * HEAD_DIM)
     if out is None:
         out = torch.empty((T, H, HEAD_DIM), dtype=torch.float32, device=q_out.device)
     _require(q_out, "q_out", (torch.uint8,))
@@ -397,8 +492,11 @@ def dequant_q(q_out, q_scale_out, *, out=None, stream=None):
 
 def dequant_kcache(kv_cache, kv_cache_scale, slots=None, *, out=None, stream=None):
     """fp4idx_dequant_debug(which=1): fp32 [rows,128] for the given slots (or all slots)."""
-    NB = kv_cache.shape[0]
+    NB = _check_fp4_cache(kv_cache, kv_cache_scale)
+    if slots is not None:
+        _shape(slots, "slots", (None,))
     rows = NB * KV_BLOCK if slots is None else slots.shape[0]
+    _numel(out, "out", rows * HEAD_DIM)
     if out is None:
         out = torch.empty((rows, HEAD_DIM), dtype=torch.float32, device=kv_cache.device)
     _require(kv_cache, "kv_cache", (torch.uint8,))
