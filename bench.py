@@ -38,6 +38,9 @@ SGLANG_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q_sglang_kernel_sglang_pre
 FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q_fp8_kernel_fp8_prefill_traffic.json")
 FQ_TRAFFIC_FILE = os.path.join(ROOT, "profiles",
                                "fake_quant_token_kernel_fake_quant_prefill_traffic.json")
+SCORER_SOURCES = ("fp4idx_internal.h", "fp4idx_scorer.hip")
+SCORER_TRAFFIC_FILE = os.path.join(ROOT, "profiles",
+                                   "mqa_logits_kernel_decode_scoring_traffic.json")
 
 
 def q_bytes_per_token(H: int) -> int:
@@ -498,7 +501,8 @@ def bench_scorer(args, dev):
                    "relu": True},
         "roofline": {"kernel": "mqa_logits_kernel<4,2,relu,decode>", "bound": "hbm", "achieved": gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes_per_launch": bytes_,
+                     "traffic": measured_traffic(SCORER_TRAFFIC_FILE, SCORER_SOURCES),
+                     "algorithmic_bytes_per_launch": bytes_,
                      "launch_us": launch_ms * 1e3,
                      "mfma": {"achieved_TFLOPs": tfs, "peak_TFLOPs": FP4_MFMA_PEAK_TFLOPS,
                               "frac": tfs / FP4_MFMA_PEAK_TFLOPS,

@@ -157,3 +157,31 @@ def test_scorer_prefill_tiles(next_n, H, relu):
                                          next_n, weights_scale=0.75, apply_relu=relu,
                                          with_bound=True)
     check_scorer(got, ref, bound, H)
+
+
+@pytest.mark.parametrize("next_n,H", [(1, 32), (4, 32), (3, 48), (67, 32), (130, 64), (9, 16)])
+def test_scorer_sparse_invalid_blocks(next_n, H):
+    """Block tables where about a third of the entries are invalid (negative or
+    past the cache), so that an invalid block falls at every place of a
+    wavefront's window of 4 (decode) or 8 (query tiles) blocks: first, last,
+    several in a row, and whole windows.  The scorer fetches each block one
+    ahead while it scores the previous one; an invalid block is never fetched
+    and its keys are -inf.  Contexts run from one block to 40 blocks with
+    ragged tails."""
+    sc = workloads.scorer_case(4100 + 7 * next_n + H, 6, next_n, H, 1, 40 * 64 - 5)
+    rng = np.random.default_rng(next_n * 131 + H)
+    bad = rng.random(sc.block_table.shape) < 0.35
+    bad[0, :8] = True                       # a whole window of the first sequence
+    bad[1, ::4] = True                      # first block of every decode window
+    bad[2, 7::8] = True                     # last block of every tiled window
+    vals = np.where(rng.random(sc.block_table.shape) < 0.5, -1, sc.NB + 3).astype(np.int32)
+    sc.block_table[bad] = vals[bad]
+    say(f"case scorer sparse next_n={next_n} H={H} ctx={list(sc.context_lens)} "
+        f"invalid={int(bad.sum())}")
+    got = run_gpu_scorer(sc, 1.25, True)
+    ref, bound = oracle.paged_mqa_logits(sc.q_out, sc.q_scale_out, sc.weights, sc.kv_cache,
+                                         sc.kv_cache_scale, sc.block_table, sc.context_lens,
+                                         next_n, weights_scale=1.25, apply_relu=True,
+                                         with_bound=True)
+    check_scorer(got, ref, bound, H)
+    assert np.isneginf(ref).any() and np.isfinite(ref).any()
