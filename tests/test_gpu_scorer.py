@@ -185,3 +185,56 @@ def test_scorer_sparse_invalid_blocks(next_n, H):
                                          with_bound=True)
     check_scorer(got, ref, bound, H)
     assert np.isneginf(ref).any() and np.isfinite(ref).any()
+
+
+def _check_row_pattern(row, pos, ctx):
+    """A logit row of a query at position pos of a context of ctx keys: finite up
+    to pos, -inf after it inside the context, untouched past it."""
+    assert np.isfinite(row[:max(pos + 1, 0)]).all()
+    assert np.isneginf(row[max(pos + 1, 0):ctx]).all()
+    assert (row[ctx:] == SENT).all()
+
+
+def test_scorer_decode_full_size_sampled():
+    """The decode-scoring batch at full size, in the launch the benchmark times
+    (64 sequences x next_n 4, H = 32, contexts U[4096, 131072], 4.6 M keys):
+    two whole sequences against the oracle, the -inf / untouched pattern of
+    every row."""
+    B, next_n, H = 64, 4, 32
+    sc = workloads.scorer_case(7, B, next_n, H, 4096, 131072)
+    say(f"case scorer decode full size: {int(sc.context_lens.sum())} keys")
+    got = run_gpu_scorer(sc)
+    for b in range(B):
+        for j in range(next_n):
+            ctx = int(sc.context_lens[b])
+            _check_row_pattern(got[b * next_n + j], ctx - next_n + j, ctx)
+    for b in (int(np.argmax(sc.context_lens)), 5):
+        rows = slice(b * next_n, (b + 1) * next_n)
+        ref, bound = oracle.paged_mqa_logits(sc.q_out[rows], sc.q_scale_out[rows],
+                                             sc.weights[rows], sc.kv_cache, sc.kv_cache_scale,
+                                             sc.block_table[b:b + 1], sc.context_lens[b:b + 1],
+                                             next_n, with_bound=True)
+        check_scorer(got[rows], ref, bound, H)
+
+
+def test_scorer_prefill_full_size_sampled():
+    """The chunked-prefill scoring case at full size, in the launch the benchmark
+    times (one sequence of 65,536 keys, its last 4,096 tokens as queries, H = 64,
+    query tiles of 2, 8 blocks per wavefront): the row pattern of every query,
+    and three groups of 4 queries (the first, a middle and the last) against
+    the oracle, each as a 4-query case whose context ends 4 keys after its
+    queries' positions, i.e. at exactly the positions of the full run."""
+    B, next_n, H, ctx_len = 1, 4096, 64, 65536
+    sc = workloads.scorer_case(11, B, next_n, H, ctx_len, ctx_len)
+    say("case scorer prefill full size: 4096 x 65536, H = 64")
+    got = run_gpu_scorer(sc)
+    for j in range(next_n):
+        _check_row_pattern(got[j], ctx_len - next_n + j, ctx_len)
+    for r0 in (0, 2050, next_n - 4):
+        ctx_sub = ctx_len - next_n + r0 + 4
+        rows = slice(r0, r0 + 4)
+        ref, bound = oracle.paged_mqa_logits(sc.q_out[rows], sc.q_scale_out[rows],
+                                             sc.weights[rows], sc.kv_cache, sc.kv_cache_scale,
+                                             sc.block_table, np.array([ctx_sub], np.int32), 4,
+                                             with_bound=True)
+        check_scorer(got[rows, :ctx_sub], ref[:, :ctx_sub], bound[:, :ctx_sub], H)
