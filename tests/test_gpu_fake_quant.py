@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 from pack_token_amd import workloads
-from harness import assert_same, say
+from harness import assert_same, random_case, say
 
 pytestmark = pytest.mark.gpu
 
@@ -117,3 +117,16 @@ def test_ue8m0_exhaustive():
 def test_empty():
     x = np.zeros((0, 128), np.uint16)
     assert gpu_fq(x, np.zeros(0, np.int64), workloads.cos_sin_table(4)).shape == (0, 128)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_cases(seed):
+    """Seeded random shapes and modes (the producer's random cases) through the
+    RoPE tail + fake quant, queries (H rows per position) and keys, both
+    scale modes, compress ratio 1, 2 or 4, the drawn floor."""
+    wl, _ = random_case(300 + seed)
+    mode = sorted(MODES)[seed % 2]
+    kw = dict(compress_ratio=[1, 2, 4][seed % 3], is_neox=wl.is_neox, rope_offset=wl.rope_offset,
+              scale_floor=wl.scale_floor)
+    check(wl.q, wl.positions, wl.cos_sin, mode, rows_per_position=wl.H, **kw)
+    check(wl.k, wl.positions, wl.cos_sin, mode, **kw)

@@ -11,7 +11,7 @@ import pytest
 import oracle
 from pack_token_amd import workloads
 from pack_token_amd.workloads import SENTINEL
-from harness import assert_same, say
+from harness import assert_same, random_case, say
 
 pytestmark = pytest.mark.gpu
 
@@ -189,3 +189,15 @@ def test_large_prefill_sampled(fmt):
                                  scale_fmt=ofmt)
     assert_same("kv_cache", kv, rkv)
     assert_same("kv_cache_scale", ks, rks)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_cases(seed):
+    """Seeded random shapes and modes (the producer's random cases) in the FP8
+    mode: either scale format, any weights scale, Hadamard and key RMSNorm as
+    drawn, clamped positions and skipped / past-the-end slots."""
+    wl, _ = random_case(100 + seed)
+    rng = np.random.default_rng(seed)
+    fmt = ["ue8m0", "fp32"][seed % 2]
+    check(wl, fmt, weights_scale=float(rng.choice([1.0, 0.3, 1.0 / 8, 7.5])),
+          gamma=wl.k_norm_gamma, had=wl.apply_hadamard, floor=wl.scale_floor)

@@ -8,7 +8,7 @@ import pytest
 import oracle
 from pack_token_amd import workloads
 from pack_token_amd.workloads import SENTINEL
-from harness import assert_all_same, assert_same, gpu_run, oracle_run, say
+from harness import assert_all_same, assert_same, gpu_run, oracle_run, random_case, say
 
 pytestmark = pytest.mark.gpu
 
@@ -421,53 +421,11 @@ def test_sglang_row_matrix(T, pos32, fused):
     check(workloads.edge_mix(seed=200 + T, T=T, positions_int32=pos32), fused=fused)
 
 
-_RANDOM_T = [1, 2, 3, 5, 63, 64, 65, 127, 300, 511, 512, 513, 1000, 1023, 1024, 1025, 2047, 2049]
-
-
-def _random_case(seed):
-    """A seeded random point of the whole input space: token counts around the
-    block and small-batch boundaries, 16..256 heads, every RoPE mode, Hadamard
-    and key RMSNorm on or off, value scales from 1e-3 to 1e3 with planted
-    zero / subnormal / half-way groups, int32 or int64 positions (a few past
-    max_pos or negative: clamped), slots with skips (-1) and a few past the end
-    of the cache, three floors, weights present or not."""
-    rng = np.random.Generator(np.random.PCG64(7000 + seed))
-    T = int(rng.choice(_RANDOM_T))
-    H = 16 * int(rng.integers(1, 17))
-    scale = float(rng.choice([1.0, 40.0, 1e-3, 1e3]))
-    q = workloads.to_bf16_bits(rng.standard_normal((T, H, 128), dtype=np.float32) * scale)
-    k = workloads.to_bf16_bits(rng.standard_normal((T, 128), dtype=np.float32) * scale)
-    workloads._plant_special_groups(rng, q.reshape(T * H, 128))
-    workloads._plant_special_groups(rng, k)
-    max_pos = int(rng.integers(1, 70000))
-    positions = rng.integers(0, max_pos, T, dtype=np.int64)
-    odd = rng.random(T) < 0.02
-    positions[odd] = np.where(rng.random(int(odd.sum())) < 0.5, -1 - rng.integers(0, 5, int(odd.sum())),
-                              max_pos + rng.integers(0, 1000, int(odd.sum())))
-    if rng.integers(2):
-        positions = positions.astype(np.int32)
-    NB = -(-T // 64) + int(rng.integers(0, 3))
-    slots = rng.permutation(NB * 64)[:T].astype(np.int64)
-    u = rng.random(T)
-    slots[u < 0.05] = -1
-    slots[(u >= 0.05) & (u < 0.07)] = NB * 64 + rng.integers(0, 100)
-    wl = workloads.Workload(f"random_{seed}_T{T}_H{H}", T, H, q, k, positions,
-                            workloads.cos_sin_table(max_pos),
-                            rng.random((T, H), dtype=np.float32), slots, NB,
-                            is_neox=bool(rng.integers(2)), rope_offset=int(rng.choice([0, 64])),
-                            apply_hadamard=bool(rng.integers(2)),
-                            scale_floor=float(np.float32(rng.choice([2.0 ** -126, 1e-10, 1e-3]))))
-    if rng.integers(2):
-        wl.k_norm_gamma = workloads.to_bf16_bits(
-            (1 + 0.1 * rng.standard_normal(128)).astype(np.float32))
-    return wl, bool(rng.integers(0, 4))
-
-
 @pytest.mark.parametrize("seed", range(24))
 def test_random_shapes_and_modes(seed):
     """Seeded random cases over shapes and modes, both the two-call path and the
     fused launch, byte for byte against the oracle."""
-    wl, with_weights = _random_case(seed)
+    wl, with_weights = random_case(seed)
     ref = oracle_run(wl, with_weights=with_weights)
     for fused in (False, True):
         say(f"case {wl.name}: neox={wl.is_neox} ro={wl.rope_offset} had={wl.apply_hadamard} "

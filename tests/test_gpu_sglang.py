@@ -12,7 +12,7 @@ import pytest
 import oracle
 from pack_token_amd import workloads
 from pack_token_amd.workloads import SENTINEL
-from harness import assert_same, say
+from harness import assert_same, random_case, say
 
 pytestmark = pytest.mark.gpu
 
@@ -196,3 +196,16 @@ def test_large_prefill_sampled():
     ref_k = np.full((n, 68), SENTINEL, np.uint8)
     oracle.k_rope_pack_store_sglang(wl.k, wl.positions, wl.cos_sin, slots, ref_k)
     assert_same("index_k_cache", got_k, ref_k)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_cases(seed):
+    """Seeded random shapes and modes (the producer's random cases) through the
+    sglang-compatible records: any floor pair, compress ratio 1, 2 or 4, key
+    RMSNorm as drawn, slot 0 and past-the-end slots among the draws."""
+    wl, _ = random_case(200 + seed)
+    rng = np.random.default_rng(seed)
+    slots = wl.slot_mapping.copy()
+    slots[rng.random(wl.T) < 0.03] = 0
+    floors = FLOORS[sorted(FLOORS)[seed % len(FLOORS)]]
+    check_both(wl, slots, wl.NB * 64, wl.k_norm_gamma, floors, ratio=[1, 2, 4][seed % 3])
