@@ -194,7 +194,7 @@ int fp4idx_qk_rope_pack_store(const void* q, const void* k, const void* position
  * fp4idx_q_rope_pack_sglang
  *   q, positions, positions_int64, cos_sin, max_pos, T, H, D, R, rope_offset,
  *   group_size, is_neox: as for fp4idx_q_rope_pack.
- *   q_packed     u8 [T, H, 68], 4-byte aligned: record of head h of token t.
+ *   q_packed     u8 [T, H, 68], 16-byte aligned: record of head h of token t.
  *
  * fp4idx_k_rope_pack_store_sglang
  *   k, positions, positions_int64, cos_sin, max_pos, slot_mapping,

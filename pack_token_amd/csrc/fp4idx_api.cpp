@@ -308,7 +308,7 @@ int fp4idx_q_rope_pack_sglang(const void* q, const void* positions, int position
     FP4IDX_TRY(check_ptr(fn, "q", q, 16));
     FP4IDX_TRY(check_ptr(fn, "positions", positions, positions_int64 ? 8 : 4));
     FP4IDX_TRY(check_ptr(fn, "cos_sin", cos_sin, 16));
-    FP4IDX_TRY(check_ptr(fn, "q_packed", q_packed, 4));
+    FP4IDX_TRY(check_ptr(fn, "q_packed", q_packed, 16));
     fp4idx::SQArgs a{};
     a.q = static_cast<const uint16_t*>(q);
     a.positions = positions;

@@ -74,13 +74,17 @@ __device__ __forceinline__ Q8 quant8_two_stage(uint4 v, int e_lo1, int e_lo2) {
 // Query records [T, H, 68]: head h of token t is 64 code bytes, then its four
 // stage-2 exponents as one dword.  Lane and load layout as q_split_token; the
 // exponents of a head's four groups sit on the two quads of its 8 lanes and
-// are merged into lane 0 of the 8 with one half-row mirror.  The records are
-// written with the default cache policy: a 68-byte record never fills whole
-// 32-byte sectors from one store instruction, and streaming stores of such
-// pieces measured ~18% slower (partial lines leave L2 before they complete).
+// are merged into lane 0 of the 8 with one half-row mirror.  A 68-byte record
+// never fills whole lines from one store instruction (streaming stores of the
+// pieces measured ~18% slower than default-policy ones, which L2 merges), so
+// the records of 32 heads are assembled in the wavefront's 2,176 bytes of
+// LDS and written as 17 whole 128-byte lines with 16-byte streaming stores
+// (the run of a token's records starts at a multiple of 32 x 68 bytes, and
+// q_packed is 16-byte aligned): 509-511 -> 497-499 us at 131072 x 64.
 template <bool NEOX>
 __device__ __forceinline__ void q_sglang_token(const SQArgs& a, int64_t t, int lane,
-                                               const float C[8], const float S[8]) {
+                                               const float C[8], const float S[8],
+                                               uint32_t* stage) {
     const int H = a.H;
     const int c = chunk_of(lane & 7);
     const int hsub = lane >> 3;
@@ -90,7 +94,8 @@ __device__ __forceinline__ void q_sglang_token(const SQArgs& a, int64_t t, int l
     const int sh_pln = 8 * (nro / 32 + (c >> 2));
     const bool writer = (lane & 7) == 0;
     const uint16_t* qt = a.q + t * (int64_t)H * 128 + hsub * 128 + 8 * c;
-    uint8_t* ot = a.q_packed + t * (int64_t)H * kSglangRecord + hsub * kSglangRecord + 4 * c;
+    uint8_t* ot = reinterpret_cast<uint8_t*>(stage) + hsub * kSglangRecord + 4 * c;
+    uint8_t* const out = a.q_packed + t * (int64_t)H * kSglangRecord;
 
     uint4 np0 = load16_stream(qt + nro), nr0 = load16_stream(qt + ro);
     uint4 np1 = load16_stream(qt + 8 * 128 + nro), nr1 = load16_stream(qt + 8 * 128 + ro);
@@ -107,7 +112,7 @@ __device__ __forceinline__ void q_sglang_token(const SQArgs& a, int64_t t, int l
         const Q8 qr0 = quant8_two_stage(rope8<NEOX>(r0, C, S), a.e_lo1, a.e_lo2);
         const Q8 qp1 = quant8_two_stage(p1, a.e_lo1, a.e_lo2);
         const Q8 qr1 = quant8_two_stage(rope8<NEOX>(r1, C, S), a.e_lo1, a.e_lo2);
-        uint8_t* o = ot + hb * kSglangRecord;
+        uint8_t* o = ot + (hb & 16) * kSglangRecord;
         store4_plain(o + nro / 2, qp0.codes);
         store4_plain(o + ro / 2, qr0.codes);
         store4_plain(o + 8 * kSglangRecord + nro / 2, qp1.codes);
@@ -119,6 +124,15 @@ __device__ __forceinline__ void q_sglang_token(const SQArgs& a, int64_t t, int l
         if (writer) {  // c == 0 here, so o is the start of the head's record
             store4_plain(o + 64, x0);
             store4_plain(o + 8 * kSglangRecord + 64, x1);
+        }
+        if ((hb & 16) || hb + 16 >= H) {  // 32 heads (or the last 16) are staged
+            wave_sync();
+            const int h0 = hb & ~31;
+            const int n16 = (hb + 16 - h0) * kSglangRecord / 16;  // 136 or 68
+            const uint4* src = reinterpret_cast<const uint4*>(stage);
+            for (int i = lane; i < n16; i += 64)
+                store16_stream(out + h0 * kSglangRecord + 16 * i, src[i]);
+            wave_sync();
         }
     }
 }
@@ -132,7 +146,8 @@ __global__ __launch_bounds__(kBlock) void q_sglang_kernel(SQArgs a) {
     const int64_t pos = clamped_position(a.positions, a.pos64, t, a.max_pos);
     float C[8], S[8];
     rope_coeffs<NEOX>(a.cos_sin + pos * 64, chunk_of(lane & 7), C, S);
-    q_sglang_token<NEOX>(a, t, lane, C, S);
+    __shared__ __attribute__((aligned(16))) uint32_t stage[kWavesPerBlock][32 * kSglangRecord / 4];
+    q_sglang_token<NEOX>(a, t, lane, C, S, stage[wave]);
 }
 
 // Key records [num_slots, 68]: 16 lanes per token as k_row_kernel.  Slot 0,

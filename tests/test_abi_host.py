@@ -231,7 +231,8 @@ SQ_REJECT = [
     (dict(pack_floor=float("inf")), fp4idx.EINVAL, "pack_floor"),
     (dict(is_neox=5), fp4idx.EINVAL, "is_neox"),
     (dict(q_packed=None), fp4idx.EINVAL, "q_packed must not be NULL"),
-    (dict(q_packed=ALIGNED + 2), fp4idx.EINVAL, "q_packed must be 4-byte"),
+    (dict(q_packed=ALIGNED + 2), fp4idx.EINVAL, "q_packed must be 16-byte"),
+    (dict(q_packed=ALIGNED + 4), fp4idx.EINVAL, "q_packed must be 16-byte"),
     (dict(q=ALIGNED + 4), fp4idx.EINVAL, "q must be 16-byte"),
     (dict(T=1 << 58), fp4idx.EINVAL, "T too large"),
 ]
