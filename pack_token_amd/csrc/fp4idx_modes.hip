@@ -77,10 +77,11 @@ __device__ __forceinline__ Q8 quant8_two_stage(uint4 v, int e_lo1, int e_lo2) {
 // are merged into lane 0 of the 8 with one half-row mirror.  A 68-byte record
 // never fills whole lines from one store instruction (streaming stores of the
 // pieces measured ~18% slower than default-policy ones, which L2 merges), so
-// the records of 32 heads are assembled in the wavefront's 2,176 bytes of
-// LDS and written as 17 whole 128-byte lines with 16-byte streaming stores
-// (the run of a token's records starts at a multiple of 32 x 68 bytes, and
-// q_packed is 16-byte aligned): 509-511 -> 497-499 us at 131072 x 64.
+// the records of 64 heads are assembled in the wavefront's 4,352 bytes of
+// LDS and written as 34 whole 128-byte lines with 16-byte streaming stores
+// (a run of 64 records starts at a multiple of 64 x 68 bytes, and q_packed is
+// 16-byte aligned): 505-511 -> 494-496 us at 131072 x 64 (497-499 with runs
+// of 32; default-policy stores of the staged lines: 538-541).
 template <bool NEOX>
 __device__ __forceinline__ void q_sglang_token(const SQArgs& a, int64_t t, int lane,
                                                const float C[8], const float S[8],
@@ -112,7 +113,7 @@ __device__ __forceinline__ void q_sglang_token(const SQArgs& a, int64_t t, int l
         const Q8 qr0 = quant8_two_stage(rope8<NEOX>(r0, C, S), a.e_lo1, a.e_lo2);
         const Q8 qp1 = quant8_two_stage(p1, a.e_lo1, a.e_lo2);
         const Q8 qr1 = quant8_two_stage(rope8<NEOX>(r1, C, S), a.e_lo1, a.e_lo2);
-        uint8_t* o = ot + (hb & 16) * kSglangRecord;
+        uint8_t* o = ot + (hb & 48) * kSglangRecord;
         store4_plain(o + nro / 2, qp0.codes);
         store4_plain(o + ro / 2, qr0.codes);
         store4_plain(o + 8 * kSglangRecord + nro / 2, qp1.codes);
@@ -125,10 +126,10 @@ __device__ __forceinline__ void q_sglang_token(const SQArgs& a, int64_t t, int l
             store4_plain(o + 64, x0);
             store4_plain(o + 8 * kSglangRecord + 64, x1);
         }
-        if ((hb & 16) || hb + 16 >= H) {  // 32 heads (or the last 16) are staged
+        if ((hb & 48) == 48 || hb + 16 >= H) {  // 64 heads (or the last 16-48) are staged
             wave_sync();
-            const int h0 = hb & ~31;
-            const int n16 = (hb + 16 - h0) * kSglangRecord / 16;  // 136 or 68
+            const int h0 = hb & ~63;
+            const int n16 = (hb + 16 - h0) * kSglangRecord / 16;  // 272, 204, 136 or 68
             const uint4* src = reinterpret_cast<const uint4*>(stage);
             for (int i = lane; i < n16; i += 64)
                 store16_stream(out + h0 * kSglangRecord + 16 * i, src[i]);
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(kBlock) void q_sglang_kernel(SQArgs a) {
     const int64_t pos = clamped_position(a.positions, a.pos64, t, a.max_pos);
     float C[8], S[8];
     rope_coeffs<NEOX>(a.cos_sin + pos * 64, chunk_of(lane & 7), C, S);
-    __shared__ __attribute__((aligned(16))) uint32_t stage[kWavesPerBlock][32 * kSglangRecord / 4];
+    __shared__ __attribute__((aligned(16))) uint32_t stage[kWavesPerBlock][64 * kSglangRecord / 4];
     q_sglang_token<NEOX>(a, t, lane, C, S, stage[wave]);
 }
 
