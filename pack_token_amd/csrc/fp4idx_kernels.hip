@@ -421,15 +421,17 @@ __global__ __launch_bounds__(kBlock) void qk_small_kernel(QArgs qa, KArgs ka) {
     const int g8 = (int)(wid - t * groups);
     const int H = qa.H;
     const int J = qa.J;
+    // The token's position is read first: it heads the only chain of dependent
+    // reads (position, then the cos/sin row).  The key row shares the query's
+    // position and table (one call, one positions and one cos_sin argument) and,
+    // on lanes 0..15, its RoPE coefficients C/S, so it adds no round trip.
+    const int64_t pos = clamped_position(qa.positions, qa.pos64, t, qa.max_pos);
     const bool krow = WITH_KEY && g8 == 0 && lane < 16;
     uint4 kv = make_uint4(0u, 0u, 0u, 0u);
     int64_t kslot = -1;
-    float KC[8], KS[8];
     if (krow) {
         kv = load16_stream(ka.k + t * 128 + 8 * chunk_of(lane));
         kslot = ka.slot_mapping[t];
-        const int64_t kpos = clamped_position(ka.positions, ka.pos64, t, ka.max_pos);
-        rope_coeffs<NEOX>(ka.cos_sin + kpos * 64, chunk_of(lane & 7), KC, KS);
     }
     uint8_t* qs = qa.q_scale_out + t * 64 * (int64_t)J;
     if (g8 == 0) {
@@ -439,7 +441,6 @@ __global__ __launch_bounds__(kBlock) void qk_small_kernel(QArgs qa, KArgs ka) {
         for (int i = lane; i < 64 * J; i += 64)
             if ((i % J) >= used) qs[i] = 0;
     }
-    const int64_t pos = clamped_position(qa.positions, qa.pos64, t, qa.max_pos);
     float C[8], S[8];
     rope_coeffs<NEOX>(qa.cos_sin + pos * 64, chunk_of(lane & 7), C, S);
     const int ro = qa.rope_offset;
@@ -475,7 +476,7 @@ __global__ __launch_bounds__(kBlock) void qk_small_kernel(QArgs qa, KArgs ka) {
             qs[(g * 16 + (h1 & 15)) * J + (h1 >> 4)] = (uint8_t)q1.e;
         }
     }
-    if (krow && kslot >= 0 && kslot < ka.nslots) k_row<NEOX, NORM, HAD>(ka, kv, kslot, lane, KC, KS);
+    if (krow && kslot >= 0 && kslot < ka.nslots) k_row<NEOX, NORM, HAD>(ka, kv, kslot, lane, C, S);
 }
 
 // ---- dequantization (debug reader) -------------------------------------------
