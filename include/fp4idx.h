@@ -50,7 +50,12 @@
  *   size, flag outside {0,1}, inconsistent optional arguments, non-finite or
  *   negative floor/eps; FP4IDX_EUNSUPPORTED (2): a shape outside the list
  *   above, the message names the argument and its value; FP4IDX_EHIP (3): a
- *   HIP launch error, the message carries the HIP error string.
+ *   HIP launch error, the message carries the HIP error string.  One call is
+ *   one launch, and a launch covers at most 2^32 - 1 work-items (the grid size
+ *   of a dispatch is 32-bit): a call past that (about 53 M query tokens,
+ *   268 M keys or key rows, or dequant_debug of more than 2^28 - 1 rows x H
+ *   query heads) returns FP4IDX_EHIP ("invalid configuration") with nothing
+ *   enqueued.
  *   All validation happens before anything is enqueued: on a non-zero return
  *   nothing has been written.  T == 0 (rows == 0) is a successful no-op once
  *   the shape arguments are valid.  fp4idx_last_error() describes the last

@@ -335,8 +335,15 @@ __device__ __forceinline__ int64_t clamped_position(const void* positions, int p
     return p >= max_pos ? max_pos - 1 : p;
 }
 
+// A dispatch's grid size is a 32-bit work-item count: a launch past it would
+// wrap, so it is refused before anything is enqueued.
+inline bool grid_fits(int64_t blocks, int64_t threads) {
+    return blocks >= 0 && blocks <= (int64_t)0xFFFFFFFF / threads;
+}
+
 template <typename K, typename A>
 hipError_t launch(K kernel, int64_t blocks, size_t lds, hipStream_t stream, const A& a) {
+    if (!grid_fits(blocks, kBlock)) return hipErrorInvalidConfiguration;
     A copy = a;
     void* args[] = {&copy};
     return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)blocks),
@@ -346,6 +353,7 @@ hipError_t launch(K kernel, int64_t blocks, size_t lds, hipStream_t stream, cons
 template <typename K>
 hipError_t launch2(K kernel, int64_t blocks, size_t lds, hipStream_t stream, const QArgs& qa,
                    const KArgs& ka, unsigned threads = kBlock) {
+    if (!grid_fits(blocks, threads)) return hipErrorInvalidConfiguration;
     QArgs q = qa;
     KArgs k = ka;
     void* args[] = {&q, &k};
