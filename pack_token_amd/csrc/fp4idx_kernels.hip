@@ -62,17 +62,7 @@ __device__ __forceinline__ void q_split_token(const QArgs& a, int64_t t, int lan
     const uint16_t* qt = a.q + t * (int64_t)H * 128 + hsub * 128 + 8 * c;
     uint8_t* ot = a.q_out + t * (int64_t)H * 64 + hsub * 64 + 4 * c;
 
-    uint4 np0 = load16_stream(qt + nro), nr0 = load16_stream(qt + ro);
-    uint4 np1 = load16_stream(qt + 8 * 128 + nro), nr1 = load16_stream(qt + 8 * 128 + ro);
-    for (int hb = 0; hb < H; hb += 16) {
-        const uint4 p0 = np0, r0 = nr0, p1 = np1, r1 = nr1;
-        if (hb + 16 < H) {
-            const uint16_t* nx = qt + (hb + 16) * 128;
-            np0 = load16_stream(nx + nro);
-            nr0 = load16_stream(nx + ro);
-            np1 = load16_stream(nx + 8 * 128 + nro);
-            nr1 = load16_stream(nx + 8 * 128 + ro);
-        }
+    auto step = [&](int hb, uint4 p0, uint4 r0, uint4 p1, uint4 r1) {
         const Q8 qp0 = quant8(p0, a.e_lo);
         const Q8 qr0 = quant8(rope8<NEOX>(r0, C, S), a.e_lo);
         const Q8 qp1 = quant8(p1, a.e_lo);
@@ -89,6 +79,25 @@ __device__ __forceinline__ void q_split_token(const QArgs& a, int64_t t, int lan
             scb[(g_pln * 16 + (h1 & 15)) * J + (h1 >> 4)] = (uint8_t)qp1.e;
             scb[(g_rot * 16 + (h1 & 15)) * J + (h1 >> 4)] = (uint8_t)qr1.e;
         }
+    };
+    // Two register sets take turns: one is computed while the other loads the
+    // next 16 heads (a single set refilled from prefetch registers costs 16
+    // register moves per step).
+    auto load = [&](int hb, uint4& p0, uint4& r0, uint4& p1, uint4& r1) {
+        const uint16_t* nx = qt + hb * 128;
+        p0 = load16_stream(nx + nro);
+        r0 = load16_stream(nx + ro);
+        p1 = load16_stream(nx + 8 * 128 + nro);
+        r1 = load16_stream(nx + 8 * 128 + ro);
+    };
+    uint4 ap0, ar0, ap1, ar1, bp0, br0, bp1, br1;
+    load(0, ap0, ar0, ap1, ar1);
+    for (int hb = 0; hb < H; hb += 32) {
+        if (hb + 16 < H) load(hb + 16, bp0, br0, bp1, br1);
+        step(hb, ap0, ar0, ap1, ar1);
+        if (hb + 16 >= H) break;
+        if (hb + 32 < H) load(hb + 32, ap0, ar0, ap1, ar1);
+        step(hb + 16, bp0, br0, bp1, br1);
     }
 }
 

@@ -98,17 +98,9 @@ __device__ __forceinline__ void q_sglang_token(const SQArgs& a, int64_t t, int l
     uint8_t* ot = reinterpret_cast<uint8_t*>(stage) + hsub * kSglangRecord + 4 * c;
     uint8_t* const out = a.q_packed + t * (int64_t)H * kSglangRecord;
 
-    uint4 np0 = load16_stream(qt + nro), nr0 = load16_stream(qt + ro);
-    uint4 np1 = load16_stream(qt + 8 * 128 + nro), nr1 = load16_stream(qt + 8 * 128 + ro);
-    for (int hb = 0; hb < H; hb += 16) {
-        const uint4 p0 = np0, r0 = nr0, p1 = np1, r1 = nr1;
-        if (hb + 16 < H) {
-            const uint16_t* nx = qt + (hb + 16) * 128;
-            np0 = load16_stream(nx + nro);
-            nr0 = load16_stream(nx + ro);
-            np1 = load16_stream(nx + 8 * 128 + nro);
-            nr1 = load16_stream(nx + 8 * 128 + ro);
-        }
+    // one 16-head step: quantize the four loaded chunks, stage the records,
+    // flush a full run of 64 heads (or the last 16-48)
+    auto step = [&](int hb, uint4 p0, uint4 r0, uint4 p1, uint4 r1) {
         const Q8 qp0 = quant8_two_stage(p0, a.e_lo1, a.e_lo2);
         const Q8 qr0 = quant8_two_stage(rope8<NEOX>(r0, C, S), a.e_lo1, a.e_lo2);
         const Q8 qp1 = quant8_two_stage(p1, a.e_lo1, a.e_lo2);
@@ -135,6 +127,25 @@ __device__ __forceinline__ void q_sglang_token(const SQArgs& a, int64_t t, int l
                 store16_stream(out + h0 * kSglangRecord + 16 * i, src[i]);
             wave_sync();
         }
+    };
+    // Two register sets take turns: set A is computed while set B loads the
+    // next 16 heads, then the roles swap.  (A single set copied from the
+    // prefetch registers each step cost 16 moves per step.)
+    auto load = [&](int hb, uint4& p0, uint4& r0, uint4& p1, uint4& r1) {
+        const uint16_t* nx = qt + hb * 128;
+        p0 = load16_stream(nx + nro);
+        r0 = load16_stream(nx + ro);
+        p1 = load16_stream(nx + 8 * 128 + nro);
+        r1 = load16_stream(nx + 8 * 128 + ro);
+    };
+    uint4 ap0, ar0, ap1, ar1, bp0, br0, bp1, br1;
+    load(0, ap0, ar0, ap1, ar1);
+    for (int hb = 0; hb < H; hb += 32) {
+        if (hb + 16 < H) load(hb + 16, bp0, br0, bp1, br1);
+        step(hb, ap0, ar0, ap1, ar1);
+        if (hb + 16 >= H) break;
+        if (hb + 32 < H) load(hb + 32, ap0, ar0, ap1, ar1);
+        step(hb + 16, bp0, br0, bp1, br1);
     }
 }
 
