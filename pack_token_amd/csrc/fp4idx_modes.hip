@@ -396,19 +396,26 @@ __global__ __launch_bounds__(kBlock) void q_fp8_split_kernel(FQArgs a) {
     float C[8], S[8];
     rope_coeffs<NEOX>(a.cos_sin + pos * 64, c, C, S);
     const uint16_t* qt = a.q + t * (int64_t)H * 128 + hsub * 128 + 8 * c;
-    uint4 np0 = load16_stream(qt + nro), nr0 = load16_stream(qt + ro);
-    uint4 np1 = load16_stream(qt + 8 * 128 + nro), nr1 = load16_stream(qt + 8 * 128 + ro);
-    for (int hb = 0; hb < H; hb += 16) {
-        const uint4 p0 = np0, r0 = nr0, p1 = np1, r1 = nr1;
-        if (hb + 16 < H) {
-            const uint16_t* nx = qt + (hb + 16) * 128;
-            np0 = load16_stream(nx + nro);
-            nr0 = load16_stream(nx + ro);
-            np1 = load16_stream(nx + 8 * 128 + nro);
-            nr1 = load16_stream(nx + 8 * 128 + ro);
-        }
+    // two load-register sets take turns (no per-step copy of a prefetch set)
+    auto load = [&](int hb, uint4& p0, uint4& r0, uint4& p1, uint4& r1) {
+        const uint16_t* nx = qt + hb * 128;
+        p0 = load16_stream(nx + nro);
+        r0 = load16_stream(nx + ro);
+        p1 = load16_stream(nx + 8 * 128 + nro);
+        r1 = load16_stream(nx + 8 * 128 + ro);
+    };
+    auto step = [&](int hb, uint4 p0, uint4 r0, uint4 p1, uint4 r1) {
         fp8_split_head<NEOX, FP32>(a, p0, r0, t, hb + hsub, c, C, S);
         fp8_split_head<NEOX, FP32>(a, p1, r1, t, hb + 8 + hsub, c, C, S);
+    };
+    uint4 ap0, ar0, ap1, ar1, bp0, br0, bp1, br1;
+    load(0, ap0, ar0, ap1, ar1);
+    for (int hb = 0; hb < H; hb += 32) {
+        if (hb + 16 < H) load(hb + 16, bp0, br0, bp1, br1);
+        step(hb, ap0, ar0, ap1, ar1);
+        if (hb + 16 >= H) break;
+        if (hb + 32 < H) load(hb + 32, ap0, ar0, ap1, ar1);
+        step(hb + 16, bp0, br0, bp1, br1);
     }
 }
 
