@@ -1,7 +1,8 @@
 """The other output modes captured in a HIP graph: the sglang-compatible
-records, the FP8 mode and the fake quant, each captured once and replayed three
-times with new inputs copied in (eager work) between replays; every replay
-must equal the oracle on that replay's inputs, byte for byte."""
+records, the FP8 mode, the fake quant and the FP4 MQA-logits scorer, each
+captured once and replayed three times with new inputs copied in (eager work)
+between replays; every replay must equal the oracle on that replay's inputs,
+byte for byte (the scorer: within its fp32 bound)."""
 import numpy as np
 import pytest
 
@@ -143,3 +144,49 @@ def test_fake_quant_graph_replay(mode):
         ref = oracle.rope_fake_quant(wl.q, base.positions, base.cos_sin, rows_per_position=H,
                                      mode=m, compress_ratio=4)
         assert_same("y", y.cpu().numpy().view(np.uint16), ref)
+
+
+@pytest.mark.parametrize("next_n,H", [(4, 32), (67, 64)])
+def test_scorer_graph_replay(next_n, H):
+    """The FP4 MQA-logits scorer (decode, and chunked prefill with its LDS
+    fetch-ahead) captured once and replayed three times with new query and key
+    bytes copied in between; every replay within the scorer's fp32 bound of the
+    oracle, -inf and untouched entries identical."""
+    import torch
+    from pack_token_amd import fp4idx
+    from test_gpu_scorer import SENT, check_scorer
+    dev = "cuda:0"
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    base = workloads.scorer_case(5000 + next_n, 3, next_n, H, 1, 900)
+    q, qs, w = up(base.q_out), up(base.q_scale_out), up(base.weights)
+    kv, ks = up(base.kv_cache), up(base.kv_cache_scale)
+    table, ctx = up(base.block_table), up(base.context_lens)
+    stride = base.max_blocks * 64
+    logits = torch.full((base.B * next_n, stride), float(SENT), dtype=torch.float32, device=dev)
+
+    def step():
+        fp4idx.paged_mqa_logits(q, qs, w, kv, ks, table, ctx, next_n, weights_scale=0.5,
+                                logits=logits)
+
+    g = _capture(step)
+    import copy
+    for rep in range(1, 4):
+        rng = np.random.default_rng(rep)
+        sc = copy.copy(base)   # same shapes, tables and scales; new codes and weights
+        sc.q_out = rng.integers(0, 256, base.q_out.shape, dtype=np.uint8)
+        sc.kv_cache = rng.integers(0, 256, base.kv_cache.shape, dtype=np.uint8)
+        sc.weights = rng.random(base.weights.shape, dtype=np.float32)
+        q.copy_(up(sc.q_out))
+        qs.copy_(up(sc.q_scale_out))
+        w.copy_(up(sc.weights))
+        kv.copy_(up(sc.kv_cache))
+        ks.copy_(up(sc.kv_cache_scale))
+        logits.fill_(float(SENT))
+        torch.cuda.synchronize()
+        say(f"case scorer graph replay next_n={next_n} H={H} rep {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        ref, bound = oracle.paged_mqa_logits(sc.q_out, sc.q_scale_out, sc.weights, sc.kv_cache,
+                                             sc.kv_cache_scale, sc.block_table, sc.context_lens,
+                                             next_n, weights_scale=0.5, with_bound=True)
+        check_scorer(logits.cpu().numpy(), ref, bound, H)
