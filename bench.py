@@ -130,6 +130,76 @@ def median_wall(fn, reps: int = 3) -> float:
     return sorted(ts)[len(ts) // 2]
 
 
+def time_legs(legs: dict, K: int, W: int, rounds: int, stream, settle_ms: float = 0.0):
+    """Times each leg (a list of calls launched back to back as one step) over
+    exactly K steps per round, with only two events around the K steps.  W
+    untimed steps of every leg come first, then untimed steps of the first leg
+    until settle_ms of GPU time has passed (clock ramp-up).  The legs run in
+    alternating order from round to round, so no leg always runs on the
+    coldest or the warmest GPU.  Returns {leg: [ms per step of each round]}."""
+    import torch
+
+    names = list(legs)
+    for name in names:
+        for _ in range(W):
+            for c in legs[name]:
+                c()
+    torch.cuda.synchronize()
+    if settle_ms > 0:
+        s0 = torch.cuda.Event(enable_timing=True)
+        s1 = torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for c in legs[names[0]]:
+            c()
+        s1.record(stream)
+        torch.cuda.synchronize()
+        n = int(settle_ms / max(s0.elapsed_time(s1), 1e-3)) + 1
+        for _ in range(n):
+            for c in legs[names[0]]:
+                c()
+        torch.cuda.synchronize()
+    out = {name: [] for name in names}
+    for r in range(rounds):
+        for name in (names if r % 2 == 0 else names[::-1]):
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0.record(stream)
+            for _ in range(K):
+                for c in legs[name]:
+                    c()
+            t1.record(stream)
+            torch.cuda.synchronize()
+            out[name].append(t0.elapsed_time(t1) / K)
+    return out
+
+
+def launch_pass(calls, K: int, stream):
+    """Per-launch durations (ms) of each call over K steps, each launch between
+    its own pair of events on `stream` (a pass of its own, after the timed
+    steps).  Returns ([mean per call], [median per call])."""
+    import numpy as np
+    import torch
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        ev[i][0].record(stream)
+        for j, c in enumerate(calls):
+            c()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    d = [[e[j].elapsed_time(e[j + 1]) for e in ev] for j in range(len(calls))]
+    return [float(np.mean(x)) for x in d], [float(np.median(x)) for x in d]
+
+
+def median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
 def oracle_baseline(run, n: int, what: str, T: int, threads: int = 1,
                     noun: str = "tokens") -> dict:
     """cpu_baseline record for run() processing n units (median of 3 walls)."""
@@ -162,6 +232,40 @@ def cpu_baseline(wl, n_tokens: int, threads: int):
     rec["single_thread_value"] = n1 / dt1
     rec["single_thread_sample"] = f"first {n1} tokens, 1 thread, median of 3 runs, {dt1:.2f} s wall"
     return rec
+
+
+def oracle_parity(wl, outputs: dict, threads: int) -> dict:
+    """The oracle (test infrastructure) on every token of the workload, its five
+    outputs compared byte for byte with the GPU's: {path: mismatched bytes}."""
+    import numpy as np
+
+    import oracle
+
+    q_out, qs, w_out = oracle.q_rope_pack(wl.q, wl.positions, wl.cos_sin, wl.weights,
+                                          is_neox=wl.is_neox, rope_offset=wl.rope_offset,
+                                          apply_hadamard=wl.apply_hadamard,
+                                          scale_floor=wl.scale_floor, threads=threads)
+    kv, ks = wl.empty_cache()
+    kw = dict(k_norm_gamma=wl.k_norm_gamma, k_norm_eps=wl.k_norm_eps, is_neox=wl.is_neox,
+              rope_offset=wl.rope_offset, apply_hadamard=wl.apply_hadamard,
+              scale_floor=wl.scale_floor, threads=threads)
+    if wl.background is not None:
+        oracle.k_rope_pack_store(wl.background["k"], wl.background["positions"], wl.cos_sin,
+                                 wl.background["slots"], kv, ks, **kw)
+    oracle.k_rope_pack_store(wl.k, wl.positions, wl.cos_sin, wl.slot_mapping, kv, ks, **kw)
+    ref = (q_out, qs, w_out.view(np.uint8), kv, ks)
+    out = {}
+    for path, got in outputs.items():
+        bad = 0
+        for g, r in zip(got, ref):
+            g = g.view(np.uint8).reshape(-1)
+            r = r.view(np.uint8).reshape(-1)
+            if g.size != r.size:
+                bad += max(g.size, r.size)
+            else:
+                bad += int(np.count_nonzero(g != r))
+        out[path] = bad
+    return out
 
 
 FP4_MFMA_PEAK_TFLOPS = 10100.0
@@ -222,26 +326,10 @@ def bench_fp8(args, dev):
         def k_call():
             fp4idx.k_rope_pack_store_fp8(k, pos, cs, slots, kv, ks, scale_fmt=fmt, stream=stream)
 
-        for _ in range(args.warmup):
-            q_call()
-            k_call()
-        torch.cuda.synchronize()
-        K = args.steps
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        for i in range(K):
-            ev[i][0].record(stream)
-            q_call()
-            ev[i][1].record(stream)
-            k_call()
-            ev[i][2].record(stream)
-        t1.record(stream)
-        torch.cuda.synchronize()
-        return (t0.elapsed_time(t1) / K,
-                float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
-                float(np.mean([e[1].elapsed_time(e[2]) for e in ev])))
+        legs = time_legs({"step": [q_call, k_call]}, args.steps, args.warmup, args.rounds, stream,
+                         settle_ms=args.settle_ms)
+        (q_l, k_l), _ = launch_pass([q_call, k_call], args.steps, stream)
+        return median(legs["step"]), q_l, k_l
 
     ms, q_ms, k_ms = run("ue8m0")
     ms32, q_ms32, k_ms32 = run("fp32")
@@ -303,21 +391,10 @@ def bench_fake_quant(args, dev):
     def run(mode):
         def call():
             fp4idx.rope_fake_quant(q, pos, cs, y=y, rows_per_position=H, mode=mode, stream=stream)
-        for _ in range(args.warmup):
-            call()
-        torch.cuda.synchronize()
-        K = args.steps
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        for i in range(K):
-            ev[i][0].record(stream)
-            call()
-            ev[i][1].record(stream)
-        t1.record(stream)
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / K, float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        legs = time_legs({"step": [call]}, args.steps, args.warmup, args.rounds, stream,
+                         settle_ms=args.settle_ms)
+        (l_ms,), _ = launch_pass([call], args.steps, stream)
+        return median(legs["step"]), l_ms
 
     ms, l_ms = run("e4m3_16")
     ms8, l_ms8 = run("ue8m0_32")
@@ -387,26 +464,11 @@ def bench_sglang(args, dev):
     def k_call():
         fp4idx.k_rope_pack_store_sglang(k, pos, cs, slots, cache, stream=stream)
 
-    for _ in range(args.warmup):
-        q_call()
-        k_call()
-    torch.cuda.synchronize()
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(K):
-        ev[i][0].record(stream)
-        q_call()
-        ev[i][1].record(stream)
-        k_call()
-        ev[i][2].record(stream)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / K
-    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    k_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    legs = time_legs({"step": [q_call, k_call]}, K, args.warmup, args.rounds, stream,
+                     settle_ms=args.settle_ms)
+    ms_per_step = median(legs["step"])
+    (q_ms, k_ms), _ = launch_pass([q_call, k_call], K, stream)
     qb = sglang_q_bytes_per_token(H) * T
     kb = sglang_k_bytes_per_token() * T
     q_gbs = qb / (q_ms * 1e-3) / 1e9
@@ -464,23 +526,12 @@ def bench_scorer(args, dev):
     def call():
         fp4idx.paged_mqa_logits(q, qs, w, kv, ks, table, ctx, next_n, logits=logits)
 
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
     stream = torch.cuda.current_stream(dev)
-    t0.record(stream)
-    for i in range(K):
-        ev[i][0].record(stream)
-        call()
-        ev[i][1].record(stream)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / K
-    launch_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    legs = time_legs({"step": [call]}, K, args.warmup, args.rounds, stream,
+                     settle_ms=args.settle_ms)
+    ms_per_step = median(legs["step"])
+    (launch_ms,), _ = launch_pass([call], K, stream)
     keys = int(sc.context_lens.astype(np.int64).sum())
     blocks = int(sum(-(-int(c) // 64) for c in sc.context_lens))
     J = workloads.q_scale_cols(H)
@@ -551,22 +602,11 @@ def bench_prefill_scoring(args, dev):
     def call():
         fp4idx.paged_mqa_logits(q, qs, w, kv, ks, table, ctx, next_n, logits=logits)
 
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(K):
-        ev[i][0].record(stream)
-        call()
-        ev[i][1].record(stream)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / K
-    launch_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    legs = time_legs({"step": [call]}, K, args.warmup, args.rounds, stream,
+                     settle_ms=args.settle_ms)
+    ms_per_step = median(legs["step"])
+    (launch_ms,), _ = launch_pass([call], K, stream)
     pos = np.arange(ctx_len - next_n, ctx_len, dtype=np.int64)
     pairs = int((pos + 1).sum())
     flops = 2.0 * 128 * H * pairs
@@ -618,6 +658,11 @@ def main():
                     help="time steps replayed from captured HIP graphs (auto: on for decode, where "
                          "host launch overhead exceeds the kernel time)")
     ap.add_argument("--graph-steps", type=int, default=10, help="steps captured per graph")
+    ap.add_argument("--rounds", type=int, default=3,
+                    help="timed rounds of K steps per leg (legs alternate; median reported)")
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="untimed GPU time spent on steps after the warm-up steps, so clocks "
+                         "have ramped up before timing")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="instead of the benchmark, time one plain device copy of this many MiB "
                          "(reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -693,8 +738,8 @@ def main():
     q_out = torch.empty((T, H, 64), dtype=torch.uint8, device=dev)
     qs = torch.empty((T, 1, 4, 16, J), dtype=torch.uint8, device=dev)
     w_out = torch.empty_like(w)
-    kv = torch.zeros((wl.NB, 1, 4, 64, 16), dtype=torch.uint8, device=dev)
-    ks = torch.zeros((wl.NB, 1, 4, 64), dtype=torch.uint8, device=dev)
+    kv = torch.full((wl.NB, 1, 4, 64, 16), workloads.SENTINEL, dtype=torch.uint8, device=dev)
+    ks = torch.full((wl.NB, 1, 4, 64), workloads.SENTINEL, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     gamma = None if wl.k_norm_gamma is None else up(wl.k_norm_gamma.view(np.int16))
 
@@ -703,12 +748,15 @@ def main():
     common = dict(is_neox=wl.is_neox, rope_offset=wl.rope_offset,
                   apply_hadamard=wl.apply_hadamard, stream=None)
     kcommon = dict(common, k_norm_gamma=gamma, k_norm_eps=wl.k_norm_eps)
-    if wl.background is not None:
-        # fill the cache with the background keys first (not timed)
+    def fill_background():
+        # the cache's background keys, written before the step (not timed)
         fp4idx.k_rope_pack_store(up(wl.background["k"].view(np.int16)),
                                  up(wl.background["positions"]), cs, up(wl.background["slots"]),
                                  kv, ks, **kcommon)
         torch.cuda.synchronize()
+
+    if wl.background is not None:
+        fill_background()
 
     def q_call():
         fp4idx.q_rope_pack(q, pos, cs, w, q_out=q_out, q_scale_out=qs, weights_out=w_out, **common)
@@ -719,30 +767,6 @@ def main():
     def qk_call():
         fp4idx.qk_rope_pack_store(q, k, pos, cs, slots, kv, ks, w, q_out=q_out, q_scale_out=qs,
                                   weights_out=w_out, **kcommon)
-
-    def timed(calls, K, W):
-        """Run W untimed then K timed steps of `calls` (launched back to back on
-        `stream`); returns (ms per step, [mean ms of each call's launch],
-        [median ms of each call's launch])."""
-        for _ in range(W):
-            for c in calls:
-                c()
-        torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
-              for _ in range(K)]
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        for i in range(K):
-            ev[i][0].record(stream)
-            for j, c in enumerate(calls):
-                c()
-                ev[i][j + 1].record(stream)
-        t1.record(stream)
-        torch.cuda.synchronize()
-        per_launch = [[e[j].elapsed_time(e[j + 1]) for e in ev] for j in range(len(calls))]
-        return (t0.elapsed_time(t1) / K, [float(np.mean(d)) for d in per_launch],
-                [float(np.median(d)) for d in per_launch])
 
     use_graph = args.graph == "on" or (args.graph == "auto" and wl.name == "decode")
 
@@ -766,17 +790,24 @@ def main():
         return g.replay
 
     K = args.steps
-    # per-launch durations always come from eager launches bracketed by events
-    ms_per_step, (fused_ms,), (fused_med_ms,) = timed([qk_call], K, args.warmup)
-    two_ms, (q_ms, k_ms), _ = timed([q_call, k_call], K, args.warmup)
+    R = max(1, args.rounds)
+    # headline and two-call step: K steps per round between two events, legs
+    # alternating in order from round to round, the median round reported
+    legs = time_legs({"fused": [qk_call], "two_call": [q_call, k_call]}, K, args.warmup, R,
+                     stream, settle_ms=args.settle_ms)
+    ms_per_step, two_ms = median(legs["fused"]), median(legs["two_call"])
+    # per-launch durations in a pass of their own (events around every launch)
+    (fused_ms,), (fused_med_ms,) = launch_pass([qk_call], K, stream)
+    (q_ms, k_ms), _ = launch_pass([q_call, k_call], K, stream)
     if use_graph:
         # step time from graph replays: K steps = ceil(K / G) replays of G steps
         reps = -(-K // G)
         K = reps * G
-        g_ms, _, _ = timed([graphed([qk_call])], reps, max(1, args.warmup // G))
-        g2_ms, _, _ = timed([graphed([q_call, k_call])], reps, max(1, args.warmup // G))
+        glegs = time_legs({"fused": [graphed([qk_call])],
+                           "two_call": [graphed([q_call, k_call])]}, reps,
+                          max(1, args.warmup // G), R, stream)
         eager_ms_per_step, eager_two_ms = ms_per_step, two_ms
-        ms_per_step, two_ms = g_ms / G, g2_ms / G
+        ms_per_step, two_ms = median(glegs["fused"]) / G, median(glegs["two_call"]) / G
 
     step_bytes = step_bytes_per_token(H) * T
     achieved = step_bytes / (fused_ms * 1e-3) / 1e9
@@ -803,6 +834,12 @@ def main():
                    "graph_replay": use_graph, "graph_steps": G if use_graph else None},
         "step_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "step_frac_of_hbm_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "timing": {"rounds": R, "fused_ms_per_step_rounds": legs["fused"],
+                   "two_call_ms_per_step_rounds": legs["two_call"],
+                   "settle_ms": args.settle_ms,
+                   "note": "each round times K steps of each leg between two events, legs in "
+                           "alternating order; ms_per_step is the median round; per-launch "
+                           "durations come from a separate pass with events around every launch"},
         "two_call_step": {"calls": "fp4idx_q_rope_pack + fp4idx_k_rope_pack_store",
                           "ms_per_step": two_ms, "tokens_per_s": T / (two_ms * 1e-3),
                           "GBps": step_bytes / (two_ms * 1e-3) / 1e9,
@@ -834,8 +871,27 @@ def main():
         rec["eager_ms_per_step"] = eager_ms_per_step
         rec["two_call_step"]["eager_ms_per_step"] = eager_two_ms
     if not args.no_cpu_baseline:
+        # outputs of one fused launch and of one two-call step, each from
+        # sentinel-filled buffers (untimed), for the parity check
+        def outputs_of(calls):
+            for o in (q_out, qs, kv, ks):
+                o.fill_(workloads.SENTINEL)
+            w_out.fill_(float("nan"))
+            if wl.background is not None:
+                fill_background()
+            for c in calls:
+                c()
+            torch.cuda.synchronize()
+            return tuple(x.cpu().numpy() for x in (q_out, qs, w_out, kv, ks))
+
+        got = {"fused": outputs_of([qk_call]), "two_call": outputs_of([q_call, k_call])}
         threads = max(1, min(16, len(os.sched_getaffinity(0))))
         rec["cpu_baseline"] = cpu_baseline(wl, min(args.cpu_sample_tokens, T), threads)
+        rec["parity"] = {"tokens": T, "outputs": ["q_out", "q_scale_out", "weights_out",
+                                                  "kv_cache", "kv_cache_scale"],
+                         "mismatched_bytes": oracle_parity(wl, got, threads),
+                         "against": "the CPU oracle on every token, byte for byte"}
+        del got
     print(json.dumps(rec), flush=True)
 
 

@@ -257,8 +257,11 @@ SLOT68 = 68
 
 
 def q_rope_pack_sglang(q_bits, positions, cos_sin, *, is_neox=True, rope_offset=64,
-                       fake_quant_floor=DEFAULT_SCALE_FLOOR, pack_floor=DEFAULT_SCALE_FLOOR):
-    """sglang-compatible query side: records u8 [T,H,68] (64 code bytes, 4 exponents)."""
+                       fake_quant_floor=DEFAULT_SCALE_FLOOR, pack_floor=DEFAULT_SCALE_FLOOR,
+                       threads=1):
+    """sglang-compatible query side: records u8 [T,H,68] (64 code bytes, 4 exponents).
+    threads > 1 splits the tokens into ranges, each a separate call (tokens are
+    independent)."""
     q_bits = _c(q_bits, np.uint16)
     T, H, D = q_bits.shape
     positions = np.ascontiguousarray(positions)
@@ -267,12 +270,21 @@ def q_rope_pack_sglang(q_bits, positions, cos_sin, *, is_neox=True, rope_offset=
         positions = _c(positions, np.int32)
     cos_sin = _c(cos_sin, np.float32)
     out = np.full((T, H, SLOT68), 0xA5, np.uint8)
-    rc = _lib().oracle_q_rope_pack_sglang(q_bits.ctypes.data, positions.ctypes.data, pos64,
-                                          cos_sin.ctypes.data, cos_sin.shape[0], T, H, D, ROPE_DIM,
-                                          rope_offset, 32, int(bool(is_neox)), fake_quant_floor,
-                                          pack_floor, out.ctypes.data)
-    if rc != 0:
-        raise ValueError(f"oracle_q_rope_pack_sglang rejected its arguments (rc={rc})")
+    lib = _lib()
+    psz = positions.itemsize
+
+    def run(rng):
+        a, b = rng
+        rc = lib.oracle_q_rope_pack_sglang(q_bits.ctypes.data + a * H * D * 2,
+                                           positions.ctypes.data + a * psz, pos64,
+                                           cos_sin.ctypes.data, cos_sin.shape[0], b - a, H, D,
+                                           ROPE_DIM, rope_offset, 32, int(bool(is_neox)),
+                                           fake_quant_floor, pack_floor,
+                                           out.ctypes.data + a * H * SLOT68)
+        if rc != 0:
+            raise ValueError(f"oracle_q_rope_pack_sglang rejected its arguments (rc={rc})")
+
+    _run_ranges(run, _split(T, threads))
     return out
 
 
@@ -322,8 +334,9 @@ def _positions(positions):
 
 def q_rope_pack_fp8(q_bits, positions, cos_sin, weights, *, weights_scale=1.0, is_neox=True,
                     rope_offset=64, apply_hadamard=False, scale_fmt=FP8_UE8M0,
-                    scale_floor=DEFAULT_SCALE_FLOOR):
-    """FP8 output mode, query side: (q_out u8 [T,H,128], weights_out bf16 bits u16 [T,H])."""
+                    scale_floor=DEFAULT_SCALE_FLOOR, threads=1):
+    """FP8 output mode, query side: (q_out u8 [T,H,128], weights_out bf16 bits u16 [T,H]).
+    threads > 1 splits the tokens into ranges, each a separate call."""
     q_bits = _c(q_bits, np.uint16)
     T, H, D = q_bits.shape
     positions, pos64 = _positions(positions)
@@ -331,13 +344,23 @@ def q_rope_pack_fp8(q_bits, positions, cos_sin, weights, *, weights_scale=1.0, i
     weights = _c(weights, np.float32)
     q_out = np.full((T, H, D), 0xA5, np.uint8)
     w_out = np.full((T, H), 0xFFFF, np.uint16)
-    rc = _lib().oracle_q_rope_pack_fp8(q_bits.ctypes.data, positions.ctypes.data, pos64,
-                                       cos_sin.ctypes.data, cos_sin.shape[0], weights.ctypes.data,
-                                       weights_scale, T, H, D, ROPE_DIM, rope_offset,
-                                       int(bool(is_neox)), int(bool(apply_hadamard)), scale_fmt,
-                                       scale_floor, q_out.ctypes.data, w_out.ctypes.data)
-    if rc != 0:
-        raise ValueError(f"oracle_q_rope_pack_fp8 rejected its arguments (rc={rc})")
+    lib = _lib()
+    psz = positions.itemsize
+
+    def run(rng):
+        a, b = rng
+        rc = lib.oracle_q_rope_pack_fp8(q_bits.ctypes.data + a * H * D * 2,
+                                        positions.ctypes.data + a * psz, pos64,
+                                        cos_sin.ctypes.data, cos_sin.shape[0],
+                                        weights.ctypes.data + a * H * 4, weights_scale, b - a, H,
+                                        D, ROPE_DIM, rope_offset, int(bool(is_neox)),
+                                        int(bool(apply_hadamard)), scale_fmt, scale_floor,
+                                        q_out.ctypes.data + a * H * D,
+                                        w_out.ctypes.data + a * H * 2)
+        if rc != 0:
+            raise ValueError(f"oracle_q_rope_pack_fp8 rejected its arguments (rc={rc})")
+
+    _run_ranges(run, _split(T, threads))
     return q_out, w_out
 
 

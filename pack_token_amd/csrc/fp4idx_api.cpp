@@ -502,7 +502,9 @@ int fp4idx_rope_fake_quant(const void* x, int64_t rows, int64_t rows_per_positio
     a.y = static_cast<uint16_t*>(y);
     a.rows = rows;
     a.max_pos = max_pos;
-    a.rows_per_position = rows_per_position;
+    // past `rows` every row maps to position 0 either way; the clamp keeps the
+    // kernel's row arithmetic (token index x rows_per_position) inside int64
+    a.rows_per_position = rows_per_position > rows ? rows : rows_per_position;
     a.pos64 = positions_int64;
     a.rope_offset = rope_offset;
     a.compress_ratio = compress_ratio;

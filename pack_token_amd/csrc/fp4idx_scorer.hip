@@ -264,13 +264,10 @@ __global__ __launch_bounds__(64 * kWaves) void mqa_logits_kernel(LArgs a) {
         has_next = i + 1 < BPW && kb + 1 < kb_end && fetched(kb + 1, blks[i + 1]);
         if (has_next) {
             fetch_block(a, blks[i + 1], lane, kbuf[p ^ 1][wave], sbuf[p ^ 1][wave]);
-            // Without query tiles every block before this one issued exactly NQ
-            // logit stores after this block's loads (lane 0's key is always
-            // inside the context, so none is skipped): those need not land.
-            if (!TILED && i != 0)
-                __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(5 + NQ));
-            else
-                __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(5));
+            // at most the next block's 5 loads may still be in flight: this
+            // block's loads, and everything issued before them, have landed
+            // (whatever else the previous block issued)
+            __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(5));
         } else {
             __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(0));
         }

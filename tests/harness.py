@@ -18,6 +18,17 @@ def say(msg: str):
     print(msg, flush=True)
 
 
+_LARGE_PREFILL = []
+
+
+def large_prefill() -> Workload:
+    """The large-prefill workload (131,072 tokens x 64 heads), generated once per
+    test session and shared by the tests that use it (inputs are read-only)."""
+    if not _LARGE_PREFILL:
+        _LARGE_PREFILL.append(workloads.large_prefill())
+    return _LARGE_PREFILL[0]
+
+
 def dev_tensors(wl: Workload, device):
     import torch
 

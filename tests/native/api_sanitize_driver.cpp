@@ -94,6 +94,13 @@ int main() {
                                  0, 0.0f, P, nullptr) == FP4IDX_EINVAL);
     CHECK(fp4idx_rope_fake_quant(P, 64, INT64_MIN, P, 1, (const float*)P, 8, 128, 64, 64, 1, 1,
                                  0, 0.0f, P, nullptr) == FP4IDX_EINVAL);
+    // rows_per_position beyond rows (all rows on position 0) reaches the kernel clamped
+    CHECK(fp4idx_rope_fake_quant(P, 64, INT64_MAX, P, 1, (const float*)P, 8, 128, 64, 64, 1, 1,
+                                 0, 0.0f, P, nullptr) == FP4IDX_OK &&
+          g_stub.fake.rows_per_position == 64);
+    CHECK(fp4idx_rope_fake_quant(P, 640, 64, P, 1, (const float*)P, 8, 128, 64, 64, 1, 1,
+                                 0, 0.0f, P, nullptr) == FP4IDX_OK &&
+          g_stub.fake.rows_per_position == 64);
     // dequant reader
     CHECK(fp4idx_dequant_debug(0, (const uint8_t*)P, (const uint8_t*)P, 4, 32, nullptr, 0, 64,
                                (float*)P, nullptr) == FP4IDX_OK && g_stub.d.J == 4);

@@ -28,8 +28,9 @@ def test_validation_under_asan_and_ubsan():
                os.path.join(NATIVE, "api_host_stubs.cpp"),
                os.path.join(NATIVE, "api_sanitize_driver.cpp"), "-o", exe]
         subprocess.run(cmd, check=True, capture_output=True, text=True)
-        env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1",
+        # verify_asan_link_order=0: the runtime need not be first in the library list
+        env = dict(os.environ,
+                   ASAN_OPTIONS="detect_leaks=1:abort_on_error=1:verify_asan_link_order=0",
                    UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
-        env.pop("LD_PRELOAD", None)
         r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
     assert r.returncode == 0 and r.stdout.startswith("ok"), r.stdout + r.stderr

@@ -11,7 +11,7 @@ import pytest
 import oracle
 from pack_token_amd import workloads
 from pack_token_amd.workloads import SENTINEL
-from harness import assert_same, random_case, say
+from harness import ORACLE_THREADS, assert_same, large_prefill, random_case, say
 
 pytestmark = pytest.mark.gpu
 
@@ -168,20 +168,19 @@ def test_converter_fp32_scales():
 
 
 @pytest.mark.parametrize("fmt", ["ue8m0", "fp32"])
-def test_large_prefill_sampled(fmt):
-    """T = 131072, H = 64: every key (codes and scales), and the query codes and
-    folded weights of 2,051 tokens."""
-    wl = workloads.large_prefill()
+def test_large_prefill_full_size(fmt):
+    """T = 131072, H = 64: the query codes and folded weights of every token and
+    every key (codes and scales), byte for byte."""
+    wl = large_prefill()
     say(f"case fp8 large_prefill fmt={fmt}")
     got_q, got_w = gpu_q(wl.q, wl.positions, wl.cos_sin, wl.weights, scale_fmt=fmt)
-    rng = np.random.default_rng(13)
-    idx = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 2049, replace=False)]))
     ofmt = {"ue8m0": 0, "fp32": 1}[fmt]
-    ref_q, ref_w = oracle.q_rope_pack_fp8(wl.q[idx], wl.positions[idx], wl.cos_sin,
-                                          wl.weights[idx], scale_fmt=ofmt)
-    assert_same("q_out[sample]", got_q[idx], ref_q)
-    assert_same("weights_out[sample]", got_w[idx], ref_w)
+    ref_q, ref_w = oracle.q_rope_pack_fp8(wl.q, wl.positions, wl.cos_sin, wl.weights,
+                                          scale_fmt=ofmt, threads=ORACLE_THREADS)
+    assert_same("q_out", got_q, ref_q)
+    assert_same("weights_out", got_w, ref_w)
     assert not ((got_q & 0x7F) == 0x7F).any()       # no NaN codes anywhere
+    del got_q, ref_q
     kv, ks = gpu_k(wl.k, wl.positions, wl.cos_sin, wl.slot_mapping, wl.NB, scale_fmt=fmt)
     rkv = np.full((wl.NB, 64, 128), SENTINEL, np.uint8)
     rks = np.full((wl.NB, 64), np.nan, np.float32)

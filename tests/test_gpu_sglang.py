@@ -12,7 +12,7 @@ import pytest
 import oracle
 from pack_token_amd import workloads
 from pack_token_amd.workloads import SENTINEL
-from harness import assert_same, random_case, say
+from harness import ORACLE_THREADS, assert_same, large_prefill, random_case, say
 
 pytestmark = pytest.mark.gpu
 
@@ -179,17 +179,17 @@ def test_extreme_floors(floors):
     assert_same("q_packed", gpu_q(q, pos, cs, **kw), oracle.q_rope_pack_sglang(q, pos, cs, **kw))
 
 
-def test_large_prefill_sampled():
-    """T = 131072, H = 64: every key record, and the query records of 2,051
-    tokens (first, last and 2,049 random ones)."""
-    wl = workloads.large_prefill()
+def test_large_prefill_full_size():
+    """T = 131072, H = 64: every query record of every token and every key
+    record, byte for byte."""
+    wl = large_prefill()
     say(f"case sglang large_prefill: T={wl.T} H={wl.H}")
     got_q = gpu_q(wl.q, wl.positions, wl.cos_sin)
-    rng = np.random.default_rng(7)
-    idx = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 2049, replace=False)]))
-    ref_q = oracle.q_rope_pack_sglang(wl.q[idx], wl.positions[idx], wl.cos_sin)
-    assert_same("q_packed[sample]", got_q[idx], ref_q)
+    ref_q = oracle.q_rope_pack_sglang(wl.q, wl.positions, wl.cos_sin, threads=ORACLE_THREADS)
+    assert_same("q_packed", got_q, ref_q)
+    del ref_q
     assert (got_q[..., 64:] >= 1).all() and (got_q[..., 64:] <= 254).all()
+    del got_q
     slots = wl.slot_mapping + 1                 # slot 0 stays unpublished
     n = wl.NB * 64 + 1
     got_k = gpu_k(wl.k, wl.positions, wl.cos_sin, slots, n)

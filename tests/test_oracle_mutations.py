@@ -56,11 +56,6 @@ MUTATIONS = {
     "weights_head_0_skipped": ("for (int h = 0; h < H; ++h) weights_out[t * H + h] = weights[t * H + h];",
                                "for (int h = 1; h < H; ++h) weights_out[t * H + h] = weights[t * H + h];"),
     "no_saturation": ("else code = 7;", "else code = 6;"),
-    "scorer_without_relu": ("double score = (apply_relu && dot < 0.0) ? 0.0 : dot;",
-                            "double score = dot;"),
-    "scorer_mask_off_by_one": ("if (s > pos || blk < 0 || blk >= NB) {",
-                               "if (s >= pos || blk < 0 || blk >= NB) {"),
-    "scorer_ignores_weights": ("acc += w * score;", "acc += score;"),
     "two_stage_sign_on_zero": ("uint8_t sign = (yv < 0.0f && code != 0) ? 1 : 0;",
                                "uint8_t sign = signbit(yv) ? 1 : 0;"),
     "two_stage_reuses_stage_1_exponent": ("int e2 = group_exponent(y, GROUP, floor2);",
@@ -107,8 +102,31 @@ MUTATIONS = {
 }
 
 
+# Scorer mistakes, each of which the hand-derived worked cases alone must catch
+# (tests/golden/scorer_worked_cases.json: values derived by hand, not by
+# re-evaluating the oracle's formula).
+SCORER_PINS = ["tests/test_oracle_scorer.py::test_scorer_worked_cases"]
+SCORER_MUTATIONS = {
+    "scorer_without_relu": ("double score = (apply_relu && dot < 0.0) ? 0.0 : dot;",
+                            "double score = dot;"),
+    "scorer_mask_off_by_one": ("if (s > pos || blk < 0 || blk >= NB) {",
+                               "if (s >= pos || blk < 0 || blk >= NB) {"),
+    "scorer_invalid_block_read": ("if (s > pos || blk < 0 || blk >= NB) {",
+                                  "if (s > pos || blk >= NB) { if (blk < 0) blk = 0;"),
+    "scorer_ignores_weights": ("acc += w * score;", "acc += score;"),
+    "scorer_relu_after_weighting": ("acc += w * score;",
+                                    "acc += (apply_relu && w * dot < 0.0) ? 0.0 : w * dot;"),
+    "scorer_ignores_weights_scale": ("*out = (float)((double)weights_scale * acc);",
+                                     "*out = (float)(acc + 0.0 * weights_scale);"),
+    "scorer_linear_key_scales": ("(p % 16) * (KV_BLOCK / 16) + p / 16];", "p];"),
+    "scorer_query_scale_transposed": ("q_scale_out[t * (int64_t)NGROUPS * 16 * J + (g * 16 + h % 16) * J + h / 16];",
+                                      "q_scale_out[t * (int64_t)NGROUPS * 16 * J + (g * 16 + h / 16) * J + h % 16];"),
+}
+
+
 def _run_mutant(name, workdir):
-    old, new = MUTATIONS[name]
+    old, new = MUTATIONS[name] if name in MUTATIONS else SCORER_MUTATIONS[name]
+    pins = PINS if name in MUTATIONS else SCORER_PINS
     src = open(obuild.SRC).read()
     if src.count(old) != 1:
         return f"mutation site not unique or missing: {name}"
@@ -120,7 +138,7 @@ def _run_mutant(name, workdir):
     lib = obuild.build(src=mutant, out=os.path.join(d, "libmutant.so"))
     env = dict(os.environ, FP4IDX_ORACLE_LIB=lib, OMP_NUM_THREADS="1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "-m", "not gpu", *PINS], cwd=ROOT, env=env, capture_output=True, text=True,
+                        "-m", "not gpu", *pins], cwd=ROOT, env=env, capture_output=True, text=True,
                        timeout=900)
     return r.returncode
 
@@ -132,12 +150,13 @@ def mutant_results(tmp_path_factory):
     workdir = str(tmp_path_factory.mktemp("mutants"))
     workers = max(1, min(6, (os.cpu_count() or 2) - 1))
     with ThreadPoolExecutor(max_workers=workers) as ex:
-        futs = {n: ex.submit(_run_mutant, n, workdir) for n in sorted(MUTATIONS)}
+        futs = {n: ex.submit(_run_mutant, n, workdir)
+                for n in sorted(MUTATIONS) + sorted(SCORER_MUTATIONS)}
         return {n: f.result() for n, f in futs.items()}
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name", sorted(MUTATIONS))
+@pytest.mark.parametrize("name", sorted(MUTATIONS) + sorted(SCORER_MUTATIONS))
 def test_pins_catch_planted_mistake(name, mutant_results):
     rc = mutant_results[name]
     assert not isinstance(rc, str), rc

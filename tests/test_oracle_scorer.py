@@ -90,3 +90,80 @@ def test_scorer_masks_and_invalid_blocks():
     # ReLU makes every visible logit >= 0 with non-negative weights
     fin = np.isfinite(got)
     assert (got[fin] >= 0).all()
+
+
+# ---- worked cases with hand-derived logits -----------------------------------
+
+import json
+import os
+
+WORKED = os.path.join(os.path.dirname(__file__), "golden", "scorer_worked_cases.json")
+
+
+def worked_case_inputs(doc, case):
+    """The fixture's structured description turned into the scorer's byte
+    inputs: every 32-group holds one nibble value and one exponent."""
+    H, next_n = case["H"], case["next_n"]
+    B = len(case["context_lens"])
+    T = B * next_n
+    J = oracle.q_scale_cols(H)
+    q_out = np.zeros((T, H, 64), np.uint8)
+    q_scale = np.zeros((T, 1, 4, 16, J), np.uint8)
+    for t in range(T):
+        for h, groups in enumerate(doc["q_heads"][:H]):
+            for g, (n, e) in enumerate(groups):
+                q_out[t, h, 16 * g:16 * g + 16] = n | (n << 4)
+                q_scale[t, 0, g, h % 16, h // 16] = e
+    NB = case["NB"]
+    kv = np.zeros((NB, 1, 4, 64, 16), np.uint8)
+    ks = np.full((NB, 1, 4, 64), 140, np.uint8)
+    for blk, pos, name in case["keys_at"]:
+        for g, (n, e) in enumerate(doc["keys"][name]):
+            kv[blk, 0, g, pos, :] = n | (n << 4)
+            ks[blk, 0, g, (pos % 16) * 4 + pos // 16] = e
+    table = np.array(case["block_table"], np.int32)
+    ctx = np.array(case["context_lens"], np.int32)
+    w = np.array(case["weights"], np.float32)
+    return q_out, q_scale, w, kv, ks, table, ctx
+
+
+def worked_case_expected(case):
+    """[T, stride] float32: the listed logits, NaN (untouched) after them."""
+    rows = []
+    for row in case["expected"]:
+        vals = []
+        for item in row:
+            if isinstance(item, list):
+                v = {"-inf": -np.inf, "zeros": 0.0}[item[0]]
+                vals += [v] * item[1]
+            else:
+                vals.append(-np.inf if item == "-inf" else float(item))
+        rows.append(vals)
+    out = np.full((len(rows), case["stride"]), np.nan, np.float32)
+    for t, vals in enumerate(rows):
+        out[t, :len(vals)] = vals
+    return out
+
+
+def worked_cases():
+    with open(WORKED) as f:
+        doc = json.load(f)
+    return doc, doc["cases"]
+
+
+@pytest.mark.parametrize("idx", range(5))
+def test_scorer_worked_cases(idx):
+    """Hand-derived logits (tests/golden/scorer_worked_cases.json): the ReLU
+    before the weighting, the weights and weights_scale, per-head and
+    per-group scale bytes, the interleaved key scale row, the causal mask,
+    invalid block entries and untouched entries, each with exact values."""
+    doc, cases = worked_cases()
+    case = cases[idx]
+    q_out, q_scale, w, kv, ks, table, ctx = worked_case_inputs(doc, case)
+    got = oracle.paged_mqa_logits(q_out, q_scale, w, kv, ks, table, ctx, case["next_n"],
+                                  weights_scale=case["weights_scale"], apply_relu=case["relu"],
+                                  stride=case["stride"])
+    want = worked_case_expected(case)
+    assert np.array_equal(np.isnan(got), np.isnan(want)), case["name"]
+    fin = ~np.isnan(want)
+    assert np.array_equal(got[fin].view(np.uint32), want[fin].view(np.uint32)), case["name"]
