@@ -638,6 +638,80 @@ def bench_prefill_scoring(args, dev):
     print(json.dumps(rec), flush=True)
 
 
+def bench_ceiling(args, dev, kind: str):
+    """Ceiling measurements (fp4idx_ceiling_stream / fp4idx_ceiling_paged_gather):
+    plain HBM traffic of the shapes the kernels move, none of their arithmetic.
+      stream_read   reads the bytes the headline step reads (17,168 per token
+                    x 131,072 tokens at H = 64), writes nothing;
+      stream_mix    the headline step's reads and writes (17,168 + 4,676 bytes
+                    per token: 78.6% reads), writes spread over the reads;
+      stream_copy   a 1:1 copy of the fake-quant input (256 bytes x 64 heads x
+                    131,072 tokens read, as many written);
+      paged_gather  the decode-scoring batch's key blocks (4,096 + 256 bytes per
+                    block of every sequence) and its logit writes, with the
+                    scorer's flat split over wavefronts.
+    Rates are bytes moved / mean launch time (events around every launch)."""
+    import numpy as np
+    import torch
+
+    from pack_token_amd import fp4idx, workloads
+
+    stream = torch.cuda.current_stream(dev)
+    T, H = args.tokens, args.heads
+    if kind == "paged_gather":
+        B, next_n = 64, 4
+        sc = workloads.scorer_case(7, B, next_n, 32, 4096, 131072)
+        up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        kv, ks = up(sc.kv_cache), up(sc.kv_cache_scale)
+        table, ctx = up(sc.block_table), up(sc.context_lens)
+        logits = torch.empty((B * next_n, sc.max_blocks * 64), dtype=torch.float32, device=dev)
+
+        def call():
+            fp4idx.ceiling_paged_gather(kv, ks, table, ctx, next_n, logits)
+
+        keys = int(sc.context_lens.astype(np.int64).sum())
+        blocks = int(sum(-(-int(c) // 64) for c in sc.context_lens))
+        read_b = blocks * (4096 + 256) + blocks * 4 + B * 4
+        write_b = keys * next_n * 4
+        shape = {"sequences": B, "next_n": next_n, "keys": keys, "blocks": blocks,
+                 "context": "U[4096,131072]"}
+    else:
+        J = ((H // 16) + 3) // 4 * 4
+        if kind == "stream_copy":
+            read_b = write_b = 256 * H * T
+        else:
+            read_b = (256 * H + 4 * H + 8 + 256 + 256 + 8) * T
+            write_b = 0 if kind == "stream_read" else (64 * H + 64 * J + 4 * H + 68) * T
+        read_b, write_b = -(-read_b // 1024) * 1024, -(-write_b // 1024) * 1024
+        src = torch.zeros(read_b, dtype=torch.uint8, device=dev)
+        dst = torch.zeros(max(write_b, 1024), dtype=torch.uint8, device=dev)
+
+        def call():
+            fp4idx.ceiling_stream(src, read_b, dst, write_b)
+
+        shape = {"tokens": T, "heads": H, "read_bytes": read_b, "write_bytes": write_b,
+                 "read_fraction": read_b / (read_b + write_b)}
+    K = args.steps
+    legs = time_legs({"step": [call]}, K, args.warmup, args.rounds, stream,
+                     settle_ms=args.settle_ms)
+    (launch_ms,), (launch_med,) = launch_pass([call], K, stream)
+    total = read_b + write_b
+    gbs = total / (launch_ms * 1e-3) / 1e9
+    rec = {
+        "metric": "HBM GB/s of plain traffic (ceiling measurement, no arithmetic)",
+        "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": median(legs["step"]), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": dict({"workload": kind}, **shape),
+        "roofline": {"kernel": "gather_kernel" if kind == "paged_gather" else "stream_kernel",
+                     "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": total, "launch_us": launch_ms * 1e3,
+                     "launch_us_median": launch_med * 1e3},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -646,7 +720,8 @@ def main():
     ap.add_argument("--workload", default="large_prefill",
                     choices=["large_prefill", "prefill_norm_rotate", "decode", "decode_scoring",
                              "prefill_scoring", "sglang_prefill", "fp8_prefill",
-                             "fake_quant_prefill"],
+                             "fake_quant_prefill", "stream_read", "stream_mix", "stream_copy",
+                             "paged_gather"],
                     help="large_prefill is the headline configuration; the other two are timed "
                          "for reference")
     ap.add_argument("--tokens", type=int, default=131072,
@@ -716,6 +791,9 @@ def main():
         return
     if args.workload == "fake_quant_prefill":
         bench_fake_quant(args, dev)
+        return
+    if args.workload in ("stream_read", "stream_mix", "stream_copy", "paged_gather"):
+        bench_ceiling(args, dev, args.workload)
         return
     if args.workload == "large_prefill":
         wl = workloads.large_prefill(T=args.tokens, H=args.heads)

@@ -1,0 +1,50 @@
+/*
+ * fp4idx_ceiling.h -- measurement entry points of libfp4idx: plain HBM
+ * traffic of the shapes the producer and the scorer move, with none of the
+ * method's arithmetic, so their measured rates can be set against what the
+ * same traffic reaches on this GPU.  Not part of the method; used by the
+ * benchmark.  Conventions as in fp4idx.h: device pointers, `stream` a
+ * hipStream_t as void* (NULL = default stream), nothing allocated, no
+ * synchronization.  Returns 0 on success, 1 for an invalid argument (nothing
+ * enqueued), 3 for a HIP error.
+ */
+#ifndef FP4IDX_CEILING_H
+#define FP4IDX_CEILING_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * Reads read_bytes from src and writes write_bytes to dst (both multiples of
+ * 1,024, both buffers 16-byte aligned) in 1 KB units, one unit per wavefront
+ * step, the write units spread evenly over the read units while write_bytes
+ * <= read_bytes: write_bytes = 0 is a read-only stream, equal sizes a copy.
+ * dst receives data derived from src (its contents are of no use) and must
+ * hold at least 1,024 bytes even for a read-only stream.  Each size is at most
+ * 2^40 bytes.  One persistent grid of 16-byte accesses.
+ */
+int fp4idx_ceiling_stream(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes,
+                          void* stream);
+
+/*
+ * The access pattern of fp4idx_paged_mqa_logits in decode: for every key block
+ * of every sequence (block_table [B, max_blocks] int32, context_lens [B] int32,
+ * clamped as the scorer clamps them), reads the block's 4,096 code bytes of
+ * kv_cache [NB,1,4,64,16] and its 256-byte row of kv_cache_scale [NB,1,4,64],
+ * and writes next_n fp32 values per key into logits [B*next_n, stride] (values
+ * of no use), with the scorer's flat, balanced split of the blocks over
+ * wavefronts.  B <= 1024, next_n <= 64, B * max_blocks < 2^31.
+ */
+int fp4idx_ceiling_paged_gather(const uint8_t* kv_cache, const uint8_t* kv_cache_scale, int64_t NB,
+                                const int32_t* block_table, int64_t max_blocks,
+                                const int32_t* context_lens, int64_t B, int next_n, float* logits,
+                                int64_t stride, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4IDX_CEILING_H */

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp4idx.so")
 SOURCES = [os.path.join(CSRC, "fp4idx_kernels.hip"), os.path.join(CSRC, "fp4idx_modes.hip"),
-           os.path.join(CSRC, "fp4idx_scorer.hip"),
+           os.path.join(CSRC, "fp4idx_scorer.hip"), os.path.join(CSRC, "fp4idx_ceiling.hip"),
            os.path.join(CSRC, "fp4idx_api.cpp")]
 ARCH = os.environ.get("FP4IDX_OFFLOAD_ARCH", "gfx950")
 

@@ -1,0 +1,241 @@
+// fp4idx_ceiling.hip -- measurement kernels: the HBM rate that plain traffic of
+// a given shape reaches on this GPU, with none of the method's arithmetic.
+// They set the ceilings the producer and scorer kernels are compared with:
+//   - a stream that reads R bytes and writes W bytes, the writes spread evenly
+//     over the reads (read-only: W = 0; the producer's 79:21 mix; a 1:1 copy);
+//   - a gather of whole paged-cache blocks (4,096 code bytes and the 256-byte
+//     scale row of each block named by a block table) with the scorer's flat,
+//     balanced decomposition, writing next_n fp32 values per key as the scorer
+//     writes its logits.
+// Every load feeds a store, so no access is dead code.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp4idx_ceiling.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4_t ld_nt(const u32x4_t* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void st_nt(u32x4_t* p, u32x4_t v) { __builtin_nontemporal_store(v, p); }
+
+// The stream works in units of 1 KB (64 lanes x 16 bytes).  A wavefront takes
+// read units u = w, w + W, ... (W wavefronts in the grid) and, whenever the
+// running write count (u + 1) * ratio crosses an integer, writes the next
+// 1 KB write unit with data it has just read, so writes follow reads evenly at
+// the ratio nw:nr (ratio = nw / nr in 32.32 fixed point, nw <= nr).  Units
+// past the mixed part are written by a write-only loop.  A read-only stream
+// folds its data into one value per lane and stores it only if every bit of it
+// is set, which zero-filled buffers never produce.
+__global__ __launch_bounds__(kThreads) void stream_kernel(const u32x4_t* __restrict__ src,
+                                                          u32x4_t* __restrict__ dst, int64_t nr,
+                                                          uint64_t ratio, int64_t nw_mixed,
+                                                          int64_t nw) {
+    const int lane = threadIdx.x & 63;
+    const int64_t W = (int64_t)gridDim.x * (kThreads / 64);
+    const int64_t w = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    u32x4_t acc = {0u, 0u, 0u, 0u};
+    for (int64_t u = w; u < nr; u += W) {
+        const u32x4_t v = ld_nt(src + u * 64 + lane);
+        acc ^= v;
+        const int64_t k0 = (int64_t)(((uint64_t)u * ratio) >> 32);
+        const int64_t k1 = (int64_t)(((uint64_t)(u + 1) * ratio) >> 32);
+        if (k1 > k0 && k0 < nw_mixed) st_nt(dst + k0 * 64 + lane, v);
+    }
+    for (int64_t k = nw_mixed + w; k < nw; k += W) st_nt(dst + k * 64 + lane, acc);
+    if (acc.x == 0xFFFFFFFFu && acc.y == 0xFFFFFFFFu && acc.z == 0xFFFFFFFFu &&
+        acc.w == 0xFFFFFFFFu)
+        dst[lane] = acc;
+}
+
+// ---- paged gather with the decode scorer's decomposition --------------------
+// Quads of blocks (4q .. 4q+3 of one sequence) in one flat list, equal
+// contiguous ranges per wavefront, as the decode scorer takes them.  A
+// wavefront keeps four blocks in flight (a ring of four register sets, the
+// block three ahead loaded while the current one is folded) and writes each
+// quad's next_n logit rows as 1 KB stores, lane 16 r + m covering keys
+// 4 m .. 4 m + 3 of the quad's block r.
+constexpr int kGatherMaxB = 1024;
+constexpr int kWaves = kThreads / 64;
+
+struct GatherArgs {
+    const uint8_t* kv_cache;
+    const uint8_t* kv_cache_scale;
+    const int32_t* block_table;
+    const int32_t* context_lens;
+    float* logits;
+    int64_t nblocks;
+    int64_t max_blocks;
+    int64_t B;
+    int64_t stride;
+    int next_n;
+    int vec4;
+};
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+struct Blk {
+    u32x4_t v[4];
+    uint32_t s;
+};
+
+__device__ __forceinline__ void load_blk(const GatherArgs& a, int blki, int j, int cnt, int lane,
+                                         Blk& q) {
+    const int32_t blk = j < cnt ? __builtin_amdgcn_readlane(blki, j) : -1;
+    if (blk >= 0 && (int64_t)blk < a.nblocks) {
+        const uint8_t* base = a.kv_cache + (int64_t)blk * 4096 + 16 * lane;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q.v[i] = ld_nt(reinterpret_cast<const u32x4_t*>(base + 1024 * i));
+        q.s = *reinterpret_cast<const uint32_t*>(a.kv_cache_scale + (int64_t)blk * 256 + 4 * lane);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q.v[i] = (u32x4_t){0u, 0u, 0u, 0u};
+        q.s = 0u;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs a) {
+    extern __shared__ int32_t prefix[];  // [B] inclusive quad counts
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int B = (int)a.B;
+    const int64_t cap = a.max_blocks * 64 < a.stride ? a.max_blocks * 64 : a.stride;
+    if (wave == 0) {
+        int carry = 0;
+        for (int base = 0; base < B; base += 64) {
+            int v = 0;
+            if (base + lane < B) {
+                int64_t c = a.context_lens[base + lane];
+                c = c < 0 ? 0 : (c > cap ? cap : c);
+                v = (int)((c + 255) >> 8);
+            }
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int u = __shfl_up(v, d, 64);
+                if (lane >= d) v += u;
+            }
+            if (base + lane < B) prefix[base + lane] = carry + v;
+            carry += __shfl(v, 63, 64);
+        }
+    }
+    __syncthreads();
+    const int64_t nquads = prefix[B - 1];
+    const int64_t W = (int64_t)gridDim.x * kWaves;
+    const int64_t w = (int64_t)blockIdx.x * kWaves + wave;
+    const int64_t lo = w * nquads / W, hi = (w + 1) * nquads / W;
+    const int g = lane >> 4, n = lane & 15;
+    int cur_b = -1;
+    int64_t ctx = 0;
+    for (int64_t win = lo; win < hi; win += 16) {
+        const int nq_win = (int)(hi - win < 16 ? hi - win : 16);
+        const int cnt = 4 * nq_win;
+        int bi = 0, kbi = 0, blki = -1;
+        if (lane < cnt) {
+            const int qf = (int)(win + (lane >> 2));
+            int l = 0, r = B;
+            while (l < r) {
+                const int m = (l + r) >> 1;
+                if (prefix[m] > qf) r = m; else l = m + 1;
+            }
+            bi = l;
+            kbi = 4 * (qf - (l ? prefix[l - 1] : 0)) + (lane & 3);
+            int64_t c = a.context_lens[l];
+            c = c < 0 ? 0 : (c > cap ? cap : c);
+            if ((int64_t)kbi * 64 < c) blki = a.block_table[(int64_t)bi * a.max_blocks + kbi];
+        }
+        Blk ring[4];
+        load_blk(a, blki, 0, cnt, lane, ring[0]);
+        load_blk(a, blki, 1, cnt, lane, ring[1]);
+        load_blk(a, blki, 2, cnt, lane, ring[2]);
+        for (int qi = 0; qi < nq_win; ++qi) {
+            const int b = __builtin_amdgcn_readlane(bi, 4 * qi);
+            const int64_t kb0 = __builtin_amdgcn_readlane(kbi, 4 * qi);
+            if (b != cur_b) {
+                cur_b = b;
+                int64_t c = a.context_lens[b];
+                ctx = c < 0 ? 0 : (c > cap ? cap : c);
+            }
+            uint32_t u = 0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                load_blk(a, blki, 4 * qi + r + 3, cnt, lane, ring[(r + 3) & 3]);
+                const u32x4_t x = ring[r].v[0] ^ ring[r].v[1] ^ ring[r].v[2] ^ ring[r].v[3];
+                if (g == r) u = (x.x ^ x.y ^ x.z ^ x.w ^ ring[r].s) & 0x3FFFFFFFu;
+            }
+            const f32x4_t o = {__uint_as_float(u), __uint_as_float(u ^ 1u), __uint_as_float(u ^ 2u),
+                               __uint_as_float(u ^ 3u)};
+            const int64_t s0 = (kb0 + g) * 64 + 4 * n;
+            for (int jj = 0; jj < a.next_n; ++jj) {
+                float* row = a.logits + ((int64_t)b * a.next_n + jj) * a.stride;
+                if (a.vec4 && s0 + 4 <= ctx) {
+                    __builtin_nontemporal_store(o, reinterpret_cast<f32x4_t*>(row + s0));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (s0 + i < ctx) __builtin_nontemporal_store(o[i], row + s0 + i);
+                }
+            }
+        }
+    }
+}
+
+int device_wgs(const void* fn, size_t lds, int* wgs) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 3;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 3;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, lds) != hipSuccess)
+        return 3;
+    *wgs = cus * (per_cu > 0 ? per_cu : 1);
+    return 0;
+}
+
+}  // namespace
+
+extern "C" int fp4idx_ceiling_stream(const void* src, int64_t read_bytes, void* dst,
+                                     int64_t write_bytes, void* stream) {
+    if (read_bytes < 0 || write_bytes < 0 || read_bytes % 1024 || write_bytes % 1024) return 1;
+    if ((read_bytes && !src) || !dst) return 1;
+    if (((uintptr_t)src | (uintptr_t)dst) & 15) return 1;
+    if (read_bytes > ((int64_t)1 << 40) || write_bytes > ((int64_t)1 << 40)) return 1;
+    int64_t nr = read_bytes / 1024, nw = write_bytes / 1024;  // 1 KB units
+    if (nr == 0 && nw == 0) return 0;
+    // writes up to the read count are spread over the reads, the rest follow
+    int64_t nw_mixed = nw < nr ? nw : nr;
+    uint64_t ratio = nr ? (uint64_t)(((unsigned __int128)nw_mixed << 32) / (uint64_t)nr) : 0;
+    // (u + 1) * ratio >> 32 may fall short of nw_mixed by rounding: the
+    // write-only loop covers from the last unit the mixed part reaches
+    nw_mixed = nr ? (int64_t)(((unsigned __int128)nr * ratio) >> 32) : 0;
+    int wgs = 0;
+    if (device_wgs(reinterpret_cast<const void*>(stream_kernel), 0, &wgs)) return 3;
+    const u32x4_t* s = static_cast<const u32x4_t*>(src);
+    u32x4_t* d = static_cast<u32x4_t*>(dst);
+    void* args[] = {&s, &d, &nr, &ratio, &nw_mixed, &nw};
+    return hipLaunchKernel(reinterpret_cast<const void*>(stream_kernel), dim3(wgs), dim3(kThreads),
+                           args, 0, static_cast<hipStream_t>(stream)) == hipSuccess ? 0 : 3;
+}
+
+extern "C" int fp4idx_ceiling_paged_gather(const uint8_t* kv_cache, const uint8_t* kv_cache_scale,
+                                           int64_t NB, const int32_t* block_table,
+                                           int64_t max_blocks, const int32_t* context_lens,
+                                           int64_t B, int next_n, float* logits, int64_t stride,
+                                           void* stream) {
+    if (B < 1 || B > kGatherMaxB || max_blocks < 1 || NB < 0 || stride < 1 || next_n < 1 ||
+        next_n > 64 || B * max_blocks >= ((int64_t)1 << 31))
+        return 1;
+    if (!kv_cache || !kv_cache_scale || !block_table || !context_lens || !logits) return 1;
+    if (((uintptr_t)kv_cache & 15) || ((uintptr_t)kv_cache_scale & 3)) return 1;
+    GatherArgs a{kv_cache, kv_cache_scale, block_table, context_lens, logits, NB, max_blocks, B,
+                 stride, next_n, ((uintptr_t)logits % 16 == 0) && (stride % 4 == 0)};
+    const size_t lds = (size_t)B * sizeof(int32_t);
+    int wgs = 0;
+    if (device_wgs(reinterpret_cast<const void*>(gather_kernel), lds, &wgs)) return 3;
+    const int64_t most = (B * ((max_blocks + 3) / 4) + kWaves - 1) / kWaves;
+    if (wgs > most) wgs = (int)most;
+    void* args[] = {&a};
+    return hipLaunchKernel(reinterpret_cast<const void*>(gather_kernel), dim3(wgs), dim3(kThreads),
+                           args, lds, static_cast<hipStream_t>(stream)) == hipSuccess ? 0 : 3;
+}

@@ -160,6 +160,7 @@ struct LArgs {
     int H;
     int J;
     int apply_relu;
+    int logits_vec4;              // set by the launcher: logits rows allow 16-byte stores
 };
 
 hipError_t launch_q_rope_pack(const QArgs& a, bool is_neox, bool hadamard, hipStream_t stream);

@@ -305,6 +305,244 @@ __global__ __launch_bounds__(64 * kWaves) void mqa_logits_kernel(LArgs a) {
     }
 }
 
+// ---- decode over a flat, balanced list of block quads ----------------------------
+// Decode (next_n <= 4) with B <= kFlatMaxB sequences.  A sequence's key blocks
+// are taken in quads (blocks 4q .. 4q+3, the last quad of a sequence possibly
+// short); the quads of all sequences form one flat list and every wavefront of
+// the grid takes an equal contiguous range of it, so no wavefront idles on a
+// short sequence and none exits without work.  Each workgroup first builds the
+// inclusive prefix of the per-sequence quad counts in LDS; a wavefront maps the
+// blocks of a window of 16 quads to (sequence, block index) by binary search
+// with one lane per block, reads their block-table entries with one load per
+// lane, and walks them with the blocks fetched two ahead into a ring of three
+// LDS buffers.  The query operands of a sequence are loaded when the walk
+// enters it.
+//
+// Key order inside a block: matrix-core tile kt takes keys 4n + kt (n = lane %
+// 16), so after the cross-row reduce lane 16r + m holds key 4m + r.  Four such
+// results (the quad's blocks) go through a 4 x 4 exchange of 16-lane rows
+// across registers, after which lane 16r' + m' holds keys 4m' .. 4m' + 3 of
+// block r' of the quad: each query token's logits of the quad (1 KB) leave in
+// one 16-byte-per-lane store.  The scale byte of key 4n + kt in its group row
+// (interleaved order (p % 16) * 4 + p / 16) is byte n / 4 of dword
+// 4 (n % 4) + kt, so a lane reads the 16 bytes at 16 (n % 4) and picks byte
+// n / 4 of each dword with byte permutes.
+constexpr int kFlatMaxB = 1024;
+constexpr int kRing = 3;
+
+__device__ __forceinline__ void wait_prefetch(int n_after) {
+    // n_after blocks (5 loads each) were fetched after the block that is needed:
+    // once at most their loads are in flight, that block and everything issued
+    // before it has landed (vector memory operations complete in issue order),
+    // whatever else was issued in between
+    if (n_after >= 2)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(10));
+    else if (n_after == 1)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(5));
+    else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(0));
+}
+
+// The lane's four code pieces (keys 4n + kt, group g) and the scale dword whose
+// byte kt belongs to key 4n + kt.
+__device__ __forceinline__ void read_block_strided(const uint8_t* kl, const uint32_t* sl, int lane,
+                                                   uint32_t sel, u32x4_t v[4], int& sb) {
+    const uint32_t ka = (uint32_t)(uintptr_t)(lds_ptr_t)kl + 1024 * (lane >> 4) + 64 * (lane & 15);
+    const uint32_t sa = (uint32_t)(uintptr_t)(lds_ptr_t)sl + 64 * (lane >> 4) + 16 * (lane & 3);
+    u32x4_t d;
+    asm volatile(
+        "ds_read_b128 %0, %5\n\t"
+        "ds_read_b128 %1, %5 offset:16\n\t"
+        "ds_read_b128 %2, %5 offset:32\n\t"
+        "ds_read_b128 %3, %5 offset:48\n\t"
+        "ds_read_b128 %4, %6\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(d)
+        : "v"(ka), "v"(sa)
+        : "memory");
+    const uint32_t x01 = __builtin_amdgcn_perm(d[1], d[0], sel);
+    const uint32_t x23 = __builtin_amdgcn_perm(d[3], d[2], sel);
+    sb = (int)__builtin_amdgcn_perm(x23, x01, 0x05040100u);
+}
+
+// rows (16 lanes) r of E[b] -> row b of T[r]: T[i] lane 16 r' + m' = E[r'] lane 16 i + m'
+__device__ __forceinline__ void exchange4x4(const float E[4], float T[4]) {
+    const auto p02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(E[0]), __float_as_uint(E[2]),
+                                                      false, false);
+    const auto p13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(E[1]), __float_as_uint(E[3]),
+                                                      false, false);
+    const auto q01 = __builtin_amdgcn_permlane16_swap(p02[0], p13[0], false, false);
+    const auto q23 = __builtin_amdgcn_permlane16_swap(p02[1], p13[1], false, false);
+    T[0] = __uint_as_float(q01[0]);
+    T[1] = __uint_as_float(q01[1]);
+    T[2] = __uint_as_float(q23[0]);
+    T[3] = __uint_as_float(q23[1]);
+}
+
+template <int NQ, int HT, bool RELU>
+__global__ __launch_bounds__(64 * kWaves, HT <= 2 ? 3 : 2) void mqa_logits_flat_kernel(LArgs a) {
+    extern __shared__ int32_t prefix[];  // [B] inclusive quad counts
+    __shared__ __attribute__((aligned(16))) uint8_t kbuf[kRing][kWaves][kBlockBytes];
+    __shared__ __attribute__((aligned(16))) uint32_t sbuf[kRing][kWaves][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int B = (int)a.B;
+    const int64_t ctx_cap = a.max_blocks * 64 < a.stride ? a.max_blocks * 64 : a.stride;
+    if (wave == 0) {
+        int carry = 0;
+        for (int base = 0; base < B; base += 64) {
+            int v = 0;
+            if (base + lane < B) {
+                int64_t c = a.context_lens[base + lane];
+                c = c < 0 ? 0 : (c > ctx_cap ? ctx_cap : c);
+                v = (int)((c + 255) >> 8);
+            }
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int u = __shfl_up(v, d, 64);
+                if (lane >= d) v += u;
+            }
+            if (base + lane < B) prefix[base + lane] = carry + v;
+            carry += __shfl(v, 63, 64);
+        }
+    }
+    __syncthreads();
+    const int64_t nquads = prefix[B - 1];
+    const int64_t W = (int64_t)gridDim.x * kWaves;
+    const int64_t w = (int64_t)blockIdx.x * kWaves + wave;
+    const int64_t lo = w * nquads / W;
+    const int64_t hi = (w + 1) * nquads / W;
+    if (lo >= hi) return;
+
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    const int H = HT * 16;
+    const int J = a.J;
+    // byte n/4 of two dwords: selector bytes (n/4, 4 + n/4, zero, zero)
+    const uint32_t sel = (uint32_t)(n >> 2) | ((uint32_t)(4 + (n >> 2)) << 8) | 0x0C0C0000u;
+    // key of this lane's reduced result inside a block, and of its stored values
+    const int key_red = 4 * n + g;
+    i32x8_t A[NQ][HT];
+    int SA[NQ][(HT + 3) / 4];
+    float4 W4[NQ][HT];
+    int cur_b = -1;
+    int64_t ctx = 0;
+    float E[NQ][4];  // the quad's reduced results per query token, block by block
+
+    for (int64_t win = lo; win < hi; win += 16) {
+        const int nq_win = (int)(hi - win < 16 ? hi - win : 16);
+        const int cnt = 4 * nq_win;  // block slots of the window, 4 per quad
+        // lane i: block i % 4 of quad win + i / 4 -> sequence, block index, entry
+        int bi = 0, kbi = 0, blki = -1, live = 0;
+        if (lane < cnt) {
+            const int qf = (int)(win + (lane >> 2));
+            int l = 0, r = B;  // first sequence whose inclusive quad count exceeds qf
+            while (l < r) {
+                const int m = (l + r) >> 1;
+                if (prefix[m] > qf) r = m; else l = m + 1;
+            }
+            bi = l;
+            kbi = 4 * (qf - (l ? prefix[l - 1] : 0)) + (lane & 3);
+            int64_t c = a.context_lens[l];
+            c = c < 0 ? 0 : (c > ctx_cap ? ctx_cap : c);
+            live = (int64_t)kbi * 64 < c;  // the quad's last blocks may lie past the context
+            if (live) blki = a.block_table[(int64_t)bi * a.max_blocks + kbi];
+        }
+        // the previous window's blocks were all consumed; the table entries land
+        __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(0));
+        auto fetched = [&](int j) {
+            if (j >= cnt) return false;
+            const int32_t blk = __builtin_amdgcn_readlane(blki, j);
+            return blk >= 0 && (int64_t)blk < a.nblocks;
+        };
+        auto fetch = [&](int j) {
+            const int32_t blk = __builtin_amdgcn_readlane(blki, j);
+            fetch_block(a, blk, lane, kbuf[j % kRing][wave], sbuf[j % kRing][wave]);
+        };
+        bool f1 = fetched(0), f2 = fetched(1);
+        if (f1) fetch(0);
+        if (f2) fetch(1);
+        int b = 0;
+        int64_t kb = 0;
+        for (int qi = 0; qi < nq_win; ++qi) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = 4 * qi + r;
+                const bool f0 = f1;  // block slot j was fetched
+                f1 = f2;
+                f2 = fetched(j + 2);
+                if (f2) fetch(j + 2);  // into the ring slot block j - 1 left
+                b = __builtin_amdgcn_readlane(bi, j);
+                kb = __builtin_amdgcn_readlane(kbi, j);
+                if (__builtin_amdgcn_readlane(live, j) == 0) continue;  // past the context
+                wait_prefetch((int)f1 + (int)f2);
+                if (b != cur_b) {  // entering a sequence: its query operands
+                    cur_b = b;
+                    int64_t c = a.context_lens[b];
+                    ctx = c < 0 ? 0 : (c > ctx_cap ? ctx_cap : c);
+                    const int64_t t0 = (int64_t)b * NQ;
+#pragma unroll
+                    for (int jj = 0; jj < NQ; ++jj) {
+                        const int64_t t = t0 + jj;
+#pragma unroll
+                        for (int ht = 0; ht < HT; ++ht) {
+                            A[jj][ht] = as_operand(*reinterpret_cast<const u32x4_t*>(
+                                a.q_out + ((t * H + 16 * ht + n) * 64 + 16 * g)));
+                            W4[jj][ht] = *reinterpret_cast<const float4*>(
+                                a.weights + t * H + 16 * ht + 4 * g);
+                        }
+#pragma unroll
+                        for (int d = 0; d < (HT + 3) / 4; ++d)
+                            SA[jj][d] = *reinterpret_cast<const int*>(
+                                a.q_scale_out + t * 64 * (int64_t)J + (g * 16 + n) * J + 4 * d);
+                    }
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(0));
+                }
+                i32x8_t Bk[4];
+                int sb = 0;
+                if (f0) {
+                    u32x4_t v[4];
+                    read_block_strided(kbuf[j % kRing][wave], sbuf[j % kRing][wave], lane, sel, v,
+                                       sb);
+#pragma unroll
+                    for (int kt = 0; kt < 4; ++kt) Bk[kt] = as_operand(v[kt]);
+                } else {
+#pragma unroll
+                    for (int kt = 0; kt < 4; ++kt) Bk[kt] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+                }
+                const int64_t s = kb * 64 + key_red;
+#pragma unroll
+                for (int jj = 0; jj < NQ; ++jj) {
+                    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+                    HeadLoop<HT, 0, RELU>::run(A[jj], SA[jj], W4[jj], Bk, sb, acc);
+                    const float v = transpose_reduce(acc);
+                    const int64_t pos = ctx - NQ + jj;
+                    E[jj][r] = (!f0 || s > pos) ? -__builtin_huge_valf() : a.weights_scale * v;
+                }
+            }
+            // The quad's logits leave: lane 16 r' + m' holds keys 4 m' .. 4 m' + 3 of
+            // block r'.  The quad's first block always lies inside the context, so b
+            // and ctx are the quad's sequence; blocks past the context (their E
+            // entries are stale) have every key >= ctx and store nothing.
+            const int64_t s0 = (kb - 3 + g) * 64 + 4 * n;
+#pragma unroll
+            for (int jj = 0; jj < NQ; ++jj) {
+                float T[4];
+                exchange4x4(E[jj], T);
+                float* row = a.logits + ((int64_t)b * NQ + jj) * a.stride;
+                if (a.logits_vec4 && s0 + 4 <= ctx) {
+                    const f32x4_t q4 = {T[0], T[1], T[2], T[3]};
+                    __builtin_nontemporal_store(q4, reinterpret_cast<f32x4_t*>(row + s0));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (s0 + i < ctx) __builtin_nontemporal_store(T[i], row + s0 + i);
+                }
+            }
+        }
+    }
+}
+
 template <int NQ, int HT, bool RELU>
 const void* kernel_for(bool tiled) {
     if constexpr (NQ == 2 || NQ == 4)
@@ -327,8 +565,42 @@ hipError_t launch_nq_ht(const LArgs& a, hipStream_t stream) {
     return hipLaunchKernel(fn, grid, dim3(64 * kWaves), args, 0, stream);
 }
 
+// Workgroups the flat decode grid keeps resident: compute units x the
+// kernel's occupancy (looked up once per device and kernel).
+template <int NQ, int HT>
+hipError_t launch_flat(const LArgs& a, hipStream_t stream) {
+    const void* fn = a.apply_relu
+                         ? reinterpret_cast<const void*>(mqa_logits_flat_kernel<NQ, HT, true>)
+                         : reinterpret_cast<const void*>(mqa_logits_flat_kernel<NQ, HT, false>);
+    const size_t lds = (size_t)a.B * sizeof(int32_t);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    int cus = 0, per_cu = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * kWaves, lds);
+    if (e != hipSuccess) return e;
+    // no more wavefronts than quads to score (bounded by B x max_blocks / 4)
+    const int64_t most = (a.B * ((a.max_blocks + 3) / 4) + kWaves - 1) / kWaves;
+    int64_t wgs = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+    wgs = wgs < most ? wgs : most;
+    LArgs copy = a;
+    copy.logits_vec4 = ((uintptr_t)a.logits % 16 == 0) && (a.stride % 4 == 0);
+    void* args[] = {&copy};
+    return hipLaunchKernel(fn, dim3((unsigned)wgs), dim3(64 * kWaves), args, lds, stream);
+}
+
 template <int NQ>
 hipError_t launch_nq(const LArgs& a, hipStream_t stream) {
+    if (a.next_n <= 4 && a.B <= kFlatMaxB && a.B * a.max_blocks < ((int64_t)1 << 31)) {
+        switch (a.H / 16) {
+            case 1: return launch_flat<NQ, 1>(a, stream);
+            case 2: return launch_flat<NQ, 2>(a, stream);
+            case 3: return launch_flat<NQ, 3>(a, stream);
+            default: return launch_flat<NQ, 4>(a, stream);
+        }
+    }
     switch (a.H / 16) {
         case 1: return launch_nq_ht<NQ, 1>(a, stream);
         case 2: return launch_nq_ht<NQ, 2>(a, stream);

@@ -80,6 +80,11 @@ def lib():
             L.fp4idx_paged_mqa_logits.restype = _i
             L.fp4idx_dequant_debug.argtypes = [_i, _p, _p, _i64, _i, _p, _i64, _i, _p, _p]
             L.fp4idx_dequant_debug.restype = _i
+            L.fp4idx_ceiling_stream.argtypes = [_p, _i64, _p, _i64, _p]
+            L.fp4idx_ceiling_stream.restype = _i
+            L.fp4idx_ceiling_paged_gather.argtypes = [_p, _p, _i64, _p, _i64, _p, _i64, _i, _p,
+                                                      _i64, _p]
+            L.fp4idx_ceiling_paged_gather.restype = _i
             L.fp4idx_last_error.argtypes = []
             L.fp4idx_last_error.restype = ctypes.c_char_p
             _lib = L
@@ -506,3 +511,37 @@ def dequant_kcache(kv_cache, kv_cache_scale, slots=None, *, out=None, stream=Non
     _check(lib().fp4idx_dequant_debug(1, _ptr(kv_cache), _ptr(kv_cache_scale), rows, 0,
                                       _ptr(slots), NB, KV_BLOCK, _ptr(out), _stream_handle(stream)))
     return out
+
+
+# ---- measurement entry points (include/fp4idx_ceiling.h) ---------------------
+
+def ceiling_stream(src, read_bytes: int, dst, write_bytes: int, *, stream=None):
+    """Plain stream: read read_bytes of src, write write_bytes of dst (writes
+    spread over the reads).  A measurement of the HBM rate of that traffic."""
+    for t, name, n in ((src, "src", read_bytes), (dst, "dst", max(write_bytes, 1024))):
+        _require(t, name, (torch.uint8,))
+        if t.numel() < n:
+            raise ValueError(f"{name} holds {t.numel()} bytes, needs {n}")
+    rc = lib().fp4idx_ceiling_stream(_ptr(src), read_bytes, _ptr(dst), write_bytes,
+                                     _stream_handle(stream))
+    if rc != OK:
+        raise Fp4IdxError(rc, "fp4idx_ceiling_stream failed")
+
+
+def ceiling_paged_gather(kv_cache, kv_cache_scale, block_table, context_lens, next_n, logits, *,
+                         stream=None):
+    """The decode scorer's reads and writes without its arithmetic."""
+    _check_fp4_cache(kv_cache, kv_cache_scale)
+    _require(block_table, "block_table", (torch.int32,))
+    _require(context_lens, "context_lens", (torch.int32,))
+    _require(logits, "logits", (torch.float32,))
+    B, max_blocks = block_table.shape
+    _numel(context_lens, "context_lens", B)
+    if logits.dim() != 2 or logits.shape[0] != B * next_n:
+        raise ValueError("logits must be [B * next_n, stride]")
+    rc = lib().fp4idx_ceiling_paged_gather(_ptr(kv_cache), _ptr(kv_cache_scale), kv_cache.shape[0],
+                                           _ptr(block_table), max_blocks, _ptr(context_lens), B,
+                                           next_n, _ptr(logits), logits.shape[1],
+                                           _stream_handle(stream))
+    if rc != OK:
+        raise Fp4IdxError(rc, "fp4idx_ceiling_paged_gather failed")

@@ -18,9 +18,29 @@ ALIGNED = 1 << 20       # a fake, well-aligned non-null address; never dereferen
 MISALIGNED = ALIGNED + 2
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     return sorted(set(re.findall(r"^(?:int|const char\*)\s+(fp4idx_\w+)\(", text, re.M)))
+
+
+def test_exports_every_measurement_symbol():
+    names = declared_functions(os.path.join(ROOT, "include", "fp4idx_ceiling.h"))
+    assert names == ["fp4idx_ceiling_paged_gather", "fp4idx_ceiling_stream"]
+    lib = ctypes.CDLL(fp4idx.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_measurement_entry_points_reject_bad_arguments():
+    L = fp4idx.lib()
+    assert L.fp4idx_ceiling_stream(ALIGNED, 1024, None, 0, None) == fp4idx.EINVAL
+    assert L.fp4idx_ceiling_stream(ALIGNED, 1040, ALIGNED, 1024, None) == fp4idx.EINVAL
+    assert L.fp4idx_ceiling_stream(MISALIGNED, 1024, ALIGNED, 1024, None) == fp4idx.EINVAL
+    assert L.fp4idx_ceiling_stream(ALIGNED, (1 << 40) + 1024, ALIGNED, 0, None) == fp4idx.EINVAL
+    assert L.fp4idx_ceiling_paged_gather(ALIGNED, ALIGNED, 4, ALIGNED, 8, ALIGNED, 1025, 1,
+                                         ALIGNED, 64, None) == fp4idx.EINVAL
+    assert L.fp4idx_ceiling_paged_gather(ALIGNED, ALIGNED, 4, ALIGNED, 8, ALIGNED, 4, 65,
+                                         ALIGNED, 64, None) == fp4idx.EINVAL
 
 
 def test_exports_every_declared_symbol():

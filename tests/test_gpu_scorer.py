@@ -241,6 +241,45 @@ def test_scorer_decode_full_size_sampled():
         check_scorer(got[rows], ref, bound, H)
 
 
+@pytest.mark.parametrize("B,next_n,H", [(1024, 1, 16), (1025, 2, 32), (700, 4, 64)])
+def test_scorer_many_sequences(B, next_n, H):
+    """Decode batches at the flat scorer's sequence limit (1,024: the per-sequence
+    block counts are scanned in 16 chunks of 64) and one past it (1,025: the
+    two-dimensional grid), with contexts of 0 to 300 keys, so that many
+    wavefronts cross one or more sequence boundaries."""
+    sc = workloads.scorer_case(5000 + B + next_n, B, next_n, H, 0, 300)
+    rng = np.random.default_rng(B)
+    bad = rng.random(sc.block_table.shape) < 0.1
+    sc.block_table[bad] = -1
+    say(f"case scorer many sequences B={B} next_n={next_n} H={H}")
+    got = run_gpu_scorer(sc, 0.5, True)
+    ref, bound = oracle.paged_mqa_logits(sc.q_out, sc.q_scale_out, sc.weights, sc.kv_cache,
+                                         sc.kv_cache_scale, sc.block_table, sc.context_lens,
+                                         next_n, weights_scale=0.5, with_bound=True)
+    check_scorer(got, ref, bound, H)
+
+
+def test_scorer_decode_long_ranges():
+    """100 sequences of 131,072 keys (204,800 blocks, 891 MB of cache) with
+    next_n = 1, H = 16: more blocks than 64 per wavefront of the resident grid,
+    so every wavefront walks several windows of block-table entries; the row
+    pattern of every query and three whole sequences against the oracle."""
+    B, next_n, H = 100, 1, 16
+    sc = workloads.scorer_case(8, B, next_n, H, 131072, 131072)
+    say(f"case scorer long ranges: {int(sc.context_lens.sum())} keys")
+    got = run_gpu_scorer(sc)
+    for b in range(B):
+        ctx = int(sc.context_lens[b])
+        _check_row_pattern(got[b], ctx - 1, ctx)
+    for b in (0, 37, B - 1):
+        rows = slice(b, b + 1)
+        ref, bound = oracle.paged_mqa_logits(sc.q_out[rows], sc.q_scale_out[rows],
+                                             sc.weights[rows], sc.kv_cache, sc.kv_cache_scale,
+                                             sc.block_table[b:b + 1], sc.context_lens[b:b + 1],
+                                             next_n, with_bound=True)
+        check_scorer(got[rows], ref, bound, H)
+
+
 def test_scorer_prefill_full_size_sampled():
     """The chunked-prefill scoring case at full size, in the launch the benchmark
     times (one sequence of 65,536 keys, its last 4,096 tokens as queries, H = 64,
