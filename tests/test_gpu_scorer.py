@@ -241,12 +241,14 @@ def test_scorer_decode_full_size_sampled():
         check_scorer(got[rows], ref, bound, H)
 
 
-@pytest.mark.parametrize("B,next_n,H", [(1024, 1, 16), (1025, 2, 32), (700, 4, 64)])
+@pytest.mark.parametrize("B,next_n,H", [(1024, 1, 16), (1025, 2, 32), (700, 4, 64), (1024, 7, 32),
+                                         (1030, 6, 16), (300, 9, 48)])
 def test_scorer_many_sequences(B, next_n, H):
-    """Decode batches at the flat scorer's sequence limit (1,024: the per-sequence
-    block counts are scanned in 16 chunks of 64) and one past it (1,025: the
-    two-dimensional grid), with contexts of 0 to 300 keys, so that many
-    wavefronts cross one or more sequence boundaries."""
+    """Batches at the flat scorer's sequence limit (1,024: the per-sequence item
+    counts are scanned in 16 chunks of 64) and past it (1,025 and 1,030: the
+    grid kernels), decode and query tiles (next_n 6, 7, 9 with a short last
+    tile), with contexts of 0 to 300 keys, so that many wavefronts cross one or
+    more sequence and tile boundaries."""
     sc = workloads.scorer_case(5000 + B + next_n, B, next_n, H, 0, 300)
     rng = np.random.default_rng(B)
     bad = rng.random(sc.block_table.shape) < 0.1
