@@ -550,7 +550,7 @@ def bench_scorer(args, dev):
         "config": {"workload": "decode_scoring", "sequences": B, "next_n": next_n, "heads": H,
                    "head_dim": 128, "kv_block_size": 64, "keys": keys, "context": "U[4096,131072]",
                    "relu": True},
-        "roofline": {"kernel": "mqa_logits_kernel<4,2,relu,decode>", "bound": "hbm", "achieved": gbs,
+        "roofline": {"kernel": "mqa_logits_flat_kernel<4,2,relu>", "bound": "hbm", "achieved": gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic(SCORER_TRAFFIC_FILE, SCORER_SOURCES),
                      "algorithmic_bytes_per_launch": bytes_,
@@ -559,6 +559,12 @@ def bench_scorer(args, dev):
                               "frac": tfs / FP4_MFMA_PEAK_TFLOPS,
                               "algorithmic_flops_per_launch": flops}},
     }
+    if not args.no_ceilings:
+        cg, cl, _, _ = measure_ceiling(args, dev, "paged_gather", sc)
+        rec["ceiling"] = {"kernel": "gather_kernel (fp4idx_ceiling_paged_gather)",
+                          "what": "the same block reads and logit writes, no arithmetic",
+                          "GBps": cg, "launch_us": cl, "frac_of_peak": cg / HBM_PEAK_GBS,
+                          "scorer_frac_of_ceiling": gbs / cg}
     if not args.no_cpu_baseline:
         import oracle
 
@@ -638,8 +644,8 @@ def bench_prefill_scoring(args, dev):
     print(json.dumps(rec), flush=True)
 
 
-def bench_ceiling(args, dev, kind: str):
-    """Ceiling measurements (fp4idx_ceiling_stream / fp4idx_ceiling_paged_gather):
+def measure_ceiling(args, dev, kind: str, sc=None):
+    """One ceiling measurement (fp4idx_ceiling_stream / fp4idx_ceiling_paged_gather):
     plain HBM traffic of the shapes the kernels move, none of their arithmetic.
       stream_read   reads the bytes the headline step reads (17,168 per token
                     x 131,072 tokens at H = 64), writes nothing;
@@ -649,8 +655,10 @@ def bench_ceiling(args, dev, kind: str):
                     131,072 tokens read, as many written);
       paged_gather  the decode-scoring batch's key blocks (4,096 + 256 bytes per
                     block of every sequence) and its logit writes, with the
-                    scorer's flat split over wavefronts.
-    Rates are bytes moved / mean launch time (events around every launch)."""
+                    scorer's flat split over wavefronts (sc: that batch, if the
+                    caller has it).
+    Returns (GB/s from the mean launch time, mean launch us, median ms per step
+    of the timed rounds, config)."""
     import numpy as np
     import torch
 
@@ -660,7 +668,8 @@ def bench_ceiling(args, dev, kind: str):
     T, H = args.tokens, args.heads
     if kind == "paged_gather":
         B, next_n = 64, 4
-        sc = workloads.scorer_case(7, B, next_n, 32, 4096, 131072)
+        if sc is None:
+            sc = workloads.scorer_case(7, B, next_n, 32, 4096, 131072)
         up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
         kv, ks = up(sc.kv_cache), up(sc.kv_cache_scale)
         table, ctx = up(sc.block_table), up(sc.context_lens)
@@ -696,18 +705,26 @@ def bench_ceiling(args, dev, kind: str):
                      settle_ms=args.settle_ms)
     (launch_ms,), (launch_med,) = launch_pass([call], K, stream)
     total = read_b + write_b
-    gbs = total / (launch_ms * 1e-3) / 1e9
+    shape = dict(shape, bytes_per_launch=total, launch_us_median=launch_med * 1e3)
+    return total / (launch_ms * 1e-3) / 1e9, launch_ms * 1e3, median(legs["step"]), shape
+
+
+def bench_ceiling(args, dev, kind: str):
+    """A ceiling measurement as its own bench line (see measure_ceiling)."""
+    gbs, launch_us, ms, shape = measure_ceiling(args, dev, kind)
     rec = {
         "metric": "HBM GB/s of plain traffic (ceiling measurement, no arithmetic)",
-        "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
-        "ms_per_step": median(legs["step"]), "higher_is_better": True, "scaling": "weak",
+        "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "u8", "data": "synthetic",
-        "config": dict({"workload": kind}, **shape),
+        "config": dict({"workload": kind}, **{k: v for k, v in shape.items()
+                                               if k not in ("bytes_per_launch",
+                                                            "launch_us_median")}),
         "roofline": {"kernel": "gather_kernel" if kind == "paged_gather" else "stream_kernel",
                      "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                     "algorithmic_bytes_per_launch": total, "launch_us": launch_ms * 1e3,
-                     "launch_us_median": launch_med * 1e3},
+                     "algorithmic_bytes_per_launch": shape["bytes_per_launch"],
+                     "launch_us": launch_us, "launch_us_median": shape["launch_us_median"]},
     }
     print(json.dumps(rec), flush=True)
 
@@ -729,6 +746,9 @@ def main():
     ap.add_argument("--heads", type=int, default=64, help="the prefill workloads")
     ap.add_argument("--cpu-sample-tokens", type=int, default=131072)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the ceiling measurements reported beside the headline and the "
+                         "decode scorer")
     ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
                     help="time steps replayed from captured HIP graphs (auto: on for decode, where "
                          "host launch overhead exceeds the kernel time)")
@@ -948,6 +968,17 @@ def main():
     if use_graph:
         rec["eager_ms_per_step"] = eager_ms_per_step
         rec["two_call_step"]["eager_ms_per_step"] = eager_two_ms
+    if not args.no_ceilings and wl.name == "large_prefill":
+        ceil = {}
+        for kind in ("stream_read", "stream_mix"):
+            cg, cl, _, shape = measure_ceiling(args, dev, kind)
+            ceil[kind] = {"GBps": cg, "launch_us": cl, "frac_of_peak": cg / HBM_PEAK_GBS,
+                          "read_bytes": shape["read_bytes"], "write_bytes": shape["write_bytes"]}
+        ceil["kernel"] = "stream_kernel (fp4idx_ceiling_stream)"
+        ceil["what"] = ("the step's read bytes alone, and its reads and writes in the same mix, as "
+                        "plain 1 KB streams")
+        ceil["fused_frac_of_stream_read"] = achieved / ceil["stream_read"]["GBps"]
+        rec["ceilings"] = ceil
     if not args.no_cpu_baseline:
         # outputs of one fused launch and of one two-call step, each from
         # sentinel-filled buffers (untimed), for the parity check
