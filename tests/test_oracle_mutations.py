@@ -56,6 +56,9 @@ MUTATIONS = {
     "weights_head_0_skipped": ("for (int h = 0; h < H; ++h) weights_out[t * H + h] = weights[t * H + h];",
                                "for (int h = 1; h < H; ++h) weights_out[t * H + h] = weights[t * H + h];"),
     "no_saturation": ("else code = 7;", "else code = 6;"),
+    "hadamard_scale_before_sums": (
+        "    for (int h = 1; h < HEAD_DIM; h <<= 1) {\n        for (int j = 0; j < HEAD_DIM; ++j) {\n            if (j & h) continue;\n            float u = x[j], w = x[j + h];\n            x[j] = u + w;\n            x[j + h] = u - w;\n        }\n    }\n    float sc = hadamard_scale();\n    for (int i = 0; i < HEAD_DIM; ++i) x[i] = round_bf16(x[i] * sc);",
+        "    float sc = hadamard_scale();\n    for (int i = 0; i < HEAD_DIM; ++i) x[i] = x[i] * sc;\n    for (int h = 1; h < HEAD_DIM; h <<= 1) {\n        for (int j = 0; j < HEAD_DIM; ++j) {\n            if (j & h) continue;\n            float u = x[j], w = x[j + h];\n            x[j] = u + w;\n            x[j + h] = u - w;\n        }\n    }\n    for (int i = 0; i < HEAD_DIM; ++i) x[i] = round_bf16(x[i]);"),
     "two_stage_sign_on_zero": ("uint8_t sign = (yv < 0.0f && code != 0) ? 1 : 0;",
                                "uint8_t sign = signbit(yv) ? 1 : 0;"),
     "two_stage_reuses_stage_1_exponent": ("int e2 = group_exponent(y, GROUP, floor2);",

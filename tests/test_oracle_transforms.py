@@ -188,3 +188,54 @@ def test_bf16_rounding_nearest_even():
     want = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo_even, lo, hi)))
     assert np.array_equal(got, want)
     assert np.array_equal(got.astype(np.float32), bf16_vals(x))
+
+
+def test_hadamard_exact_on_small_integer_and_dyadic_rows():
+    """Rows whose every butterfly sum is exact in fp32 (integers of magnitude
+    <= 64 and dyadic fractions k/2^m), so any stage order gives the exact
+    product H x: the result must be bf16(fl((H x) * fp32(1/sqrt(128)))) with
+    H = scipy's Sylvester Hadamard matrix, exactly.  A sequency-ordered
+    transform, a scale applied before the sums, a missing bf16 rounding or a
+    wrong constant fails this."""
+    rng = np.random.default_rng(21)
+    ints = rng.integers(-64, 65, (300, 128)).astype(np.float32)
+    dyad = (rng.integers(-255, 256, (300, 128)) / 2.0 ** rng.integers(0, 12, (300, 1)))
+    x = np.concatenate([ints, dyad.astype(np.float32)])
+    assert np.array_equal(bf16_vals(x), x)                   # the inputs are bf16 values
+    H = scipy.linalg.hadamard(128).astype(np.int64)
+    exact = x.astype(np.float64) @ H.T.astype(np.float64)    # sums of <= 128 exact terms
+    assert np.array_equal(exact.astype(np.float32).astype(np.float64), exact)
+    s = np.array([0x3DB504F3], np.uint32).view(np.float32)[0]
+    want = bf16_vals(exact.astype(np.float32) * s)
+    assert np.array_equal(oracle.fwht_rows(x), want)
+
+
+def test_rope_exact_dyadic_coefficients():
+    """cos/sin entries that are powers of two and bf16 inputs with short
+    significands make both products and their sum exact, so the result is
+    bf16(a c - b s) and bf16(b c + a s) exactly, whatever the rounding order:
+    pins the pairing, the columns and the signs with equality."""
+    rng = np.random.default_rng(22)
+    n = 64
+    cs = np.zeros((n, 64), np.float32)
+    cs[:, :32] = 2.0 ** rng.integers(-3, 2, (n, 32))
+    cs[:, 32:] = np.where(rng.random((n, 32)) < 0.5, -1.0, 1.0) * 2.0 ** rng.integers(-3, 2, (n, 32))
+    x = (rng.integers(-15, 16, (n, 128)) * 2.0 ** rng.integers(-4, 5, (n, 1))).astype(np.float32)
+    for is_neox in (True, False):
+        for ro in (0, 64):
+            got = oracle.rope_rows(x, cs, rope_offset=ro, is_neox=is_neox)
+            want = rope_f64(x, cs, ro, is_neox)                # exact here
+            assert np.array_equal(got.astype(np.float64), bf16_vals(want).astype(np.float64))
+
+
+def test_rmsnorm_exact_on_constant_magnitude_rows():
+    """|x_i| = c, a power of two, with any signs and eps = 0: mean c^2, root c
+    and reciprocal 1/c are exact, so y_i = sign(x_i) * gamma_i exactly."""
+    rng = np.random.default_rng(23)
+    gamma_f = bf16_vals(1.0 + 0.25 * rng.standard_normal(128))
+    gamma = to_bf16_bits(gamma_f)
+    for c in (2.0 ** -3, 1.0, 2.0 ** 5):
+        signs = np.where(rng.random((8, 128)) < 0.5, -1.0, 1.0).astype(np.float32)
+        x = (signs * np.float32(c)).astype(np.float32)
+        got = oracle.rmsnorm_rows(x, gamma, 0.0)
+        assert np.array_equal(got, signs * gamma_f), c
