@@ -149,8 +149,12 @@ __device__ __forceinline__ void q_sglang_token(const SQArgs& a, int64_t t, int l
     }
 }
 
+// Six wavefronts per SIMD: the neox build needs 82 VGPRs (five wavefronts); held
+// to 80 the compiler keeps one 8-byte value in scratch (reloaded twice per 32
+// heads) and the kernel ran at 475.6 against 489.6 us at 131072 x 64 back to
+// back (seven wavefronts, 72 VGPRs and 44 bytes of spills per lane: 481 us).
 template <bool NEOX>
-__global__ __launch_bounds__(kBlock) void q_sglang_kernel(SQArgs a) {
+__global__ __launch_bounds__(kBlock, 6) void q_sglang_kernel(SQArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
