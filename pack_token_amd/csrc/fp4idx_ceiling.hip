@@ -53,13 +53,19 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const u32x4_t* __restr
 
 // ---- paged gather with the decode scorer's decomposition --------------------
 // Quads of blocks (4q .. 4q+3 of one sequence) in one flat list, equal
-// contiguous ranges per wavefront, as the decode scorer takes them.  A
-// wavefront keeps four blocks in flight (a ring of four register sets, the
-// block three ahead loaded while the current one is folded) and writes each
-// quad's next_n logit rows as 1 KB stores, lane 16 r + m covering keys
-// 4 m .. 4 m + 3 of the quad's block r.
+// contiguous ranges per wavefront, as the decode scorer takes them, and the
+// scorer's data movement: each block's 4,096 code bytes and 256-byte scale row
+// come in through LDS-DMA loads (global_load_lds: lane L's 16 or 4 bytes land
+// at the slot base + 16 L or 4 L) into a ring of three slots per wavefront,
+// two blocks ahead of the one being read.  A block is read out of LDS and
+// folded into one value per lane; each quad's next_n logit rows leave as 1 KB
+// stores, lane 16 r + m covering keys 4 m .. 4 m + 3 of the quad's block r.
+// (A ring of four register sets, three blocks ahead, at five wavefronts per
+// SIMD moved the same bytes 8% slower.)
 constexpr int kGatherMaxB = 1024;
 constexpr int kWaves = kThreads / 64;
+constexpr int kRing = 3;
+constexpr int kBlockBytes = 4096;
 
 struct GatherArgs {
     const uint8_t* kv_cache;
@@ -76,29 +82,59 @@ struct GatherArgs {
 };
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-struct Blk {
-    u32x4_t v[4];
-    uint32_t s;
-};
+constexpr int waitcnt_vmcnt(int n) {  // s_waitcnt with only vmcnt limited (gfx9 encoding)
+    return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
 
-__device__ __forceinline__ void load_blk(const GatherArgs& a, int blki, int j, int cnt, int lane,
-                                         Blk& q) {
-    const int32_t blk = j < cnt ? __builtin_amdgcn_readlane(blki, j) : -1;
-    if (blk >= 0 && (int64_t)blk < a.nblocks) {
-        const uint8_t* base = a.kv_cache + (int64_t)blk * 4096 + 16 * lane;
+// Block blk's codes and scale row into one ring slot: five loads.
+__device__ __forceinline__ void fetch_block(const GatherArgs& a, int32_t blk, int lane, uint8_t* kl,
+                                            uint32_t* sl) {
+    const uint8_t* base = a.kv_cache + (int64_t)blk * kBlockBytes + 16 * lane;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) q.v[i] = ld_nt(reinterpret_cast<const u32x4_t*>(base + 1024 * i));
-        q.s = *reinterpret_cast<const uint32_t*>(a.kv_cache_scale + (int64_t)blk * 256 + 4 * lane);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) q.v[i] = (u32x4_t){0u, 0u, 0u, 0u};
-        q.s = 0u;
-    }
+    for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds(base + 1024 * i, (lds_ptr_t)(kl + 1024 * i), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(a.kv_cache_scale + (int64_t)blk * 256 + 4 * lane,
+                                     (lds_ptr_t)sl, 4, 0, 0);
+}
+
+// Vector memory operations complete in issue order: with the loads of n_after
+// later blocks (5 each) allowed in flight, every earlier block has landed.
+__device__ __forceinline__ void wait_landed(int n_after) {
+    if (n_after >= 2)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(10));
+    else if (n_after == 1)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(5));
+    else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(0));
+}
+
+// The lane's 64 bytes of a landed slot and its scale dword, folded to 32 bits;
+// the reads wait for themselves before the block ends.
+__device__ __forceinline__ uint32_t fold_slot(const uint8_t* kl, const uint32_t* sl, int lane) {
+    const uint32_t ka = (uint32_t)(uintptr_t)(lds_ptr_t)kl + 16 * lane;
+    const uint32_t sa = (uint32_t)(uintptr_t)(lds_ptr_t)sl + 4 * lane;
+    u32x4_t v0, v1, v2, v3;
+    uint32_t sc;
+    asm volatile(
+        "ds_read_b128 %0, %5\n\t"
+        "ds_read_b128 %1, %5 offset:1024\n\t"
+        "ds_read_b128 %2, %5 offset:2048\n\t"
+        "ds_read_b128 %3, %5 offset:3072\n\t"
+        "ds_read_b32 %4, %6\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3), "=&v"(sc)
+        : "v"(ka), "v"(sa)
+        : "memory");
+    const u32x4_t x = v0 ^ v1 ^ v2 ^ v3;
+    return x.x ^ x.y ^ x.z ^ x.w ^ sc;
 }
 
 __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs a) {
     extern __shared__ int32_t prefix[];  // [B] inclusive quad counts
+    __shared__ __attribute__((aligned(16))) uint8_t kbuf[kRing][kWaves][kBlockBytes];
+    __shared__ __attribute__((aligned(16))) uint32_t sbuf[kRing][kWaves][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int B = (int)a.B;
@@ -146,10 +182,20 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs a) {
             c = c < 0 ? 0 : (c > cap ? cap : c);
             if ((int64_t)kbi * 64 < c) blki = a.block_table[(int64_t)bi * a.max_blocks + kbi];
         }
-        Blk ring[4];
-        load_blk(a, blki, 0, cnt, lane, ring[0]);
-        load_blk(a, blki, 1, cnt, lane, ring[1]);
-        load_blk(a, blki, 2, cnt, lane, ring[2]);
+        // the previous window's blocks were all read; the entries land
+        __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(0));
+        auto fetched = [&](int j) {
+            if (j >= cnt) return false;
+            const int32_t blk = __builtin_amdgcn_readlane(blki, j);
+            return blk >= 0 && (int64_t)blk < a.nblocks;
+        };
+        auto fetch = [&](int j) {
+            fetch_block(a, __builtin_amdgcn_readlane(blki, j), lane, kbuf[j % kRing][wave],
+                        sbuf[j % kRing][wave]);
+        };
+        bool f1 = fetched(0), f2 = fetched(1);
+        if (f1) fetch(0);
+        if (f2) fetch(1);
         for (int qi = 0; qi < nq_win; ++qi) {
             const int b = __builtin_amdgcn_readlane(bi, 4 * qi);
             const int64_t kb0 = __builtin_amdgcn_readlane(kbi, 4 * qi);
@@ -161,9 +207,15 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs a) {
             uint32_t u = 0;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                load_blk(a, blki, 4 * qi + r + 3, cnt, lane, ring[(r + 3) & 3]);
-                const u32x4_t x = ring[r].v[0] ^ ring[r].v[1] ^ ring[r].v[2] ^ ring[r].v[3];
-                if (g == r) u = (x.x ^ x.y ^ x.z ^ x.w ^ ring[r].s) & 0x3FFFFFFFu;
+                const int j = 4 * qi + r;
+                const bool f0 = f1;  // block slot j was fetched
+                f1 = f2;
+                f2 = fetched(j + 2);
+                if (f2) fetch(j + 2);  // into the slot block j - 1 left
+                wait_landed((int)f1 + (int)f2);
+                const uint32_t x = f0 ? fold_slot(kbuf[j % kRing][wave], sbuf[j % kRing][wave], lane)
+                                      : 0u;
+                if (g == r) u = x & 0x3FFFFFFFu;
             }
             const f32x4_t o = {__uint_as_float(u), __uint_as_float(u ^ 1u), __uint_as_float(u ^ 2u),
                                __uint_as_float(u ^ 3u)};
