@@ -314,9 +314,10 @@ __global__ __launch_bounds__(64 * kWaves) void mqa_logits_kernel(LArgs a) {
 // inclusive prefix of the per-sequence quad counts in LDS; a wavefront maps the
 // blocks of a window of 16 quads to (sequence, block index) by binary search
 // with one lane per block, reads their block-table entries with one load per
-// lane, and walks them with the blocks fetched two ahead into a ring of three
-// LDS buffers.  The query operands of a sequence are loaded when the walk
-// enters it.
+// lane, and walks them with each block fetched one ahead into a ring of two
+// LDS buffers (fetching two ahead into three buffers measured 2% slower: 80-82
+// against 79-80 us on the 4.6 M-key decode batch).  The query operands of a
+// sequence are loaded when the walk enters it.
 //
 // Key order inside a block: matrix-core tile kt takes keys 4n + kt (n = lane %
 // 16), so after the cross-row reduce lane 16r + m holds key 4m + r.  Four such
@@ -328,16 +329,14 @@ __global__ __launch_bounds__(64 * kWaves) void mqa_logits_kernel(LArgs a) {
 // 4 (n % 4) + kt, so a lane reads the 16 bytes at 16 (n % 4) and picks byte
 // n / 4 of each dword with byte permutes.
 constexpr int kFlatMaxB = 1024;
-constexpr int kRing = 3;
+constexpr int kRing = 2;
 
 __device__ __forceinline__ void wait_prefetch(int n_after) {
     // n_after blocks (5 loads each) were fetched after the block that is needed:
     // once at most their loads are in flight, that block and everything issued
     // before it has landed (vector memory operations complete in issue order),
     // whatever else was issued in between
-    if (n_after >= 2)
-        __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(10));
-    else if (n_after == 1)
+    if (n_after >= 1)
         __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(5));
     else
         __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(0));
@@ -459,9 +458,8 @@ __global__ __launch_bounds__(64 * kWaves, HT <= 2 ? 3 : 2) void mqa_logits_flat_
             const int32_t blk = __builtin_amdgcn_readlane(blki, j);
             fetch_block(a, blk, lane, kbuf[j % kRing][wave], sbuf[j % kRing][wave]);
         };
-        bool f1 = fetched(0), f2 = fetched(1);
+        bool f1 = fetched(0);
         if (f1) fetch(0);
-        if (f2) fetch(1);
         int b = 0;
         int64_t kb = 0;
         for (int qi = 0; qi < nq_win; ++qi) {
@@ -469,13 +467,12 @@ __global__ __launch_bounds__(64 * kWaves, HT <= 2 ? 3 : 2) void mqa_logits_flat_
             for (int r = 0; r < 4; ++r) {
                 const int j = 4 * qi + r;
                 const bool f0 = f1;  // block slot j was fetched
-                f1 = f2;
-                f2 = fetched(j + 2);
-                if (f2) fetch(j + 2);  // into the ring slot block j - 1 left
+                f1 = fetched(j + 1);
+                if (f1) fetch(j + 1);  // into the ring slot block j - 1 left
                 b = __builtin_amdgcn_readlane(bi, j);
                 kb = __builtin_amdgcn_readlane(kbi, j);
                 if (__builtin_amdgcn_readlane(live, j) == 0) continue;  // past the context
-                wait_prefetch((int)f1 + (int)f2);
+                wait_prefetch((int)f1);
                 if (b != cur_b) {  // entering a sequence: its query operands
                     cur_b = b;
                     int64_t c = a.context_lens[b];
