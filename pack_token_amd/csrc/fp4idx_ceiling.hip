@@ -54,10 +54,12 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const u32x4_t* __restr
 // ---- paged gather with the decode scorer's decomposition --------------------
 // Quads of blocks (4q .. 4q+3 of one sequence) in one flat list, equal
 // contiguous ranges per wavefront, as the decode scorer takes them, and the
-// scorer's data movement: each block's 4,096 code bytes and 256-byte scale row
-// come in through LDS-DMA loads (global_load_lds: lane L's 16 or 4 bytes land
-// at the slot base + 16 L or 4 L) into a ring of three slots per wavefront,
-// two blocks ahead of the one being read.  A block is read out of LDS and
+// scorer's kind of data movement: each block's 4,096 code bytes and 256-byte
+// scale row come in through LDS-DMA loads (global_load_lds: lane L's 16 or 4
+// bytes land at the slot base + 16 L or 4 L) into a ring of slots per
+// wavefront, here three slots two blocks ahead of the one being read (the
+// fastest depth for the reads alone; the scorer, with its arithmetic between
+// reads, keeps one block ahead in two).  A block is read out of LDS and
 // folded into one value per lane; each quad's next_n logit rows leave as 1 KB
 // stores, lane 16 r + m covering keys 4 m .. 4 m + 3 of the quad's block r.
 // (A ring of four register sets, three blocks ahead, at five wavefronts per
