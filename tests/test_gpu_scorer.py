@@ -328,3 +328,46 @@ def test_scorer_worked_cases(idx):
     assert (got[untouched] == SENT).all(), case["name"]
     assert np.array_equal(got[~untouched].view(np.uint32), want[~untouched].view(np.uint32)), \
         case["name"]
+
+
+def test_scorer_logits_past_32_bit_offsets():
+    """Chunked prefill whose logits tensor holds more than 2^32 bytes (20,000
+    queries x 131,072 keys, 10.5 GB): rows near the end are addressed past
+    every 32-bit offset.  On the device, the -inf count is exactly the causal
+    triangle and no entry is left untouched; four groups of queries (the first,
+    two in the middle, the last) against the oracle, each as a case whose
+    context ends right after its queries, as in the full run."""
+    import torch
+
+    from pack_token_amd import fp4idx
+
+    B, next_n, H, ctx_len = 1, 20000, 16, 131072
+    sc = workloads.scorer_case(13, B, next_n, H, ctx_len, ctx_len)
+    say("case scorer logits past 32-bit offsets: 20000 x 131072, H = 16")
+    dev = "cuda:0"
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    logits = torch.full((next_n, ctx_len), float(SENT), dtype=torch.float32, device=dev)
+    assert logits.numel() * 4 > 2 ** 32
+    fp4idx.paged_mqa_logits(t(sc.q_out), t(sc.q_scale_out), t(sc.weights), t(sc.kv_cache),
+                            t(sc.kv_cache_scale), t(sc.block_table), t(sc.context_lens),
+                            next_n, logits=logits)
+    torch.cuda.synchronize()
+    n_inf = int(torch.isneginf(logits).sum().item())
+    n_sent = int((logits == float(SENT)).sum().item())
+    n_fin = int(torch.isfinite(logits).sum().item())
+    assert n_inf == next_n * (next_n - 1) // 2
+    assert n_sent == 0
+    assert n_fin + n_inf == logits.numel()
+    for r0 in (0, 9998, 12001, next_n - 4):
+        got = logits[r0:r0 + 4].cpu().numpy()
+        for j in range(4):
+            _check_row_pattern(got[j], ctx_len - next_n + r0 + j, ctx_len)
+        ctx_sub = ctx_len - next_n + r0 + 4
+        rows = slice(r0, r0 + 4)
+        ref, bound = oracle.paged_mqa_logits(sc.q_out[rows], sc.q_scale_out[rows],
+                                             sc.weights[rows], sc.kv_cache, sc.kv_cache_scale,
+                                             sc.block_table, np.array([ctx_sub], np.int32), 4,
+                                             with_bound=True)
+        check_scorer(got[:, :ctx_sub], ref[:, :ctx_sub], bound[:, :ctx_sub], H)
+    del logits
+    torch.cuda.empty_cache()
