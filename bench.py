@@ -753,7 +753,7 @@ def main():
                     help="time steps replayed from captured HIP graphs (auto: on for decode, where "
                          "host launch overhead exceeds the kernel time)")
     ap.add_argument("--graph-steps", type=int, default=10, help="steps captured per graph")
-    ap.add_argument("--rounds", type=int, default=3,
+    ap.add_argument("--rounds", type=int, default=5,
                     help="timed rounds of K steps per leg (legs alternate; median reported)")
     ap.add_argument("--settle-ms", type=float, default=100.0,
                     help="untimed GPU time spent on steps after the warm-up steps, so clocks "
