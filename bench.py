@@ -34,6 +34,7 @@ CSRC = os.path.join(ROOT, "pack_token_amd", "csrc")
 MAIN_SOURCES = ("fp4idx_device.h", "fp4idx_kernels.hip")
 MODE_SOURCES = ("fp4idx_device.h", "fp4idx_modes.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qk_kernel_large_prefill_traffic.json")
+PNR_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qk_kernel_prefill_norm_rotate_traffic.json")
 SGLANG_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q_sglang_kernel_sglang_prefill_traffic.json")
 FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q_fp8_kernel_fp8_prefill_traffic.json")
 FQ_TRAFFIC_FILE = os.path.join(ROOT, "profiles",
@@ -641,6 +642,17 @@ def bench_prefill_scoring(args, dev):
         "hbm_view": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": bytes_},
     }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        # the last 4 queries against the whole context (their causal pairs)
+        nq = 4
+        sub_pairs = int((pos[-nq:] + 1).sum())
+        rec["cpu_baseline"] = oracle_baseline(
+            lambda: oracle.paged_mqa_logits(sc.q_out[-nq:], sc.q_scale_out[-nq:],
+                                            sc.weights[-nq:], sc.kv_cache, sc.kv_cache_scale,
+                                            sc.block_table, np.array([ctx_len], np.int32), nq),
+            sub_pairs, f"the last {nq} queries' causal pairs x {H} heads", pairs, noun="pairs")
     print(json.dumps(rec), flush=True)
 
 
@@ -909,7 +921,11 @@ def main():
 
     step_bytes = step_bytes_per_token(H) * T
     achieved = step_bytes / (fused_ms * 1e-3) / 1e9
-    traffic = measured_traffic() if wl.name == "large_prefill" and (T, H) == (131072, 64) else None
+    traffic = None
+    if wl.name == "large_prefill" and (T, H) == (131072, 64):
+        traffic = measured_traffic()
+    elif wl.name == "prefill_norm_rotate" and (T, H) == (16384, 64):
+        traffic = measured_traffic(PNR_TRAFFIC_FILE)
     rec = {
         "metric": "tokens/s and achieved HBM GB/s (% of peak), fused q+k RoPE/FP4 pack+store",
         "value": T / (ms_per_step * 1e-3),
@@ -960,10 +976,10 @@ def main():
         hbm = rec["roofline"]
         rec["roofline"] = {"kernel": hbm["kernel"], "bound": "alu", "achieved": gops,
                            "peak": VALU_PEAK_GOPS, "unit": "Gop/s", "frac": gops / VALU_PEAK_GOPS,
-                           "traffic": None, "algorithmic_ops_per_launch": ops,
+                           "traffic": hbm["traffic"], "algorithmic_ops_per_launch": ops,
                            "launch_us": hbm["launch_us"],
                            "launch_us_median": hbm["launch_us_median"]}
-        rec["hbm_view"] = {k: hbm[k] for k in ("achieved", "peak", "unit", "frac",
+        rec["hbm_view"] = {k: hbm[k] for k in ("achieved", "peak", "unit", "frac", "traffic",
                                                "algorithmic_bytes_per_launch")}
     if use_graph:
         rec["eager_ms_per_step"] = eager_ms_per_step
