@@ -286,6 +286,17 @@ def alu_ops_per_token(H: int, hadamard: bool, norm: bool) -> int:
     return (H + 1) * row + (128 * 3 if norm else 0)
 
 
+def stream_ceiling(args, dev, read_b: int, write_b: int, kernel_gbs: float) -> dict:
+    """The launch's read and written bytes as plain 1 KB streams (measured live),
+    and the kernel's rate as a fraction of that stream's."""
+    cg, cl, _, _ = measure_ceiling(args, dev, "stream_rw", rw=(read_b, write_b))
+    return {"kernel": "stream_kernel (fp4idx_ceiling_stream)",
+            "what": "the launch's read and written bytes as plain 1 KB streams, writes spread "
+                    "over the reads",
+            "read_bytes": read_b, "write_bytes": write_b, "GBps": cg, "launch_us": cl,
+            "frac_of_peak": cg / HBM_PEAK_GBS, "kernel_frac_of_ceiling": kernel_gbs / cg}
+
+
 def fp8_q_bytes_per_token(H: int) -> int:
     return 256 * H + 4 * H + 8 + 256 + 128 * H + 2 * H
 
@@ -357,6 +368,9 @@ def bench_fp8(args, dev):
                      else None,
                      "algorithmic_bytes_per_launch": qb, "launch_us": q_ms * 1e3},
     }
+    if not args.no_ceilings:
+        rec["ceiling"] = stream_ceiling(args, dev, (256 * H + 4 * H + 8 + 256) * T,
+                                        (128 * H + 2 * H) * T, q_gbs)
     if not args.no_cpu_baseline:
         n = min(args.cpu_sample_tokens, T, 16384)
 
@@ -419,6 +433,8 @@ def bench_fake_quant(args, dev):
                      else None,
                      "algorithmic_bytes_per_launch": b, "launch_us": l_ms * 1e3},
     }
+    if not args.no_ceilings:
+        rec["ceiling"] = stream_ceiling(args, dev, (256 * H + 8 + 256) * T, 256 * H * T, gbs)
     if not args.no_cpu_baseline:
         n = min(args.cpu_sample_tokens, T, 4096)
         rec["cpu_baseline"] = oracle_baseline(
@@ -493,6 +509,8 @@ def bench_sglang(args, dev):
                      "algorithmic_bytes_per_launch": qb,
                      "launch_us": q_ms * 1e3},
     }
+    if not args.no_ceilings:
+        rec["ceiling"] = stream_ceiling(args, dev, (256 * H + 8 + 256) * T, 68 * H * T, q_gbs)
     if not args.no_cpu_baseline:
         n = min(args.cpu_sample_tokens, T, 16384)
 
@@ -656,7 +674,7 @@ def bench_prefill_scoring(args, dev):
     print(json.dumps(rec), flush=True)
 
 
-def measure_ceiling(args, dev, kind: str, sc=None):
+def measure_ceiling(args, dev, kind: str, sc=None, rw=None):
     """One ceiling measurement (fp4idx_ceiling_stream / fp4idx_ceiling_paged_gather):
     plain HBM traffic of the shapes the kernels move, none of their arithmetic.
       stream_read   reads the bytes the headline step reads (17,168 per token
@@ -668,7 +686,9 @@ def measure_ceiling(args, dev, kind: str, sc=None):
       paged_gather  the decode-scoring batch's key blocks (4,096 + 256 bytes per
                     block of every sequence) and its logit writes, with the
                     scorer's flat split over wavefronts (sc: that batch, if the
-                    caller has it).
+                    caller has it);
+      stream_rw     rw = (read bytes, written bytes) of a caller's launch, writes
+                    spread over the reads.
     Returns (GB/s from the mean launch time, mean launch us, median ms per step
     of the timed rounds, config)."""
     import numpy as np
@@ -698,7 +718,9 @@ def measure_ceiling(args, dev, kind: str, sc=None):
                  "context": "U[4096,131072]"}
     else:
         J = ((H // 16) + 3) // 4 * 4
-        if kind == "stream_copy":
+        if kind == "stream_rw":
+            read_b, write_b = rw
+        elif kind == "stream_copy":
             read_b = write_b = 256 * H * T
         else:
             read_b = (256 * H + 4 * H + 8 + 256 + 256 + 8) * T
