@@ -341,6 +341,29 @@ inline bool grid_fits(int64_t blocks, int64_t threads) {
     return blocks >= 0 && blocks <= (int64_t)0xFFFFFFFF / threads;
 }
 
+// Dynamic LDS for a launch that keeps at most `per_cu` of its workgroups
+// resident on a compute unit: the launch reserves about 1/per_cu of the unit's
+// LDS (the part beyond `dyn` and the kernel's static LDS is not used).  The
+// streaming kernels move their bytes faster with fewer wavefronts resident
+// (fewer concurrent DRAM streams); the cap is chosen per kernel by measurement.
+// If the device cannot give a workgroup that much LDS, or reading its limits
+// fails, the launch keeps `dyn` and its occupancy.
+inline size_t resident_cap_lds(const void* fn, size_t dyn, int per_cu) {
+    int dev = 0, lds_cu = 0, lds_wg = 0;
+    hipFuncAttributes fa;
+    if (per_cu <= 0 || hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&lds_wg, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+            hipSuccess ||
+        hipFuncGetAttributes(&fa, fn) != hipSuccess)
+        return dyn;
+    // per_cu workgroups fit and per_cu + 1 do not
+    const size_t total = (size_t)lds_cu / (size_t)per_cu - 1024;
+    if (total > (size_t)lds_wg || total <= fa.sharedSizeBytes + dyn) return dyn;
+    return total - fa.sharedSizeBytes;
+}
+
 template <typename K, typename A>
 hipError_t launch(K kernel, int64_t blocks, size_t lds, hipStream_t stream, const A& a) {
     if (!grid_fits(blocks, kBlock)) return hipErrorInvalidConfiguration;

@@ -572,8 +572,15 @@ hipError_t launch_q_rope_pack(const QArgs& a, bool is_neox, bool hadamard, hipSt
     if (hadamard)
         return is_neox ? launch(q_row_kernel<true>, blocks, lds, stream, a)
                        : launch(q_row_kernel<false>, blocks, lds, stream, a);
-    return is_neox ? launch(q_split_kernel<true>, blocks, lds, stream, a)
-                   : launch(q_split_kernel<false>, blocks, lds, stream, a);
+    // two workgroups per compute unit: 409 against 431 us at 131072 x 64 with
+    // the five that the registers allow
+    if (is_neox)
+        return launch(q_split_kernel<true>, blocks,
+                      resident_cap_lds(reinterpret_cast<const void*>(q_split_kernel<true>), lds, 2),
+                      stream, a);
+    return launch(q_split_kernel<false>, blocks,
+                  resident_cap_lds(reinterpret_cast<const void*>(q_split_kernel<false>), lds, 2),
+                  stream, a);
 }
 
 hipError_t launch_k_rope_pack_store(const KArgs& a, bool is_neox, bool hadamard,
@@ -603,13 +610,24 @@ hipError_t launch_qk_rope_pack_store(const QArgs& qa, const KArgs& ka, bool is_n
     const bool norm = ka.gamma != nullptr;
     const int sel = (is_neox ? 4 : 0) | (hadamard ? 2 : 0) | (norm ? 1 : 0);
     const unsigned kw = kBlock + 64;  // a fifth wavefront for the key rows (no Hadamard)
+    // without the Hadamard, two workgroups per compute unit: 416 against 427 us
+    // at 131072 x 64 with the four that the registers allow (three: 426 us)
+    auto cap = [&](const void* fn) { return resident_cap_lds(fn, lds, 2); };
     switch (sel) {
-        case 0: return launch2(qk_kernel<false, false, false>, blocks, lds, stream, qa, ka, kw);
-        case 1: return launch2(qk_kernel<false, false, true>, blocks, lds, stream, qa, ka, kw);
+        case 0: return launch2(qk_kernel<false, false, false>, blocks,
+                               cap(reinterpret_cast<const void*>(qk_kernel<false, false, false>)),
+                               stream, qa, ka, kw);
+        case 1: return launch2(qk_kernel<false, false, true>, blocks,
+                               cap(reinterpret_cast<const void*>(qk_kernel<false, false, true>)),
+                               stream, qa, ka, kw);
         case 2: return launch2(qk_kernel<false, true, false>, blocks, lds, stream, qa, ka);
         case 3: return launch2(qk_kernel<false, true, true>, blocks, lds, stream, qa, ka);
-        case 4: return launch2(qk_kernel<true, false, false>, blocks, lds, stream, qa, ka, kw);
-        case 5: return launch2(qk_kernel<true, false, true>, blocks, lds, stream, qa, ka, kw);
+        case 4: return launch2(qk_kernel<true, false, false>, blocks,
+                               cap(reinterpret_cast<const void*>(qk_kernel<true, false, false>)),
+                               stream, qa, ka, kw);
+        case 5: return launch2(qk_kernel<true, false, true>, blocks,
+                               cap(reinterpret_cast<const void*>(qk_kernel<true, false, true>)),
+                               stream, qa, ka, kw);
         case 6: return launch2(qk_kernel<true, true, false>, blocks, lds, stream, qa, ka);
         default: return launch2(qk_kernel<true, true, true>, blocks, lds, stream, qa, ka);
     }

@@ -617,8 +617,15 @@ __global__ __launch_bounds__(kBlock) void fake_quant_token_kernel(FakeQArgs a) {
 hipError_t launch_q_rope_pack_sglang(const SQArgs& a, bool is_neox, hipStream_t stream) {
     if (a.T == 0) return hipSuccess;
     const int64_t blocks = (a.T + kWavesPerBlock - 1) / kWavesPerBlock;
-    return is_neox ? launch(q_sglang_kernel<true>, blocks, 0, stream, a)
-                   : launch(q_sglang_kernel<false>, blocks, 0, stream, a);
+    // four workgroups per compute unit: 421-427 against 474-478 us at 131072 x 64
+    // with the six that the registers allow (three: 429-438, two: 540)
+    if (is_neox)
+        return launch(q_sglang_kernel<true>, blocks,
+                      resident_cap_lds(reinterpret_cast<const void*>(q_sglang_kernel<true>), 0, 4),
+                      stream, a);
+    return launch(q_sglang_kernel<false>, blocks,
+                  resident_cap_lds(reinterpret_cast<const void*>(q_sglang_kernel<false>), 0, 4),
+                  stream, a);
 }
 
 hipError_t launch_k_rope_pack_store_sglang(const SKArgs& a, bool is_neox, hipStream_t stream) {
