@@ -149,10 +149,11 @@ __device__ __forceinline__ void q_sglang_token(const SQArgs& a, int64_t t, int l
     }
 }
 
-// Six wavefronts per SIMD: the neox build needs 82 VGPRs (five wavefronts); held
-// to 80 the compiler keeps one 8-byte value in scratch (reloaded twice per 32
-// heads) and the kernel ran at 475.6 against 489.6 us at 131072 x 64 back to
-// back (seven wavefronts, 72 VGPRs and 44 bytes of spills per lane: 481 us).
+// Registers held to 80 (the bound of six wavefronts per SIMD): the neox build
+// would take 82; at 80 the compiler keeps one 8-byte value in scratch (reloaded
+// twice per 32 heads).  With the launcher's four resident workgroups per CU the
+// kernel ran at 425-427 us at 131072 x 64 against 489-492 without the bound
+// (at full occupancy: 475.6 against 489.6; seven wavefronts, 72 VGPRs: 481).
 template <bool NEOX>
 __global__ __launch_bounds__(kBlock, 6) void q_sglang_kernel(SQArgs a) {
     const int lane = threadIdx.x & 63;
