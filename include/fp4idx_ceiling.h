@@ -19,12 +19,14 @@ extern "C" {
 
 /*
  * Reads read_bytes from src and writes write_bytes to dst (both multiples of
- * 1,024, both buffers 16-byte aligned) in 1 KB units, one unit per wavefront
- * step, the write units spread evenly over the read units while write_bytes
- * <= read_bytes: write_bytes = 0 is a read-only stream, equal sizes a copy.
- * dst receives data derived from src (its contents are of no use) and must
- * hold at least 1,024 bytes even for a read-only stream.  Each size is at most
- * 2^40 bytes.  One persistent grid of 16-byte accesses.
+ * 1,024, both buffers 16-byte aligned) in 1 KB units, the write units spread
+ * evenly over the read units while write_bytes <= read_bytes: write_bytes = 0
+ * is a read-only stream, equal sizes a copy.  A read-only stream takes four
+ * units per wavefront step on two workgroups per compute unit, a stream with
+ * writes one unit per step at full occupancy (the shapes that measured
+ * fastest for each).  dst receives data derived from src (its contents are of
+ * no use) and must hold at least 1,024 bytes even for a read-only stream.
+ * Each size is at most 2^40 bytes.  One persistent grid of 16-byte accesses.
  */
 int fp4idx_ceiling_stream(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes,
                           void* stream);
@@ -36,7 +38,8 @@ int fp4idx_ceiling_stream(const void* src, int64_t read_bytes, void* dst, int64_
  * kv_cache [NB,1,4,64,16] and its 256-byte row of kv_cache_scale [NB,1,4,64],
  * and writes next_n fp32 values per key into logits [B*next_n, stride] (values
  * of no use), with the scorer's flat, balanced split of the blocks over
- * wavefronts.  B <= 1024, next_n <= 64, B * max_blocks < 2^31.
+ * wavefronts and LDS-DMA loads into a per-wavefront ring.  B <= 1024,
+ * next_n <= 64, B * max_blocks < 2^31.
  */
 int fp4idx_ceiling_paged_gather(const uint8_t* kv_cache, const uint8_t* kv_cache_scale, int64_t NB,
                                 const int32_t* block_table, int64_t max_blocks,
