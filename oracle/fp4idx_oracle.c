@@ -572,11 +572,15 @@ void oracle_quantize_rows_two_stage(const float* x, int64_t n, float floor1, flo
 /* ------------------------------------------------------------------ */
 #define FP8_MAX 448.0f
 
-/* e4m3fn code of a finite y.  Magnitudes: k * 2^-9 for codes k < 8
-   (subnormals), (8 + m) * 2^(E - 10) for code (E << 3) | m, E = 1..15,
-   except code 0x7F (NaN).  Nearest value, ties to the even code; anything
-   at or beyond 448 saturates to 448 (0x7E). */
+/* e4m3fn code of y.  Magnitudes: k * 2^-9 for codes k < 8 (subnormals),
+   (8 + m) * 2^(E - 10) for code (E << 3) | m, E = 1..15, except code 0x7F
+   (NaN).  Nearest value, ties to the even code; anything at or beyond 448,
+   infinities included, saturates to 448 (0x7E).  A NaN y (inf / inf, when
+   an infinite amax makes an fp32 scale infinite) is the format's NaN
+   pattern with the sign bit clear, 0x7F: IEEE arithmetic leaves the sign of
+   that NaN unspecified. */
 static uint8_t e4m3_code(float y) {
+    if (isnan(y)) return 0x7F;
     const uint8_t sign = signbit(y) ? 0x80 : 0x00;
     const double a = fabs((double)y);
     if (a >= 448.0) return (uint8_t)(sign | 0x7E);

@@ -65,6 +65,35 @@ def test_zero_sign_and_saturation():
     assert oracle.e4m3_codes(y).tolist() == [0x00, 0x80, 0x80, 0x7E, 0x7E, 0xFE, 0x00, 0x80]
 
 
+def test_infinities_saturate_and_nan_is_0x7f():
+    """Infinities lie beyond 448 and saturate like every other such value; a
+    NaN (of either sign) is e4m3fn's all-ones pattern S.1111.111 with S = 0
+    (the torch cast agrees on the pattern, not on the saturation)."""
+    y = np.array([np.inf, -np.inf, 3.4e38, -3.4e38], np.float32)
+    assert oracle.e4m3_codes(y).tolist() == [0x7E, 0xFE, 0x7E, 0xFE]
+    nan = np.array([np.nan, -np.nan], np.float32)
+    assert oracle.e4m3_codes(nan).tolist() == [0x7F, 0x7F]
+    assert torch_e4m3(nan[:1]).tolist() == [0x7F]
+
+
+def test_infinite_row_amax():
+    """A row holding an infinity: amax / 448 is infinite.  Under ue8m0 its
+    exponent field 255 clamps to 254 (s = 2^127) and the infinity saturates
+    to 448; under fp32 scales s = inf, a finite x / s is a signed zero and
+    inf / inf a NaN (0x7F)."""
+    x = np.zeros((1, 16, 128), np.uint16)
+    x[0, 0, :4] = [0x7F80, 0xFF80, 0x3F80, 0xBF80]      # +inf, -inf, 1, -1
+    x[0, 0, 64:] = workloads.to_bf16_bits(np.linspace(-3, 3, 64).astype(np.float32))
+    pos = np.zeros(1, np.int64)
+    cs = workloads.cos_sin_table(1)                      # position 0: no rotation
+    w = np.ones((1, 16), np.float32)
+    q, _ = oracle.q_rope_pack_fp8(x, pos, cs, w, scale_fmt=0)
+    assert q[0, 0, :4].tolist() == [0x7E, 0xFE, 0x00, 0x80]   # 1 / 2^127 is far below 2^-9
+    q, wo = oracle.q_rope_pack_fp8(x, pos, cs, w, scale_fmt=1)
+    assert q[0, 0, :4].tolist() == [0x7F, 0x7F, 0x00, 0x80]
+    assert (q[0, 0, 4:] & 0x7F == 0).all() and wo[0, 0] == 0x7F80   # bf16 +inf weight
+
+
 def test_scales():
     rng = np.random.default_rng(1)
     amax = (rng.uniform(0.5, 1, 5000) * 2.0 ** rng.integers(-130, 120, 5000)).astype(np.float32)
