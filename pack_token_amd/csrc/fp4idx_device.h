@@ -123,8 +123,10 @@ __device__ __forceinline__ uint4 select4(bool c, uint4 a, uint4 b) {
 // ---- quantizer ---------------------------------------------------------------
 // UE8M0 exponent of a group whose largest |value| is the bf16 number with
 // magnitude bits m: the least e with amax <= 6 * 2^(e-127), which equals the
-// biased exponent of ceil_pow2(fl(amax / 6)) for every bf16 amax, i.e.
-// ((m + 0x3F) >> 7) - 2, then raised to the floor's exponent e_lo >= 1.
+// biased exponent of ceil_pow2(fl(amax / 6)) for every finite bf16 amax, i.e.
+// ((m + 0x3F) >> 7) - 2, then raised to the floor's exponent e_lo >= 1.  An
+// infinite amax (a rotated or normalised value past the fp32 range) makes
+// amax / 6 infinite, whose exponent field 255 clamps to 254.
 // Codes come from the gfx950 scaled converter, which divides by the
 // power-of-two scale 2^(e-127) exactly and rounds to the E2M1 grid with ties
 // to even, keeping the sign of zero.
@@ -144,7 +146,7 @@ __device__ __forceinline__ Q8 quant8(uint4 v, int e_lo) {
     uint32_t m = max((uint32_t)m2.x, (uint32_t)m2.y);
     m = max(m, dpp<kDppXor1>(m));
     m = max(m, dpp<kDppXor2>(m));
-    const int e = max((int)((m + 0x3Fu) >> 7) - 2, e_lo);
+    const int e = m >= 0x7F80u ? 254 : max((int)((m + 0x3Fu) >> 7) - 2, e_lo);
     const float scale = __uint_as_float((uint32_t)e << 23);
     // each converter writes one byte of its first operand and the four calls
     // cover all of it, so a dead value seeds the chain (no zeroing move)

@@ -35,7 +35,7 @@ __device__ __forceinline__ Q8 quant8_two_stage(uint4 v, int e_lo1, int e_lo2) {
     uint32_t m = max((uint32_t)m2.x, (uint32_t)m2.y);
     m = max(m, dpp<kDppXor1>(m));
     m = max(m, dpp<kDppXor2>(m));
-    const int e1 = max((int)((m + 0x3Fu) >> 7) - 2, e_lo1);
+    const int e1 = m >= 0x7F80u ? 254 : max((int)((m + 0x3Fu) >> 7) - 2, e_lo1);
     const float scale1 = __uint_as_float((uint32_t)e1 << 23);
     // each converter writes one byte of its first operand; the four calls
     // overwrite all of it, so any dead value may seed the chain
@@ -227,6 +227,39 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
     return pack_bf16x2(x, 0.0f) & 0xFFFFu;
 }
 
+// A row whose amax is infinite (a rotated or normalised value past the fp32
+// range) has an infinite amax / 448 (the division sequence below would give
+// NaN), so under fp32 scales s = inf and under ue8m0 s = 2^127 (e = 254).
+// Its codes:
+//   ue8m0: the converter turns +-inf into the NaN code (0x7F / 0xFF) while
+//     every value at or beyond 448 saturates to 448, so bytes 0x7F / 0xFF
+//     become 0x7E / 0xFE.  A finite x never meets the NaN code here (s >=
+//     amax / 448 keeps |x| / s <= 448), so rows with s = 2^127 are patched
+//     whether or not they hold an infinity.  (t + 1 reaches bit 7 of a byte
+//     exactly when its low seven bits are all set, with no carry into the
+//     next byte.)
+//   fp32: x / inf is +-0 for a finite x (0x00 / 0x80) and NaN for an infinite
+//     one (0x7F); w0, w1 hold four bf16 values, the result their codes.
+constexpr uint32_t kUe8m0MaxScaleBits = 254u << 23;  // 2^127
+
+__device__ __forceinline__ uint32_t saturate_nan_codes(uint32_t d) {
+    const uint32_t t = d & 0x7F7F7F7Fu;
+    return d ^ (((t + 0x01010101u) & 0x80808080u) >> 7);
+}
+
+__device__ __forceinline__ uint32_t infinite_scale_codes(uint32_t w0, uint32_t w1) {
+    const uint32_t h[4] = {w0 & 0xFFFFu, w0 >> 16, w1 & 0xFFFFu, w1 >> 16};
+    uint32_t r = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        r |= ((h[i] & 0x7FFFu) >= 0x7F80u ? 0x7Fu : (h[i] >> 8) & 0x80u) << (8 * i);
+    return r;
+}
+
+__device__ __forceinline__ float fp8_amax_over_448(uint32_t m) {
+    return m >= 0x7F80u ? __builtin_huge_valf() : div_const_rn(__uint_as_float(m << 16), 448.0f, kRcp448);
+}
+
 template <bool FP32>
 __device__ __forceinline__ uint2 quant_fp8_row(uint4 v, float scale_floor, float& s_out) {
     const u16x2_t a0 = __builtin_bit_cast(u16x2_t, v.x & 0x7FFF7FFFu);
@@ -240,7 +273,7 @@ __device__ __forceinline__ uint2 quant_fp8_row(uint4 v, float scale_floor, float
     m = max(m, dpp<kDppXor2>(m));
     m = max(m, dpp<kDppHalfMirror>(m));
     m = max(m, dpp<kDppRor8>(m));
-    float s = div_const_rn(__uint_as_float(m << 16), 448.0f, kRcp448);
+    float s = fp8_amax_over_448(m);
     s = s < scale_floor ? scale_floor : s;
     s16x2_t lo = {0, 0}, hi = {0, 0};
     if (!FP32) {
@@ -251,6 +284,13 @@ __device__ __forceinline__ uint2 quant_fp8_row(uint4 v, float scale_floor, float
         lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, __builtin_bit_cast(bf16x2_t, v.y), s, true);
         hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, __builtin_bit_cast(bf16x2_t, v.z), s, false);
         hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, __builtin_bit_cast(bf16x2_t, v.w), s, true);
+        if (__float_as_uint(s) == kUe8m0MaxScaleBits) {
+            lo = __builtin_bit_cast(s16x2_t, saturate_nan_codes(__builtin_bit_cast(uint32_t, lo)));
+            hi = __builtin_bit_cast(s16x2_t, saturate_nan_codes(__builtin_bit_cast(uint32_t, hi)));
+        }
+    } else if (s == __builtin_huge_valf()) {
+        lo = __builtin_bit_cast(s16x2_t, infinite_scale_codes(v.x, v.y));
+        hi = __builtin_bit_cast(s16x2_t, infinite_scale_codes(v.z, v.w));
     } else {
         const float r = __frcp_rn(s);  // RN(1/s)
         float x[8], y[8];
@@ -336,7 +376,7 @@ __device__ __forceinline__ float fp8_head_scale(uint4 p, uint4 r, float scale_fl
     m = max(m, dpp<kDppXor1>(m));
     m = max(m, dpp<kDppXor2>(m));
     m = max(m, dpp<kDppHalfMirror>(m));
-    float s = div_const_rn(__uint_as_float(m << 16), 448.0f, kRcp448);
+    float s = fp8_amax_over_448(m);
     s = s < scale_floor ? scale_floor : s;
     if (!FP32) {
         const uint32_t b = __float_as_uint(s);
@@ -354,6 +394,13 @@ __device__ __forceinline__ uint2 fp8_codes8(uint4 v, float s, float r) {
         lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, __builtin_bit_cast(bf16x2_t, v.y), s, true);
         hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, __builtin_bit_cast(bf16x2_t, v.z), s, false);
         hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, __builtin_bit_cast(bf16x2_t, v.w), s, true);
+        if (__float_as_uint(s) == kUe8m0MaxScaleBits) {
+            lo = __builtin_bit_cast(s16x2_t, saturate_nan_codes(__builtin_bit_cast(uint32_t, lo)));
+            hi = __builtin_bit_cast(s16x2_t, saturate_nan_codes(__builtin_bit_cast(uint32_t, hi)));
+        }
+    } else if (s == __builtin_huge_valf()) {
+        lo = __builtin_bit_cast(s16x2_t, infinite_scale_codes(v.x, v.y));
+        hi = __builtin_bit_cast(s16x2_t, infinite_scale_codes(v.z, v.w));
     } else {
         float x[8], y[8];
         unpack8(v, x);

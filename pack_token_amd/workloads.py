@@ -150,6 +150,38 @@ def sweep_case(seed: int, T: int, H: int, is_neox: bool, rope_offset: int,
                     rope_offset=rope_offset)
 
 
+def _plant_overflow_pairs(rng, rows_bits: np.ndarray, rope_offset: int, is_neox: bool):
+    """rows_bits: uint16 [n,128] modified in place.  About half of the rows get
+    one RoPE pair of the slice at rope_offset whose two elements have the
+    largest finite bf16 magnitude (0x7F7F) with random signs, so that the
+    rotated value of the pair can exceed the fp32 range.  One pair per row:
+    the rotation sends at most one of its two outputs past the range."""
+    n = rows_bits.shape[0]
+    rows = np.nonzero(rng.random(n) < 0.5)[0]
+    pair = rng.integers(0, ROPE_DIM // 2, rows.size)
+    if is_neox:
+        ia, ib = pair, pair + ROPE_DIM // 2
+    else:
+        ia, ib = 2 * pair, 2 * pair + 1
+    signs = rng.integers(0, 2, (rows.size, 2)).astype(np.uint16) << 15
+    rows_bits[rows, rope_offset + ia] = 0x7F7F | signs[:, 0]
+    rows_bits[rows, rope_offset + ib] = 0x7F7F | signs[:, 1]
+
+
+def overflow_case(seed: int, T: int, H: int, is_neox: bool, rope_offset: int,
+                  apply_hadamard: bool) -> Workload:
+    """A sweep point whose rows carry pairs of largest-magnitude bf16 values in
+    the rotated slice (see _plant_overflow_pairs), positions U[0,4096)."""
+    wl = sweep_case(seed, T, H, is_neox, rope_offset)
+    rng = np.random.Generator(np.random.PCG64(seed + 7))
+    _plant_overflow_pairs(rng, wl.q.reshape(T * H, HEAD_DIM), rope_offset, is_neox)
+    _plant_overflow_pairs(rng, wl.k, rope_offset, is_neox)
+    wl.name = f"overflow_T{T}_H{H}_{'neox' if is_neox else 'inter'}_o{rope_offset}" + (
+        "_had" if apply_hadamard else "")
+    wl.apply_hadamard = apply_hadamard
+    return wl
+
+
 _MID_MULTS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0],
                       np.float32)
 

@@ -56,6 +56,17 @@ def test_modes_ragged(mode, neox, ro):
 
 
 @pytest.mark.parametrize("mode", sorted(MODES))
+@pytest.mark.parametrize("neox,ro", [(True, 64), (False, 0)])
+def test_overflow_rows(mode, neox, ro):
+    """Rows whose rotation leaves the fp32 range (one RoPE pair of
+    largest-magnitude bf16 values in about half of the rows)."""
+    wl = workloads.overflow_case(81 + ro + neox, 37, 48, neox, ro, False)
+    check(wl.q, wl.positions, wl.cos_sin, mode, rows_per_position=48, is_neox=neox,
+          rope_offset=ro)
+    check(wl.k, wl.positions, wl.cos_sin, mode, is_neox=neox, rope_offset=ro)
+
+
+@pytest.mark.parametrize("mode", sorted(MODES))
 def test_floors(mode):
     wl = workloads.edge_mix(seed=620, T=40, H=16)
     for floor in (0.0, 1e-3, 3.0):

@@ -87,6 +87,16 @@ def test_modes(fmt, neox, ro, had):
 
 
 @pytest.mark.parametrize("fmt", ["ue8m0", "fp32"])
+@pytest.mark.parametrize("neox,ro", [(True, 64), (False, 0)])
+@pytest.mark.parametrize("had", [False, True])
+def test_overflow_rows(fmt, neox, ro, had):
+    """Rows whose rotation leaves the fp32 range (one RoPE pair of
+    largest-magnitude bf16 values in about half of the rows): the row amax
+    is infinite."""
+    check(workloads.overflow_case(71 + ro + neox, 300, 16, neox, ro, had), fmt, had=had)
+
+
+@pytest.mark.parametrize("fmt", ["ue8m0", "fp32"])
 def test_floors_and_tiny_rows(fmt):
     wl = workloads.edge_mix(seed=520, T=64, H=16)
     q = wl.q.copy()

@@ -66,6 +66,28 @@ def test_modes_ragged(is_neox, rope_offset, norm, had, fused):
 
 
 @FUSED
+@pytest.mark.parametrize("is_neox", [True, False])
+@pytest.mark.parametrize("rope_offset", [0, 64])
+@pytest.mark.parametrize("had", [False, True])
+def test_overflow_rows(is_neox, rope_offset, had, fused):
+    """Finite inputs whose rotation leaves the fp32 range: half of the query
+    and key rows carry one RoPE pair of largest-magnitude bf16 values, so one
+    output of the pair is +-inf.  Its group amax is infinite, amax / 6 too, and
+    the exponent field 255 clamps to e = 254 (the block-exponent rule of
+    sgl-project/sglang PR 39656, review); the infinite value takes code 7.
+    With the Hadamard the infinity reaches every value of its row (no NaN: a
+    row holds one infinity).  T = 40 runs the small-batch kernel, T = 613 the
+    per-token ones."""
+    for T in (40, 613):
+        wl = workloads.overflow_case(31 + T, T, 16 if T < 100 else 48, is_neox, rope_offset, had)
+        say(f"case {wl.name}: T={wl.T} H={wl.H} fused={fused}")
+        got = gpu_run(wl, fused=fused)
+        ref = oracle_run(wl)
+        assert (ref[1] == 254).any() and (ref[4] == 254).any()  # the case reaches e = 254
+        assert_all_same(got, ref)
+
+
+@FUSED
 @pytest.mark.parametrize("had", [False, True])
 def test_maximum_heads(had, fused):
     """H = 2048, the largest head count the ABI accepts (J = 128 q-scale

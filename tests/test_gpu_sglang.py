@@ -110,6 +110,18 @@ def test_modes_with_rmsnorm(neox, ro):
     check_both(wl, slots, n, gamma=gamma)
 
 
+@pytest.mark.parametrize("neox,ro", [(True, 64), (True, 0), (False, 64), (False, 0)])
+def test_overflow_rows(neox, ro):
+    """Rows whose rotation leaves the fp32 range (one RoPE pair of
+    largest-magnitude bf16 values in about half of the rows): the stage-1
+    amax is infinite, so e1 = 254, and the infinite values take code 7."""
+    wl = workloads.overflow_case(61 + ro + neox, 300, 16, neox, ro, False)
+    ref = oracle.q_rope_pack_sglang(wl.q, wl.positions, wl.cos_sin, is_neox=neox, rope_offset=ro)
+    assert (ref[:, :, 64:] == 254).any()  # the case reaches e = 254
+    slots, n = with_slot_zero(wl)
+    check_both(wl, slots, n)
+
+
 def test_maximum_heads():
     """H = 2048 query records (139 KB per token) and ragged T."""
     wl = workloads.sweep_case(778, 5, 2048, False, 0)
