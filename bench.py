@@ -270,9 +270,43 @@ def oracle_parity(wl, outputs: dict, threads: int) -> dict:
 
 
 FP4_MFMA_PEAK_TFLOPS = 10100.0
-# fp32 vector operations per second, one per lane per cycle (adds and multiplies
-# that are not fused; packed fp32 is not used): 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
-VALU_PEAK_GOPS = 256 * 4 * 16 * 2.4
+# fp32 vector lane operations per second: MI355X's published fp32 vector rate,
+# 157.3 TFLOP/s with a fused multiply-add counted as two flops, is 78.6 T lane
+# operations (an add, a multiply or a fused multiply-add each) per second.
+# Plain (not packed) fp32 adds and fused multiply-adds issue at most of that
+# rate (fp4idx_ceiling_valu, measured beside the ALU-bound kernels).
+VALU_PEAK_GOPS = 157.3e3 / 2
+VALU_CEILING_KINDS = ("fp32_add", "fp32_fma", "fp32_max", "bf16_pack", "fp4_convert")
+
+
+def valu_ceiling(args, dev, kernel_gops: float) -> dict:
+    """Issue rate of single VALU instruction kinds (fp4idx_ceiling_valu): 8
+    workgroups of 256 threads per compute unit (8 wavefronts per SIMD), 8
+    independent chains per lane; lane operations per second from the mean
+    launch time, and the ALU-bound kernel's rate as a fraction of the fp32-add
+    rate."""
+    import torch
+
+    from pack_token_amd import fp4idx
+
+    stream = torch.cuda.current_stream(dev)
+    wg = 8 * torch.cuda.get_device_properties(dev).multi_processor_count
+    iters = 4096
+    out = torch.empty(wg * 256, dtype=torch.int32, device=dev)
+    rec = {"kernel": "valu_kernel (fp4idx_ceiling_valu)",
+           "what": "lane operations per second of one instruction kind, 8 independent chains "
+                   "per lane, 8 wavefronts per SIMD",
+           "workgroups": wg, "iterations": iters}
+    for kind in VALU_CEILING_KINDS:
+        def call(kind=kind):
+            fp4idx.ceiling_valu(kind, wg, iters, out)
+
+        for _ in range(max(args.warmup, 2)):
+            call()
+        (ms,), _ = launch_pass([call], max(args.steps, 5), stream)
+        rec[kind + "_Gops"] = wg * 256 * iters * 8 / (ms * 1e-3) / 1e9
+    rec["kernel_frac_of_fp32_add"] = kernel_gops / rec["fp32_add_Gops"]
+    return rec
 
 
 def alu_ops_per_token(H: int, hadamard: bool, norm: bool) -> int:
@@ -660,6 +694,8 @@ def bench_prefill_scoring(args, dev):
         "hbm_view": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": bytes_},
     }
+    if not args.no_ceilings:
+        rec["valu_ceiling"] = valu_ceiling(args, dev, gops)
     if not args.no_cpu_baseline:
         import oracle
 
@@ -1003,6 +1039,8 @@ def main():
                            "launch_us_median": hbm["launch_us_median"]}
         rec["hbm_view"] = {k: hbm[k] for k in ("achieved", "peak", "unit", "frac", "traffic",
                                                "algorithmic_bytes_per_launch")}
+        if not args.no_ceilings:
+            rec["valu_ceiling"] = valu_ceiling(args, dev, gops)
     if use_graph:
         rec["eager_ms_per_step"] = eager_ms_per_step
         rec["two_call_step"]["eager_ms_per_step"] = eager_two_ms

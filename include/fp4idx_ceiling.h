@@ -2,7 +2,8 @@
  * fp4idx_ceiling.h -- measurement entry points of libfp4idx: plain HBM
  * traffic of the shapes the producer and the scorer move, with none of the
  * method's arithmetic, so their measured rates can be set against what the
- * same traffic reaches on this GPU.  Not part of the method; used by the
+ * same traffic reaches on this GPU; and the VALU issue rate of single
+ * instruction kinds, for the kernels bound by vector ALU issue.  Not part of the method; used by the
  * benchmark.  Conventions as in fp4idx.h: device pointers, `stream` a
  * hipStream_t as void* (NULL = default stream), nothing allocated, no
  * synchronization.  Returns 0 on success, 1 for an invalid argument (nothing
@@ -45,6 +46,23 @@ int fp4idx_ceiling_paged_gather(const uint8_t* kv_cache, const uint8_t* kv_cache
                                 const int32_t* block_table, int64_t max_blocks,
                                 const int32_t* context_lens, int64_t B, int next_n, float* logits,
                                 int64_t stride, void* stream);
+
+/*
+ * VALU issue rate: `workgroups` workgroups of 256 threads, every lane running
+ * 8 independent chains of `iterations` steps of one instruction kind, so that
+ * with several wavefronts per SIMD the rate at which the SIMDs issue that
+ * instruction bounds the launch:
+ *   kind 0  fp32 add (v_add_f32), 1  fp32 fused multiply-add with distinct
+ *   operands (v_fma_f32), 2  fp32 max (v_max_f32), 3  fp32 pair -> packed
+ *   bf16 (v_cvt_pk_bf16_f32), 4  bf16 pair -> E2M1 with a power-of-two scale
+ *   (v_cvt_scalef32_pk_fp4_bf16).
+ * Lane operations performed: workgroups * 256 * iterations * 8.  out (4-byte
+ * aligned) receives workgroups * 256 dwords, one per thread, derived from its
+ * chains (values of no use).  kind outside 0..4, workgroups outside
+ * [1, 2^20], iterations outside [0, 2^32] or a null out: 1, nothing enqueued.
+ */
+int fp4idx_ceiling_valu(int kind, int64_t workgroups, int64_t iterations, uint32_t* out,
+                        void* stream);
 
 #ifdef __cplusplus
 }

@@ -7,6 +7,8 @@
 //     scale row of each block named by a block table) with the scorer's flat,
 //     balanced decomposition, writing next_n fp32 values per key as the scorer
 //     writes its logits.
+//   - a VALU issue-rate kernel: independent chains of one instruction kind,
+//     the rate the ALU-bound kernels are set against.
 // Every load feeds a store, so no access is dead code.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -252,6 +254,66 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs a) {
     }
 }
 
+// VALU issue rate of one instruction kind: every lane runs 8 independent chains
+// of `iterations` steps (8 wave instructions per step, so the issue rate, not
+// the latency of one chain, limits a SIMD holding several wavefronts) and
+// stores one dword that depends on all of them.
+//   0  fp32 add              v_add_f32           f = f + y
+//   1  fp32 fused mul-add    v_fma_f32 / fmac    f = fma(f, y, z)
+//   2  fp32 max              v_max_f32           f = max(f, y)
+//   3  fp32 -> packed bf16   v_cvt_pk_bf16_f32   u = bf16x2(u, u')
+//   4  bf16 -> E2M1 scaled   v_cvt_scalef32_pk_fp4_bf16, one byte of u
+typedef __bf16 ceil_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float ceil_f32x2_t __attribute__((ext_vector_type(2)));
+
+template <int KIND>
+__global__ __launch_bounds__(kThreads) void valu_kernel(uint32_t* out, int64_t iterations, float y,
+                                                       float z) {
+    const int64_t tid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    float f[8];
+    uint32_t u[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        f[i] = (float)(tid & 1023) * 0.001f + (float)i;
+        u[i] = (uint32_t)tid * 2654435761u + 0x3F803F80u * (uint32_t)i;
+    }
+    // the step operands in vector registers, as the kernels measured against
+    // hold theirs (an operand read from a scalar register measured slower)
+    float yv, zv;
+    asm("v_mov_b32 %0, %1" : "=v"(yv) : "s"(y));
+    asm("v_mov_b32 %0, %1" : "=v"(zv) : "s"(z));
+    auto step = [&]() {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (KIND == 0) f[i] = f[i] + yv;
+            if (KIND == 1) f[i] = __builtin_fmaf(f[i], yv, zv);
+            // written out: fmaxf would first quiet signalling NaNs with a
+            // second max of the operand with itself
+            if (KIND == 2) asm("v_max_f32_e32 %0, %0, %1" : "+v"(f[i]) : "v"(yv));
+            if (KIND == 3) {
+                const ceil_f32x2_t v = {__uint_as_float(u[i]), __uint_as_float(u[(i + 1) & 7])};
+                u[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, ceil_bf16x2_t));
+            }
+            if (KIND == 4)
+                u[i] = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
+                    u[i], __builtin_bit_cast(ceil_bf16x2_t, u[(i + 3) & 7]), yv, 0);
+        }
+    };
+    // four steps per trip, so the loop's scalar bookkeeping is a small share
+    int64_t it = 0;
+    for (; it + 4 <= iterations; it += 4) {
+        step();
+        step();
+        step();
+        step();
+    }
+    for (; it < iterations; ++it) step();
+    uint32_t r = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r ^= u[i] ^ __float_as_uint(f[i]);
+    out[tid] = r;
+}
+
 int device_wgs(const void* fn, size_t lds, int* wgs) {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 3;
@@ -319,4 +381,21 @@ extern "C" int fp4idx_ceiling_paged_gather(const uint8_t* kv_cache, const uint8_
     void* args[] = {&a};
     return hipLaunchKernel(reinterpret_cast<const void*>(gather_kernel), dim3(wgs), dim3(kThreads),
                            args, lds, static_cast<hipStream_t>(stream)) == hipSuccess ? 0 : 3;
+}
+
+extern "C" int fp4idx_ceiling_valu(int kind, int64_t workgroups, int64_t iterations, uint32_t* out,
+                                   void* stream) {
+    if (kind < 0 || kind > 4 || workgroups < 1 || workgroups > ((int64_t)1 << 20) ||
+        iterations < 0 || iterations > ((int64_t)1 << 32) || !out || ((uintptr_t)out & 3))
+        return 1;
+    const void* fns[] = {reinterpret_cast<const void*>(valu_kernel<0>),
+                         reinterpret_cast<const void*>(valu_kernel<1>),
+                         reinterpret_cast<const void*>(valu_kernel<2>),
+                         reinterpret_cast<const void*>(valu_kernel<3>),
+                         reinterpret_cast<const void*>(valu_kernel<4>)};
+    // y, z: a step that keeps add and fma chains finite and non-constant
+    float y = 1.0001f, z = 0.25f;
+    void* args[] = {&out, &iterations, &y, &z};
+    return hipLaunchKernel(fns[kind], dim3((unsigned)workgroups), dim3(kThreads), args, 0,
+                           static_cast<hipStream_t>(stream)) == hipSuccess ? 0 : 3;
 }

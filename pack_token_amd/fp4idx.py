@@ -85,6 +85,8 @@ def lib():
             L.fp4idx_ceiling_paged_gather.argtypes = [_p, _p, _i64, _p, _i64, _p, _i64, _i, _p,
                                                       _i64, _p]
             L.fp4idx_ceiling_paged_gather.restype = _i
+            L.fp4idx_ceiling_valu.argtypes = [_i, _i64, _i64, _p, _p]
+            L.fp4idx_ceiling_valu.restype = _i
             L.fp4idx_last_error.argtypes = []
             L.fp4idx_last_error.restype = ctypes.c_char_p
             _lib = L
@@ -545,3 +547,24 @@ def ceiling_paged_gather(kv_cache, kv_cache_scale, block_table, context_lens, ne
                                            _stream_handle(stream))
     if rc != OK:
         raise Fp4IdxError(rc, "fp4idx_ceiling_paged_gather failed")
+
+
+VALU_KINDS = {"fp32_add": 0, "fp32_fma": 1, "fp32_max": 2, "bf16_pack": 3, "fp4_convert": 4}
+
+
+def ceiling_valu(kind: str, workgroups: int, iterations: int, out, *, stream=None):
+    """VALU issue rate of one instruction kind: workgroups x 256 threads, 8
+    independent chains of `iterations` steps per lane (workgroups * 256 *
+    iterations * 8 lane operations); out (int32, workgroups * 256 elements)
+    receives one value per thread."""
+    if kind not in VALU_KINDS:
+        raise ValueError(f"kind must be one of {sorted(VALU_KINDS)}")
+    if out is None:
+        raise ValueError("out is required")
+    _require(out, "out", (torch.int32,))
+    if out.numel() < workgroups * 256:
+        raise ValueError(f"out holds {out.numel()} elements, needs {workgroups * 256}")
+    rc = lib().fp4idx_ceiling_valu(VALU_KINDS[kind], workgroups, iterations, _ptr(out),
+                                   _stream_handle(stream))
+    if rc != OK:
+        raise Fp4IdxError(rc, "fp4idx_ceiling_valu failed")

@@ -25,7 +25,7 @@ def declared_functions(header=HEADER):
 
 def test_exports_every_measurement_symbol():
     names = declared_functions(os.path.join(ROOT, "include", "fp4idx_ceiling.h"))
-    assert names == ["fp4idx_ceiling_paged_gather", "fp4idx_ceiling_stream"]
+    assert names == ["fp4idx_ceiling_paged_gather", "fp4idx_ceiling_stream", "fp4idx_ceiling_valu"]
     lib = ctypes.CDLL(fp4idx.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -41,6 +41,14 @@ def test_measurement_entry_points_reject_bad_arguments():
                                          ALIGNED, 64, None) == fp4idx.EINVAL
     assert L.fp4idx_ceiling_paged_gather(ALIGNED, ALIGNED, 4, ALIGNED, 8, ALIGNED, 4, 65,
                                          ALIGNED, 64, None) == fp4idx.EINVAL
+    assert L.fp4idx_ceiling_valu(5, 8, 16, ALIGNED, None) == fp4idx.EINVAL
+    assert L.fp4idx_ceiling_valu(-1, 8, 16, ALIGNED, None) == fp4idx.EINVAL
+    assert L.fp4idx_ceiling_valu(0, 0, 16, ALIGNED, None) == fp4idx.EINVAL
+    assert L.fp4idx_ceiling_valu(0, (1 << 20) + 1, 16, ALIGNED, None) == fp4idx.EINVAL
+    assert L.fp4idx_ceiling_valu(0, 8, -1, ALIGNED, None) == fp4idx.EINVAL
+    assert L.fp4idx_ceiling_valu(0, 8, (1 << 32) + 1, ALIGNED, None) == fp4idx.EINVAL
+    assert L.fp4idx_ceiling_valu(0, 8, 16, None, None) == fp4idx.EINVAL
+    assert L.fp4idx_ceiling_valu(0, 8, 16, ALIGNED + 2, None) == fp4idx.EINVAL
 
 
 def test_exports_every_declared_symbol():

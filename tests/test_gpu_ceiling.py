@@ -63,3 +63,41 @@ def test_paged_gather_writes_in_context_entries_only(stride_pad):
         rows = got[4 * b:4 * b + 4]
         assert (rows[:, :ctx] >= 0).all() and np.isfinite(rows[:, :ctx]).all()
         assert (rows[:, ctx:] == -7.0).all()
+
+
+def _valu_expected(kind, workgroups, iterations):
+    """Per-thread results of the fp32 add / max chains (numpy fp32, one rounding
+    per operation, as the kernel computes them)."""
+    tid = np.arange(workgroups * 256, dtype=np.int64)
+    y = np.float32(1.0001)
+    r = np.zeros(tid.size, np.uint32)
+    for i in range(8):
+        f = (tid & 1023).astype(np.float32) * np.float32(0.001) + np.float32(i)
+        for _ in range(iterations):
+            f = (f + y) if kind == "fp32_add" else np.maximum(f, y)
+        u = (tid.astype(np.uint64) * 2654435761 + 0x3F803F80 * i).astype(np.uint32)
+        r ^= u ^ f.astype(np.float32).view(np.uint32)
+    return r
+
+
+def test_valu_issue_kernel_runs_its_chains():
+    """The issue-rate kernel computes what it claims: the fp32 add and max
+    chains match a numpy evaluation, every kind is deterministic, and nothing
+    past workgroups * 256 elements is written."""
+    import torch
+
+    from pack_token_amd import fp4idx
+
+    wg, it = 4, 37
+    for kind in fp4idx.VALU_KINDS:
+        say(f"case ceiling valu kind={kind}")
+        outs = []
+        for _ in range(2):
+            out = torch.full((wg * 256 + 64,), -5, dtype=torch.int32, device="cuda:0")
+            fp4idx.ceiling_valu(kind, wg, it, out)
+            torch.cuda.synchronize()
+            outs.append(out.cpu().numpy())
+        assert np.array_equal(outs[0], outs[1])
+        assert (outs[0][wg * 256:] == -5).all()
+        if kind in ("fp32_add", "fp32_max"):
+            assert np.array_equal(outs[0][:wg * 256].view(np.uint32), _valu_expected(kind, wg, it))
