@@ -283,8 +283,8 @@ def valu_ceiling(args, dev, kernel_gops: float) -> dict:
     """Issue rate of single VALU instruction kinds (fp4idx_ceiling_valu): 8
     workgroups of 256 threads per compute unit (8 wavefronts per SIMD), 8
     independent chains per lane; lane operations per second from the mean
-    launch time, and the ALU-bound kernel's rate as a fraction of the fp32-add
-    rate."""
+    launch time, the fp32 adds again at 2 wavefronts per SIMD, and the
+    ALU-bound kernel's rate as a fraction of the fp32-add rate."""
     import torch
 
     from pack_token_amd import fp4idx
@@ -305,6 +305,16 @@ def valu_ceiling(args, dev, kernel_gops: float) -> dict:
             call()
         (ms,), _ = launch_pass([call], max(args.steps, 5), stream)
         rec[kind + "_Gops"] = wg * 256 * iters * 8 / (ms * 1e-3) / 1e9
+    # the same adds at two wavefronts per SIMD (the scorers' occupancy)
+    wg2 = wg // 4
+
+    def call2():
+        fp4idx.ceiling_valu("fp32_add", wg2, iters, out)
+
+    for _ in range(max(args.warmup, 2)):
+        call2()
+    (ms,), _ = launch_pass([call2], max(args.steps, 5), stream)
+    rec["fp32_add_2_waves_per_simd_Gops"] = wg2 * 256 * iters * 8 / (ms * 1e-3) / 1e9
     rec["kernel_frac_of_fp32_add"] = kernel_gops / rec["fp32_add_Gops"]
     return rec
 
