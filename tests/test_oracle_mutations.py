@@ -20,6 +20,8 @@ MUTATIONS = {
     "tie_at_5_goes_down": ("else if (m <= 5.0f) code = 6;", "else if (m < 5.0f) code = 6;"),
     "zero_code_drops_sign": ("return (uint8_t)((sign << 3) | code);",
                              "return (uint8_t)(((code ? sign : 0) << 3) | code);"),
+    "exponent_clamped_at_253": ("    if (e < 1) e = 1;\n    if (e > 254) e = 254;\n    return e;",
+                                "    if (e < 1) e = 1;\n    if (e > 253) e = 253;\n    return e;"),
     "floor_exponent_rule": ("uint32_t b = f2u(q);\n    int e = (int)(b >> 23) + ((b & 0x7FFFFFu) != 0u ? 1 : 0);",
                             "uint32_t b = f2u(q);\n    int e = (int)(b >> 23);"),
     "neox_interleaved_swapped": ("int ia = is_neox ? i : 2 * i;", "int ia = is_neox ? 2 * i : i;"),

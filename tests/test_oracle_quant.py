@@ -89,6 +89,30 @@ def test_group_exponent_closed_forms():
     assert oracle.group_exponents(big)[0] == 253
 
 
+def test_infinite_amax_and_overflowing_rotation():
+    """Values past the fp32 range.  A group holding +-inf: amax / 6 is infinite,
+    and its exponent field 255 (mantissa 0) clamps to e = 254 by the
+    block-exponent rule (sgl-project/sglang PR 39656, review); the infinities
+    take code 7 with their sign, every finite v the code of v * 2^-127.  And a
+    neox pair of largest-magnitude bf16 values rotated at cos = sin =
+    fp32(sqrt(1/2)): a' = fl(a c) - fl(b s) = 0 exactly, b' = fl(b c) + fl(a s)
+    overflows to +inf, so b's group gets e = 254 and code 7."""
+    g = np.zeros((1, 32), np.float32)
+    g[0, :6] = [np.inf, -np.inf, 2.0 ** 127, -3.0 * 2.0 ** 126, 1.0, -1.0]
+    assert oracle.group_exponents(g)[0] == 254
+    assert oracle.e2m1_nibbles(g, 254)[0, :6].tolist() == [0x7, 0xF, 0x2, 0xB, 0x0, 0x8]
+    big = bf16_bits_to_f32(np.array([0x7F7F], np.uint16))[0]
+    x = np.zeros((1, 128), np.float32)
+    x[0, 64] = x[0, 96] = big                       # pair 0 of the slice at 64
+    cs = np.zeros((1, 64), np.float32)
+    cs[0, 0] = cs[0, 32] = np.float32(np.sqrt(0.5))
+    y = oracle.rope_rows(x, cs)
+    assert y[0, 64] == 0.0 and y[0, 96] == np.inf
+    b, e = oracle.quantize_rows(y)
+    assert e[0].tolist() == [1, 1, 1, 254]          # groups 0-2 hold zeros only
+    assert b[0, 48] & 0xF == 0x7 and (b[0, 49:] == 0).all()
+
+
 def test_group_exponent_exhaustive_against_definition():
     """All 32,639 positive finite bf16 amax values: (bits>>23)+(mant!=0) of
     fl(amax/6) equals the least e with amax <= 6*2^(e-127), clamped to [1,254];
