@@ -38,7 +38,10 @@
  *   1, 254) where E(x) is the biased exponent of x rounded up to a power of
  *   two, (bits >> 23) + (mantissa != 0) (sgl-project/sglang PR 39656,
  *   review).  `scale_floor` is the eps floor applied after the divide; 2^-126
- *   (FLT_MIN) makes it coincide with the lower clamp.
+ *   (FLT_MIN) makes it coincide with the lower clamp.  A finite input that the
+ *   rotation, RMSNorm or Hadamard carries past the fp32 range is +-inf: its
+ *   group's amax / 6 is infinite, E = 255 clamps to e = 254, and the
+ *   infinite values take code 7 with their sign.
  * - Codes: each value v of the group becomes the E2M1 code of v * 2^(127-e)
  *   rounded to nearest, ties to even, with the sign bit of v kept even when
  *   the magnitude code is 0 (ROCm/aiter PR 5484 "One deliberate deviation").
@@ -241,8 +244,10 @@ int fp4idx_k_rope_pack_store_sglang(const void* k, const void* positions, int po
  *     s = 2^(E - 127), E = clamp(E(amax / 448 floored), 1, 254)   (ue8m0 = 0)
  * with E() the block-exponent rule above, and every element the e4m3fn code
  * nearest to x / s (x / s rounded to fp32 first; ties to even; the sign kept
- * on zero; codes 0x7F/0xFF never produced).  The preshuffled cache layout
- * is not provided.
+ * on zero; every magnitude at or beyond 448, infinities included, saturates
+ * to 448).  Codes 0x7F/0xFF are never produced, except 0x7F for inf / inf
+ * when an infinite value makes an fp32 scale infinite (its other elements
+ * are then signed zeros).  The preshuffled cache layout is not provided.
  *
  * fp4idx_q_rope_pack_fp8
  *   q, positions, positions_int64, cos_sin, max_pos, T, H, D, R,
