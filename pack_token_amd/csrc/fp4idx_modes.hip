@@ -257,7 +257,8 @@ __device__ __forceinline__ uint32_t infinite_scale_codes(uint32_t w0, uint32_t w
 }
 
 __device__ __forceinline__ float fp8_amax_over_448(uint32_t m) {
-    return m >= 0x7F80u ? __builtin_huge_valf() : div_const_rn(__uint_as_float(m << 16), 448.0f, kRcp448);
+    return m >= 0x7F80u ? __builtin_huge_valf()
+                        : div_const_rn(__uint_as_float(m << 16), 448.0f, kRcp448);
 }
 
 template <bool FP32>
