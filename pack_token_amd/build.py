@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libfp4idx.so")
 SOURCES = [os.path.join(CSRC, "fp4idx_kernels.hip"), os.path.join(CSRC, "fp4idx_modes.hip"),
            os.path.join(CSRC, "fp4idx_scorer.hip"), os.path.join(CSRC, "fp4idx_ceiling.hip"),
            os.path.join(CSRC, "fp4idx_api.cpp")]
-ARCH = os.environ.get("FP4IDX_OFFLOAD_ARCH", "gfx950")
+ARCH = "gfx950"  # the kernels use gfx950-only instructions (scaled FP4 converters and MFMA)
 
 
 def hipcc() -> str:
