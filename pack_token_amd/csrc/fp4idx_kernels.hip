@@ -253,7 +253,7 @@ __device__ __forceinline__ void q_quad_token(const QArgs& a, int64_t t, int lane
         int eg[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const Q8 q = quant8(pack8(x[g]), a.e_lo);
+            const Q8 q = quant8_f(x[g], a.e_lo);
             stage[hs * 16 + 4 * g + r] = q.codes;  // bytes 16g + 4r of head hs
             eg[g] = q.e;
         }
