@@ -305,7 +305,7 @@ def valu_ceiling(args, dev, kernel_gops: float) -> dict:
             call()
         (ms,), _ = launch_pass([call], max(args.steps, 5), stream)
         rec[kind + "_Gops"] = wg * 256 * iters * 8 / (ms * 1e-3) / 1e9
-    # the same adds at two wavefronts per SIMD (the scorers' occupancy)
+    # the same adds at two wavefronts per SIMD (issue rate at low occupancy)
     wg2 = wg // 4
 
     def call2():
