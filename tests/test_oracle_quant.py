@@ -168,8 +168,9 @@ def test_inverse_scale_equals_division_below_254():
     exponent 254)."""
     v = bf16_bits_to_f32(FINITE_BF16)
     for e in list(range(1, 20)) + list(range(120, 136)) + list(range(240, 254)):
-        a = v * np.float32(2.0 ** (127 - e))
-        b = v / np.float32(2.0 ** (e - 127))
+        with np.errstate(over="ignore"):  # large values at small e overflow to inf on both sides
+            a = v * np.float32(2.0 ** (127 - e))
+            b = v / np.float32(2.0 ** (e - 127))
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), e
 
 
